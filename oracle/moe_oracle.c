@@ -1,0 +1,363 @@
+/*
+ * CPU oracle for the routed-expert MoE feed-forward layer of the
+ * HunyuanImage-3.0 decoder.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline use it. It shares no code, header, table or constant with the
+ * HIP implementation.
+ *
+ * It is written to be checked by eye against the pages, not to be fast:
+ * plain loops, fp64 arithmetic, one rounding at each point where the layer
+ * stores a value in its working precision. OpenMP parallelises over token
+ * rows only, so results do not depend on the thread count.
+ *
+ * What it computes, per real (non-padding) token row x of length H:
+ *
+ *   1. Router logits l[e] = sum_h x[h] * Wr[e,h] for e < E.  The gate linear
+ *      is kept in fp32 (HunyuanImage-3.0 model-coverage page, "Train":
+ *      the router stays in fp32, gate_precision float32; model API page,
+ *      HunyuanImage3ForCausalMM: 'mlp.gate' is in _keep_in_fp32_modules_strict),
+ *      so the exact dot product (fp64; products of bf16/fp32 by fp32 are exact
+ *      in fp64) is rounded once to fp32.
+ *   2. p = softmax(l) over ALL E experts (model API page, build_moe_config:
+ *      softmax over all experts, top-k, renormalized, one shared expert),
+ *      evaluated in fp64 from the fp32 logits.
+ *   3. Top-K: the K largest p; on equal p the lower expert index is taken
+ *      first.  The output order is descending p, ties by ascending index.
+ *   4. Renormalise: w[k] = p[idx[k]] / sum_k' p[idx[k']] (sum in k order).
+ *   5. For each selected expert e: [u; g] = W13[e] x with W13[e] of shape
+ *      [2I, H] holding the up rows first and the gate rows second
+ *      (layers API page, HunyuanSharedMLP: gate_and_up_proj holds [up; gate],
+ *      up first; model-coverage page: fused [up; gate] expert projections
+ *      converted to grouped experts); h = SiLU(g) * u with
+ *      SiLU(z) = z / (1 + exp(-z)); h is an activation, stored in the layer's
+ *      dtype (rounded once: bf16 round-to-nearest-even, or fp32);
+ *      y_e = W2[e] h with W2[e] of shape [H, I] (down_proj), kept unrounded.
+ *   6. Shared expert (model API page, HunyuanImage3Block: routed experts plus
+ *      the fused shared expert; report section 3.1.1: one shared MLP): the
+ *      same SwiGLU with Ws13 [2Is, H], Ws2 [H, Is], applied to every real
+ *      token and added without any weight.
+ *   7. out = (((w[0] y_0 + w[1] y_1) + ...) + w[K-1] y_{K-1}) + y_shared,
+ *      rounded once to the layer's dtype.
+ *   8. Padding rows (padding_mask true at padding, model API page,
+ *      HunyuanImage3Block.forward): x is not read, out is not written, and the
+ *      route outputs are idx = -1, w = 0.
+ *
+ * dtype codes: 0 = fp32, 1 = bf16 (uint16 bit patterns).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* ------------------------------------------------------------ numbers */
+
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double elem(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORC_BF16)
+        return bf16_bits_to_double(((const uint16_t *)base)[i]);
+    return (double)((const float *)base)[i];
+}
+
+/* Nearest bf16 value to v, ties to even, computed directly from the double
+ * (no intermediate fp32 rounding). bf16 keeps 8 significant bits and fp32's
+ * exponent range. */
+static double round_bf16(double v)
+{
+    if (v == 0.0 || isnan(v) || isinf(v))
+        return v;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);                    /* a = m * 2^e, m in [0.5, 1) */
+    int q = e - 8;                   /* spacing of 8-bit significands */
+    if (q < -133)
+        q = -133;                    /* bf16 subnormal spacing 2^-133 */
+    double r = rint(ldexp(a, -q));   /* default rounding: nearest, ties even */
+    double out = ldexp(r, q);
+    if (out > 3.3895313892515355e38) /* beyond the largest finite bf16 */
+        out = INFINITY;
+    return v < 0 ? -out : out;
+}
+
+static double round_dtype(double v, int dtype)
+{
+    if (dtype == ORC_BF16)
+        return round_bf16(v);
+    return (double)(float)v;
+}
+
+static void store_dtype(void *base, int dtype, int64_t i, double rounded)
+{
+    float f = (float)rounded; /* exact: rounded is already representable */
+    if (dtype == ORC_BF16) {
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        ((uint16_t *)base)[i] = (uint16_t)(u >> 16);
+    } else {
+        ((float *)base)[i] = f;
+    }
+}
+
+/* ------------------------------------------------------------ router */
+
+/* Step 1 for one token row: logits in fp32. */
+static void router_logits_row(const void *x, int dtype, int64_t t, int64_t H,
+                              const float *w_router, int E, float *logits)
+{
+    for (int e = 0; e < E; e++) {
+        double acc = 0.0;
+        for (int64_t h = 0; h < H; h++)
+            acc += elem(x, dtype, t * H + h) * (double)w_router[(int64_t)e * H + h];
+        logits[e] = (float)acc;
+    }
+}
+
+/* Steps 2-4 for one row: softmax over all experts, top-K, renormalise. */
+static void softmax_topk_row(const float *logits, int E, int K,
+                             double *probs, int32_t *idx, double *w)
+{
+    double m = (double)logits[0];
+    for (int e = 1; e < E; e++)
+        if ((double)logits[e] > m)
+            m = (double)logits[e];
+    double z = 0.0;
+    for (int e = 0; e < E; e++) {
+        probs[e] = exp((double)logits[e] - m);
+        z += probs[e];
+    }
+    for (int e = 0; e < E; e++)
+        probs[e] /= z;
+
+    char taken[1024];
+    memset(taken, 0, sizeof taken);
+    for (int k = 0; k < K; k++) {
+        int best = -1;
+        for (int e = 0; e < E; e++) {
+            if (taken[e])
+                continue;
+            if (best < 0 || probs[e] > probs[best]) /* strict: lower index wins ties */
+                best = e;
+        }
+        idx[k] = best;
+        taken[best] = 1;
+    }
+    double s = 0.0;
+    for (int k = 0; k < K; k++)
+        s += probs[idx[k]];
+    for (int k = 0; k < K; k++)
+        w[k] = probs[idx[k]] / s;
+}
+
+/* ------------------------------------------------------------ expert */
+
+/* Step 5 (and 6): one SwiGLU expert on one token row xr (already in fp64).
+ * w_up_gate: [2*I, H] with the up rows first; w_down: [H, I]. */
+static void swiglu_row(const double *xr, const void *w_up_gate, const void *w_down,
+                       int dtype, int64_t H, int64_t I, double *hbuf, double *y)
+{
+    for (int64_t i = 0; i < I; i++) {
+        double u = 0.0, g = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            u += xr[h] * elem(w_up_gate, dtype, i * H + h);
+            g += xr[h] * elem(w_up_gate, dtype, (I + i) * H + h);
+        }
+        double silu_g = g / (1.0 + exp(-g));
+        hbuf[i] = round_dtype(silu_g * u, dtype);
+    }
+    for (int64_t j = 0; j < H; j++) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; i++)
+            acc += hbuf[i] * elem(w_down, dtype, j * I + i);
+        y[j] = acc;
+    }
+}
+
+static size_t expert_up_gate_elems(int64_t H, int64_t I) { return (size_t)(2 * I * H); }
+static size_t expert_down_elems(int64_t H, int64_t I) { return (size_t)(H * I); }
+
+static const void *offset_elems(const void *base, int dtype, size_t n)
+{
+    if (dtype == ORC_BF16)
+        return (const uint16_t *)base + n;
+    return (const float *)base + n;
+}
+
+/* ------------------------------------------------------------ public API */
+
+/*
+ * Router only, for the listed rows: fp32 logits [nrows, E], fp64 softmax
+ * probabilities [nrows, E] (nullable), top-K ids [nrows, K] and renormalised
+ * weights [nrows, K]. Padding rows give idx = -1, w = 0 and do not read x.
+ */
+void orc_route(const void *x, int dtype, const float *w_router, const uint8_t *pad,
+               int64_t H, int E, int K, const int64_t *rows, int64_t nrows,
+               float *logits, double *probs, int32_t *idx, double *w)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t t = rows[r];
+        double pbuf[1024];
+        if (pad && pad[t]) {
+            for (int e = 0; e < E; e++) {
+                if (logits) logits[r * E + e] = 0.0f;
+                if (probs) probs[r * E + e] = 0.0;
+            }
+            for (int k = 0; k < K; k++) {
+                idx[r * K + k] = -1;
+                w[r * K + k] = 0.0;
+            }
+            continue;
+        }
+        float lbuf[1024];
+        router_logits_row(x, dtype, t, H, w_router, E, lbuf);
+        softmax_topk_row(lbuf, E, K, pbuf, idx + r * K, w + r * K);
+        for (int e = 0; e < E; e++) {
+            if (logits) logits[r * E + e] = lbuf[e];
+            if (probs) probs[r * E + e] = pbuf[e];
+        }
+    }
+}
+
+/*
+ * The whole layer for the listed rows.
+ *
+ * If idx_in/w_in are given ([nrows, K]), they replace the router's choice
+ * (used where two selections are both correct); otherwise steps 1-4 run.
+ * idx_out/w_out ([nrows, K], nullable) receive the routes used.
+ * out_exact ([nrows, H] fp64, nullable) receives the value before the final
+ * rounding; out ([nrows, H] in dtype, nullable) the rounded output.
+ * Padding rows: x not read, out/out_exact not written, idx -1, w 0.
+ */
+void orc_moe_rows(const void *x, int dtype, const float *w_router,
+                  const void *w13, const void *w2, const void *ws13, const void *ws2,
+                  const uint8_t *pad, int64_t H, int E, int K, int64_t I, int64_t Is,
+                  const int64_t *rows, int64_t nrows,
+                  const int32_t *idx_in, const double *w_in,
+                  int32_t *idx_out, double *w_out, double *out_exact, void *out)
+{
+    int64_t Imax = I > Is ? I : Is;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t t = rows[r];
+        if (pad && pad[t]) {
+            for (int k = 0; k < K; k++) {
+                if (idx_out) idx_out[r * K + k] = -1;
+                if (w_out) w_out[r * K + k] = 0.0;
+            }
+            continue;
+        }
+        int32_t idx[1024];
+        double w[1024];
+        if (idx_in) {
+            for (int k = 0; k < K; k++) {
+                idx[k] = idx_in[r * K + k];
+                w[k] = w_in[r * K + k];
+            }
+        } else {
+            float lbuf[1024];
+            double pbuf[1024];
+            router_logits_row(x, dtype, t, H, w_router, E, lbuf);
+            softmax_topk_row(lbuf, E, K, pbuf, idx, w);
+        }
+        double *xr = malloc(sizeof(double) * (size_t)H);
+        double *hb = malloc(sizeof(double) * (size_t)Imax);
+        double *y = malloc(sizeof(double) * (size_t)H);
+        double *acc = malloc(sizeof(double) * (size_t)H);
+        for (int64_t h = 0; h < H; h++)
+            xr[h] = elem(x, dtype, t * H + h);
+        for (int64_t j = 0; j < H; j++)
+            acc[j] = 0.0;
+        for (int k = 0; k < K; k++) {
+            int e = idx[k];
+            swiglu_row(xr, offset_elems(w13, dtype, (size_t)e * expert_up_gate_elems(H, I)),
+                       offset_elems(w2, dtype, (size_t)e * expert_down_elems(H, I)),
+                       dtype, H, I, hb, y);
+            for (int64_t j = 0; j < H; j++)
+                acc[j] += w[k] * y[j];
+        }
+        swiglu_row(xr, ws13, ws2, dtype, H, Is, hb, y);
+        for (int64_t j = 0; j < H; j++) {
+            double v = acc[j] + y[j];
+            if (out_exact) out_exact[r * H + j] = v;
+            if (out) store_dtype(out, dtype, r * H + j, round_dtype(v, dtype));
+        }
+        for (int k = 0; k < K; k++) {
+            if (idx_out) idx_out[r * K + k] = idx[k];
+            if (w_out) w_out[r * K + k] = w[k];
+        }
+        free(xr);
+        free(hb);
+        free(y);
+        free(acc);
+    }
+}
+
+/*
+ * Dense brute force for the listed rows: every one of the E experts is
+ * evaluated and weighted by its renormalised gate weight if it is among the
+ * given routes (idx/w, [nrows, K]) and by zero otherwise; then the shared
+ * expert is added. Summation runs in expert-index order. Output is the fp64
+ * value before rounding, [nrows, H]. Padding rows are not written.
+ */
+void orc_moe_dense_rows(const void *x, int dtype, const void *w13, const void *w2,
+                        const void *ws13, const void *ws2, const uint8_t *pad,
+                        int64_t H, int E, int K, int64_t I, int64_t Is,
+                        const int64_t *rows, int64_t nrows,
+                        const int32_t *idx, const double *w, double *out_exact)
+{
+    int64_t Imax = I > Is ? I : Is;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t t = rows[r];
+        if (pad && pad[t])
+            continue;
+        double *xr = malloc(sizeof(double) * (size_t)H);
+        double *hb = malloc(sizeof(double) * (size_t)Imax);
+        double *y = malloc(sizeof(double) * (size_t)H);
+        double *acc = malloc(sizeof(double) * (size_t)H);
+        for (int64_t h = 0; h < H; h++)
+            xr[h] = elem(x, dtype, t * H + h);
+        for (int64_t j = 0; j < H; j++)
+            acc[j] = 0.0;
+        for (int e = 0; e < E; e++) {
+            double we = 0.0;
+            for (int k = 0; k < K; k++)
+                if (idx[r * K + k] == e)
+                    we = w[r * K + k];
+            swiglu_row(xr, offset_elems(w13, dtype, (size_t)e * expert_up_gate_elems(H, I)),
+                       offset_elems(w2, dtype, (size_t)e * expert_down_elems(H, I)),
+                       dtype, H, I, hb, y);
+            for (int64_t j = 0; j < H; j++)
+                acc[j] += we * y[j];
+        }
+        swiglu_row(xr, ws13, ws2, dtype, H, Is, hb, y);
+        for (int64_t j = 0; j < H; j++)
+            out_exact[r * H + j] = acc[j] + y[j];
+        free(xr);
+        free(hb);
+        free(y);
+        free(acc);
+    }
+}
+
+/* Round an fp64 array to bf16 bit patterns (used by tests for the
+ * tolerance-attainability check). */
+void orc_round_bf16_array(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        store_dtype(out, ORC_BF16, i, round_bf16(v[i]));
+}
+
+int orc_max_experts(void) { return 1024; }
