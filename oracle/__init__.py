@@ -85,8 +85,8 @@ def _check_weights(x, w_router, w13, w2, ws13, ws2, K):
 def route(x, w_router, K, pad_mask=None, rows=None):
     """Steps 1-4 for the given rows (all rows by default).
 
-    Returns dict(logits fp32 [n,E], probs fp64 [n,E], idx int32 [n,K],
-    w fp64 [n,K]); padding rows give idx -1, w 0."""
+    Returns dict(logits fp32 [n,E], probs fp32 [n,E], idx int32 [n,K],
+    w fp32 [n,K]); padding rows give idx -1, w 0."""
     lib = _load()
     x = np.ascontiguousarray(x)
     w_router = np.ascontiguousarray(w_router, np.float32)
@@ -95,9 +95,9 @@ def route(x, w_router, K, pad_mask=None, rows=None):
     n = rows.size
     pad = None if pad_mask is None else np.ascontiguousarray(pad_mask, np.uint8)
     logits = np.zeros((n, E), np.float32)
-    probs = np.zeros((n, E), np.float64)
+    probs = np.zeros((n, E), np.float32)
     idx = np.zeros((n, K), np.int32)
-    w = np.zeros((n, K), np.float64)
+    w = np.zeros((n, K), np.float32)
     lib.orc_route(_ptr(x), _dtype_of(x), _ptr(w_router), _ptr(pad), H, E, K,
                   _ptr(rows), n, _ptr(logits), _ptr(probs), _ptr(idx), _ptr(w))
     return {"logits": logits, "probs": probs, "idx": idx, "w": w}

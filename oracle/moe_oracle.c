@@ -8,8 +8,10 @@
  * HIP implementation.
  *
  * It is written to be checked by eye against the pages, not to be fast:
- * plain loops, fp64 arithmetic, one rounding at each point where the layer
- * stores a value in its working precision. OpenMP parallelises over token
+ * plain loops, fp64 arithmetic (except the router, which the pages keep in
+ * fp32: its logits are rounded once to fp32 and its softmax, selection and
+ * renormalisation run in fp32), and one rounding at each point where the
+ * layer stores a value in its working precision. OpenMP parallelises over token
  * rows only, so results do not depend on the thread count.
  *
  * What it computes, per real (non-padding) token row x of length H:
@@ -22,10 +24,16 @@
  *      in fp64) is rounded once to fp32.
  *   2. p = softmax(l) over ALL E experts (model API page, build_moe_config:
  *      softmax over all experts, top-k, renormalized, one shared expert),
- *      evaluated in fp64 from the fp32 logits.
- *   3. Top-K: the K largest p; on equal p the lower expert index is taken
- *      first.  The output order is descending p, ties by ascending index.
- *   4. Renormalise: w[k] = p[idx[k]] / sum_k' p[idx[k']] (sum in k order).
+ *      in fp32 like the rest of the router: m = max l, s[e] = expf(l[e] - m)
+ *      (host libm), Z = sum of s in ascending e, p[e] = s[e] / Z.
+ *   3. Top-K: the K experts with the largest p. Softmax preserves the order
+ *      of the logits strictly, so this is the K largest logits; the choice is
+ *      made on the fp32 logits, because fp32 p can underflow and make
+ *      distinct logits tie. On equal logits the lower expert index is taken
+ *      first. Output order: descending logit (so non-increasing weight), ties
+ *      by ascending index.
+ *   4. Renormalise: w[k] = p[idx[k]] / sum_k' p[idx[k']], sum in k order,
+ *      in fp32.
  *   5. For each selected expert e: [u; g] = W13[e] x with W13[e] of shape
  *      [2I, H] holding the up rows first and the gate rows second
  *      (layers API page, HunyuanSharedMLP: gate_and_up_proj holds [up; gate],
@@ -124,21 +132,22 @@ static void router_logits_row(const void *x, int dtype, int64_t t, int64_t H,
     }
 }
 
-/* Steps 2-4 for one row: softmax over all experts, top-K, renormalise. */
+/* Steps 2-4 for one row: softmax over all experts, top-K, renormalise
+ * (fp32). */
 static void softmax_topk_row(const float *logits, int E, int K,
-                             double *probs, int32_t *idx, double *w)
+                             float *probs, int32_t *idx, float *w)
 {
-    double m = (double)logits[0];
+    float m = logits[0];
     for (int e = 1; e < E; e++)
-        if ((double)logits[e] > m)
-            m = (double)logits[e];
-    double z = 0.0;
+        if (logits[e] > m)
+            m = logits[e];
+    float z = 0.0f;
     for (int e = 0; e < E; e++) {
-        probs[e] = exp((double)logits[e] - m);
+        probs[e] = expf(logits[e] - m);
         z += probs[e];
     }
     for (int e = 0; e < E; e++)
-        probs[e] /= z;
+        probs[e] = probs[e] / z;
 
     char taken[1024];
     memset(taken, 0, sizeof taken);
@@ -147,13 +156,13 @@ static void softmax_topk_row(const float *logits, int E, int K,
         for (int e = 0; e < E; e++) {
             if (taken[e])
                 continue;
-            if (best < 0 || probs[e] > probs[best]) /* strict: lower index wins ties */
+            if (best < 0 || logits[e] > logits[best]) /* strict: lower index wins ties */
                 best = e;
         }
         idx[k] = best;
         taken[best] = 1;
     }
-    double s = 0.0;
+    float s = 0.0f;
     for (int k = 0; k < K; k++)
         s += probs[idx[k]];
     for (int k = 0; k < K; k++)
@@ -197,26 +206,26 @@ static const void *offset_elems(const void *base, int dtype, size_t n)
 /* ------------------------------------------------------------ public API */
 
 /*
- * Router only, for the listed rows: fp32 logits [nrows, E], fp64 softmax
- * probabilities [nrows, E] (nullable), top-K ids [nrows, K] and renormalised
- * weights [nrows, K]. Padding rows give idx = -1, w = 0 and do not read x.
+ * Router only, for the listed rows: fp32 logits [nrows, E], fp32 softmax
+ * probabilities [nrows, E] (nullable), top-K ids [nrows, K] and fp32
+ * renormalised weights [nrows, K]. Padding rows give idx = -1, w = 0 and do not read x.
  */
 void orc_route(const void *x, int dtype, const float *w_router, const uint8_t *pad,
                int64_t H, int E, int K, const int64_t *rows, int64_t nrows,
-               float *logits, double *probs, int32_t *idx, double *w)
+               float *logits, float *probs, int32_t *idx, float *w)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; r++) {
         int64_t t = rows[r];
-        double pbuf[1024];
+        float pbuf[1024];
         if (pad && pad[t]) {
             for (int e = 0; e < E; e++) {
                 if (logits) logits[r * E + e] = 0.0f;
-                if (probs) probs[r * E + e] = 0.0;
+                if (probs) probs[r * E + e] = 0.0f;
             }
             for (int k = 0; k < K; k++) {
                 idx[r * K + k] = -1;
-                w[r * K + k] = 0.0;
+                w[r * K + k] = 0.0f;
             }
             continue;
         }
@@ -266,10 +275,11 @@ void orc_moe_rows(const void *x, int dtype, const float *w_router,
                 w[k] = w_in[r * K + k];
             }
         } else {
-            float lbuf[1024];
-            double pbuf[1024];
+            float lbuf[1024], pbuf[1024], wf[1024];
             router_logits_row(x, dtype, t, H, w_router, E, lbuf);
-            softmax_topk_row(lbuf, E, K, pbuf, idx, w);
+            softmax_topk_row(lbuf, E, K, pbuf, idx, wf);
+            for (int k = 0; k < K; k++)
+                w[k] = (double)wf[k];
         }
         double *xr = malloc(sizeof(double) * (size_t)H);
         double *hb = malloc(sizeof(double) * (size_t)Imax);

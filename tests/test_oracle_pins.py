@@ -85,9 +85,10 @@ def test_topk_tie_worked_example(E, dtype):
         x = wk.f32_to_bf16_bits(x)
     r = oracle.route(x, wr, K=2)
     assert r["idx"][0].tolist() == g["expected"]["idx"]
-    np.testing.assert_allclose(r["w"][0], g["expected"]["w"], rtol=1e-15)
+    # the router runs in fp32: a few fp32 ulps
+    np.testing.assert_allclose(r["w"][0], g["expected"]["w"], rtol=4e-7)
     if E == 4:
-        np.testing.assert_allclose(r["probs"][0], g["expected"]["probs"], rtol=1e-14)
+        np.testing.assert_allclose(r["probs"][0], g["expected"]["probs"], rtol=4e-7)
 
 
 def test_uniform_router():
@@ -100,6 +101,26 @@ def test_uniform_router():
     assert np.all(r["w"] == 0.25)
 
 
+def test_selection_survives_fp32_underflow():
+    # One expert's logit is far above the rest, so every other fp32
+    # probability underflows to 0 (or a subnormal) and many tie in p. The
+    # selection must still be the exact order of the probabilities, i.e. of
+    # the logits: the second pick is the second-largest logit.
+    E, H = 16, 64
+    rng = np.random.default_rng(3)
+    wr = rng.standard_normal((E, H)).astype(np.float32) * np.float32(0.1)
+    wr[:, 0] = 0.0
+    wr[11, 0] = 200.0
+    x = rng.standard_normal((4, H)).astype(np.float32)
+    x[:, 0] = 1.0
+    r = oracle.route(x, wr, K=3)
+    l64 = x.astype(np.float64) @ wr.astype(np.float64).T
+    for t in range(4):
+        order = np.argsort(-l64[t], kind="stable")[:3]
+        assert r["idx"][t].tolist() == order.tolist()
+        assert r["w"][t, 0] == 1.0 and np.all(r["w"][t, 1:] < 1e-30)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("E,K", [(8, 2), (16, 5), (64, 8)])
 def test_route_invariants_and_library(seed, E, K):
@@ -109,8 +130,9 @@ def test_route_invariants_and_library(seed, E, K):
     wr = d["w_router"] * np.float32(10.0)
     r = oracle.route(d["x"], wr, K=K)
     idx, w, probs, logits = r["idx"], r["w"], r["probs"], r["logits"]
-    # weights: sum to 1, non-increasing, ids distinct and in range
-    np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=4e-16 * K)
+    # weights: sum to 1 (fp32: within 2K units of 2^-24), non-increasing,
+    # ids distinct and in range
+    np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, rtol=0, atol=2 * K * 2.0 ** -24)
     assert np.all(np.diff(w, axis=1) <= 0)
     assert np.all((idx >= 0) & (idx < E))
     assert all(len(set(row)) == K for row in idx.tolist())
@@ -120,18 +142,21 @@ def test_route_invariants_and_library(seed, E, K):
     ulp = np.spacing(np.abs(ref_logits))
     assert np.all(np.abs(logits - ref_logits) <= ulp)
     # softmax over all experts: numpy float64 on the oracle's fp32 logits
+    # (the oracle evaluates it in fp32: a few ulps, relative)
     l64 = logits.astype(np.float64)
     ref_p = np.exp(l64 - l64.max(1, keepdims=True))
     ref_p /= ref_p.sum(1, keepdims=True)
-    np.testing.assert_allclose(probs, ref_p, rtol=1e-14, atol=0)
-    # top-k: stable argsort of -p (lower index first on ties)
-    ref_idx = np.argsort(-probs, axis=1, kind="stable")[:, :K]
+    np.testing.assert_allclose(probs, ref_p, rtol=2e-6, atol=1e-37)
+    # top-k: stable argsort of the negated logits (lower index first on
+    # ties), and the same order as float64 probabilities
+    ref_idx = np.argsort(-logits, axis=1, kind="stable")[:, :K]
     assert np.array_equal(idx, ref_idx)
+    assert np.array_equal(idx, np.argsort(-ref_p, axis=1, kind="stable")[:, :K])
     # renormalisation identity: renorm(topK(softmax(l))) = softmax(l[idx])
     sel = np.take_along_axis(l64, idx.astype(np.int64), 1)
     ref_w = np.exp(sel - sel.max(1, keepdims=True))
     ref_w /= ref_w.sum(1, keepdims=True)
-    np.testing.assert_allclose(w, ref_w, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(w, ref_w, rtol=2e-6, atol=1e-37)
 
 
 # ---------------------------------------------------------------- expert
@@ -158,10 +183,15 @@ def test_swiglu_up_first_worked_example(dtype):
     r = oracle.moe(x, d["w_router"], w13, w2, z(d["ws13"]), z(d["ws2"]), K=K)
     out = _as_f64(r["out"])[0]
     want = g["expected"]["out0_bf16" if dtype == wk.BF16 else "out0_f32"]
-    assert out[0] == want
-    assert out[0] != g["expected"]["swapped_layout_value"]
+    if dtype == wk.BF16:
+        # exact: h is rounded to bf16, far from a rounding boundary
+        assert out[0] == want
+    else:
+        # the fp32 gate weights sum to 1 within an ulp
+        np.testing.assert_allclose(out[0], want, rtol=2.5e-7)
+    assert abs(out[0] - g["expected"]["swapped_layout_value"]) > 0.1
     assert np.all(out[1:] == 0)
-    np.testing.assert_allclose(r["exact"][0, 0], want, rtol=1e-15)
+    np.testing.assert_allclose(r["exact"][0, 0], want, rtol=2.5e-7)
 
 
 def _numpy_swiglu(x64, w13, w2, dtype):
@@ -207,11 +237,11 @@ def test_k_equals_e_is_full_softmax_mixture(dtype):
     for e in range(E):
         ref += p[:, e:e + 1] * _numpy_swiglu(x64, d["w13"][e], d["w2"][e], dtype)
     scale = np.sqrt(np.mean(ref ** 2))
-    assert np.max(np.abs(r["exact"] - ref)) <= 1e-3 * scale
-    assert np.mean(np.abs(r["exact"] - ref) > 1e-10 * scale) < 0.01
-    # and the gate weights are exactly the probabilities, in descending order
+    # gate weights are fp32 (router precision): ~1e-7 relative differences
+    assert np.max(np.abs(r["exact"] - ref)) <= 1e-5 * scale
+    # and the gate weights are the probabilities, in descending order
     ref_w = -np.sort(-p, axis=1)
-    np.testing.assert_allclose(r["w"], ref_w, rtol=1e-12)
+    np.testing.assert_allclose(r["w"], ref_w, rtol=2e-6)
 
 
 @pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
