@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE feed-forward layer on one MI355X.
+
+One step = one hi3_moe_forward call over one batch of synthetic tokens: the
+router, dispatch, grouped [up; gate] + SwiGLU GEMM, grouped down GEMM,
+shared expert and combine. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s over the real tokens (the metric), with the
+layer's TFLOP/s and fraction of the bf16 MFMA peak, the roofline entry of the
+dominant kernel (its duration measured with HIP events recorded on the
+launch stream inside the timed region), per-stage times, and the CPU oracle
+timed on a bounded sample of the same workload on this host's cores.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wk  # noqa: E402
+
+METRIC = "MoE-layer tokens/s + TFLOP/s (% bf16 MFMA peak), 64e top-8, H=4096, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def stage_bytes(wl):
+    """Algorithmic HBM bytes per call of the memory-bound stages."""
+    sh = wl.shape
+    es = 2 if sh.dtype == wk.BF16 else 4
+    Tv, T, H, E, K = wl.T_valid, wl.T, sh.H, sh.E, sh.K
+    return {
+        # x read once, fp32 router weight (split once into 3 bf16 terms), routes written
+        "router": Tv * H * es + E * H * 4 + T * K * 8,
+        # x rows read once, written to K slots
+        "gather": Tv * H * es * (1 + K),
+        # K fp32 expert rows + the fp32 shared row read, one output row written
+        "combine": Tv * (K * H * 4 + H * 4 + H * es + K * 8),
+    }
+
+
+def gemm_flops(wl):
+    sh = wl.shape
+    Tv = wl.T_valid
+    return {
+        "gemm_up_gate_swiglu": Tv * (sh.K * 2 * sh.H * 2 * sh.I + 2 * sh.H * 2 * sh.Is),
+        "gemm_down": Tv * (sh.K * 2 * sh.I * sh.H + 2 * sh.Is * sh.H),
+    }
+
+
+def cpu_baseline(wl, d, K, target_s):
+    """The CPU oracle as it stands, on a bounded sample of real tokens."""
+    import oracle
+    pad = d["pad_mask"]
+    valid = np.nonzero(pad == 0)[0]
+    cores = len(os.sched_getaffinity(0))
+    args = (d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"])
+    n = max(1, min(cores, valid.size))
+    t0 = time.perf_counter()
+    oracle.moe(*args, K=K, pad_mask=pad, rows=valid[:n])
+    first = time.perf_counter() - t0
+    # grow the sample to about target_s seconds of wall time in total
+    n2 = int(min(valid.size - n, max(0, (target_s - first) / max(first, 1e-3) * n)))
+    total_n, total_t = n, first
+    if n2 > 0:
+        t0 = time.perf_counter()
+        oracle.moe(*args, K=K, pad_mask=pad, rows=valid[n:n + n2])
+        total_t += time.perf_counter() - t0
+        total_n += n2
+    return {"value": total_n / total_t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{total_n} real tokens of {wl.name} (full layer per token, fp64 C, "
+                      f"OpenMP over tokens), {total_t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="image_1024", choices=wk.WORKLOADS)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-time budget of the CPU oracle sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is measured on one GPU's share)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_decoder_ffn_amd as m
+
+    wl = wk.workload(args.workload, args.seed)
+    sh = wl.shape
+    log(f"[bench] workload {wl.name}: T={wl.T} real={wl.T_valid} H={sh.H} E={sh.E} "
+        f"K={sh.K} I={sh.I} Is={sh.Is}")
+    t0 = time.perf_counter()
+    d = wk.make_inputs(wl, args.seed)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    dd = {k: dev(v) for k, v in d.items()}
+    pad = dd["pad_mask"] if wl.T != wl.T_valid else None
+    x = dd["x"]
+    out = torch.zeros_like(x)
+    idx = torch.empty((wl.T, sh.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((wl.T, sh.K), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((sh.E,), dtype=torch.int32, device="cuda")
+    ws = m.workspace_for(x, sh.E, sh.K, sh.I, sh.Is)
+    log(f"[bench] workspace {ws.numel() / 2**20:.0f} MiB")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events is None:
+            m.hi3_moe_forward(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"],
+                              pad, sh.K, out, idx, wts, cnt, ws, stream)
+        else:
+            m.hi3_moe_forward_instrumented(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
+                                           dd["ws2"], pad, sh.K, out, idx, wts, cnt, ws,
+                                           events, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    hip = HipEvents()
+    ns = m.HI3_NUM_STAGES
+    evsets = [hip.create(ns + 1) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evsets[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] {args.steps} timed steps done")
+
+    stage_ms = np.zeros(ns)
+    for evs in evsets:
+        for s in range(ns):
+            stage_ms[s] += hip.elapsed_ms(evs[s], evs[s + 1])
+    stage_ms /= args.steps
+    for evs in evsets:
+        hip.destroy(evs)
+    names = [m.hi3_moe_stage_name(s) for s in range(ns)]
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_s = wl.T_valid / (ms_per_step * 1e-3)
+    flops = wl.T_valid * wk.flop_per_valid_token(sh)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    gf = gemm_flops(wl)
+    sb = stage_bytes(wl)
+    stages = {}
+    for s, name in enumerate(names):
+        e = {"us": round(stage_ms[s] * 1e3, 2)}
+        if name in gf and stage_ms[s] > 0:
+            e["tflops"] = round(gf[name] / (stage_ms[s] * 1e-3) / 1e12, 1)
+            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if name in sb and stage_ms[s] > 0:
+            e["gbs"] = round(sb[name] / (stage_ms[s] * 1e-3) / 1e9, 1)
+            e["frac_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        stages[name] = e
+    for name, e in stages.items():
+        log(f"  {name:22s} {e}")
+
+    dom = "gemm_up_gate_swiglu"
+    dom_ms = stage_ms[names.index(dom)]
+    achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
+    roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(wl, d, sh.K, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == wk.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "T_valid": wl.T_valid, "H": sh.H,
+                   "E": sh.E, "K": sh.K, "I": sh.I, "I_shared": sh.Is, "seed": args.seed},
+        "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * hi3_moe.h - C ABI of the routed-expert MoE feed-forward layer of the
+ * HunyuanImage-3.0 decoder, for AMD MI355X (gfx950).
+ *
+ * What the layer computes, per real (non-padding) token row x[t] of length H:
+ *
+ *   logits = W_r x (W_r is [E, H] fp32, the router kept in fp32:
+ *            HunyuanImage-3.0 model-coverage page, "Train"; model API page,
+ *            HunyuanImage3ForCausalMM, 'mlp.gate' kept in fp32)
+ *   p      = softmax(logits) over all E experts (fp32); take the top K;
+ *            renormalise the K selected p to sum to 1 (model API page,
+ *            build_moe_config: softmax over all experts, top-k, renormalized,
+ *            one shared expert). The top K is taken on the fp32 logits, the
+ *            exact order of p (unaffected by fp32 underflow of small p);
+ *            equal logits: lower expert index first.
+ *   y_e    = W2[e] (SiLU(g) * u) with [u; g] = W13[e] x, where W13[e] is
+ *            [2I, H] holding the up rows first and the gate rows second
+ *            (layers API page, HunyuanSharedMLP: gate_and_up_proj holds
+ *            [up; gate], up first; model-coverage page: fused [up; gate]
+ *            expert projections converted to grouped experts)
+ *   out[t] = sum_k w_k y_{e_k} + SharedSwiGLU(x[t])  (model API page,
+ *            HunyuanImage3Block: routed experts plus the fused shared expert;
+ *            technical report section 3.1.1: 64 experts, 8 active, one shared
+ *            MLP)
+ *
+ * Numeric contract (bf16 layers): the router runs in fp32 with products
+ * formed exactly; expert and shared projections accumulate in fp32; the
+ * SwiGLU activation h is stored as bf16; y stays fp32; the combine sums in
+ * fp32 in the order w_0 y_0 + w_1 y_1 + ... + shared and rounds once to bf16
+ * (nearest, ties to even). fp32 layers keep every value in fp32.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless stated otherwise; tensors are dense,
+ *    row-major, in the layouts given; every pointer must be 16-byte aligned.
+ *  - The caller owns every buffer. The library allocates no device memory,
+ *    keeps no pointer after returning and has no global mutable state: calls
+ *    on different streams with different workspaces may run concurrently.
+ *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream)
+ *    and the call returns without waiting. There is no device-to-host
+ *    synchronisation inside any call.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    validation error nothing is enqueued, nothing is written and a negative
+ *    status is returned. HI3_E_HIP means a launch failed after validation
+ *    (earlier stages of the call may have run).
+ *  - pad_mask is a [T] uint8 array, nonzero at padding rows (the polarity of
+ *    the pages' padding_mask: true at padding). NULL means no padding.
+ *    Padding rows are never read from x and never written to out.
+ *  - T = 0 returns HI3_OK and enqueues nothing.
+ *  - Builder's limits (HI3_E_UNSUPPORTED otherwise): dtype HI3_F32 or
+ *    HI3_BF16; 1 <= K <= E <= 64; H, I, I_shared multiples of 64;
+ *    T * K < 2^31.
+ */
+#ifndef HI3_MOE_H
+#define HI3_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of x, expert weights, shared weights and out. The router weight is
+ * always fp32. bf16 values are raw 16-bit bfloat16 patterns. */
+#define HI3_F32 0
+#define HI3_BF16 1
+
+/* status codes */
+#define HI3_OK 0
+#define HI3_E_NULL (-1)        /* a required pointer is NULL */
+#define HI3_E_SHAPE (-2)       /* T < 0, a size <= 0, or K > E */
+#define HI3_E_UNSUPPORTED (-3) /* outside the builder's limits above */
+#define HI3_E_WORKSPACE (-4)   /* workspace smaller than required */
+#define HI3_E_HIP (-5)         /* a HIP launch failed */
+
+/* Number of timed stages of hi3_moe_forward_instrumented. */
+#define HI3_NUM_STAGES 8
+
+/*
+ * Workspace bytes that hi3_moe_forward needs for these sizes (host-only, no
+ * HIP call). With I = I_shared = 0 it returns the smaller amount that
+ * hi3_moe_route and hi3_moe_dispatch need; the forward amount also serves
+ * them. Returns 0 for invalid sizes and for T = 0.
+ */
+size_t hi3_moe_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K,
+                              int32_t I, int32_t I_shared, int32_t dtype);
+
+/*
+ * Router only (softmax over all experts, top-k, renormalised).
+ *   x           [T, H] dtype, input rows (the [batch, sequence, hidden] input
+ *               of the pages' Block.forward, flattened).
+ *   w_router    [E, H] fp32 (linear layout [out, in]).
+ *   pad_mask    [T] uint8 or NULL.
+ *   topk_idx    [T, K] int32 out: per row the K expert ids in descending
+ *               logit (so non-increasing weight), equal logits by ascending
+ *               id; padding rows -1.
+ *   topk_w      [T, K] fp32 out: renormalised gate weights; padding rows 0.
+ *   expert_counts [E] int32 out or NULL: number of real rows routed to each
+ *               expert.
+ *   workspace   device memory of at least
+ *               hi3_moe_workspace_size(T, H, E, K, 0, 0, dtype) bytes.
+ */
+int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask,
+                  int64_t T, int32_t H, int32_t E, int32_t K, int32_t dtype,
+                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                  void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Dispatch only: groups given routes by expert (the pages' "grouped
+ * experts", model-coverage page, "Model Class"). Slots are numbered expert
+ * by expert; inside one expert, pairs keep ascending (token, k) order.
+ *   topk_idx      [T, K] int32 in, ids in [0, E); rows with pad_mask set
+ *                 are ignored (their ids are not read).
+ *   x             [T, H] dtype; read only when x_sorted is not NULL.
+ *   expert_offsets [E + 1] int32 out: first slot of each expert; the last
+ *                 entry is the number of real (token, k) pairs S.
+ *   perm_token    [T * K] int32 out: token of each slot; entries >= S are
+ *                 left unwritten.
+ *   slot_of       [T * K] int32 out: slot of pair (t, k), -1 for padding.
+ *   x_sorted      [T * K, H] dtype out or NULL: x_sorted[s] = x[perm_token[s]]
+ *                 for s < S.
+ *   workspace     as for hi3_moe_route.
+ */
+int hi3_moe_dispatch(const int32_t *topk_idx, const uint8_t *pad_mask, const void *x,
+                     int64_t T, int32_t H, int32_t E, int32_t K, int32_t dtype,
+                     int32_t *expert_offsets, int32_t *perm_token, int32_t *slot_of,
+                     void *x_sorted, void *workspace, size_t workspace_bytes,
+                     void *hip_stream);
+
+/*
+ * The whole layer: router, dispatch, grouped [up; gate] projection with the
+ * SwiGLU epilogue, grouped down projection, shared expert, combine.
+ *   x                [T, H] dtype.
+ *   w_router         [E, H] fp32.
+ *   w_up_gate        [E, 2*I, H] dtype; rows [0, I) up, [I, 2I) gate.
+ *   w_down           [E, H, I] dtype.
+ *   w_shared_up_gate [2*I_shared, H] dtype, same [up; gate] order.
+ *   w_shared_down    [H, I_shared] dtype.
+ *   pad_mask         [T] uint8 or NULL.
+ *   out              [T, H] dtype out; padding rows are not written. Must
+ *                    not overlap x (the residual add is the caller's).
+ *   topk_idx, topk_w, expert_counts: as in hi3_moe_route, each may be NULL.
+ *   workspace        at least hi3_moe_workspace_size(T, H, E, K, I,
+ *                    I_shared, dtype) bytes.
+ */
+int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
+                    const void *w_down, const void *w_shared_up_gate,
+                    const void *w_shared_down, const uint8_t *pad_mask,
+                    int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                    int32_t I_shared, int32_t dtype, void *out,
+                    int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * hi3_moe_forward with per-stage timing: stage_events holds
+ * HI3_NUM_STAGES + 1 hipEvent_t handles created by the caller; event i is
+ * recorded on hip_stream just before stage i is enqueued and the last one
+ * after the final stage (stage names: hi3_moe_stage_name). Same results as
+ * hi3_moe_forward. stage_events must not be NULL.
+ */
+int hi3_moe_forward_instrumented(const void *x, const float *w_router,
+                                 const void *w_up_gate, const void *w_down,
+                                 const void *w_shared_up_gate,
+                                 const void *w_shared_down, const uint8_t *pad_mask,
+                                 int64_t T, int32_t H, int32_t E, int32_t K,
+                                 int32_t I, int32_t I_shared, int32_t dtype,
+                                 void *out, int32_t *topk_idx, float *topk_w,
+                                 int32_t *expert_counts, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream,
+                                 void *const *stage_events);
+
+/* Static name of timed stage i (0 <= i < HI3_NUM_STAGES), else "?". */
+const char *hi3_moe_stage_name(int stage);
+
+/* Static description of a status code (host-only). */
+const char *hi3_moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HI3_MOE_H */

@@ -1,0 +1,200 @@
+"""Python binding of libhi3moe.so, the MI355X (gfx950) routed-expert MoE
+feed-forward layer of the HunyuanImage-3.0 decoder.
+
+The functions carry the names of the C entry points in include/hi3_moe.h and
+only marshal arguments: sizes are read from tensor shapes, pointers from
+tensors, the stream from torch's current stream. Every step of the layer runs
+in the library's HIP kernels; torch provides device memory and streams. There
+is no fallback: importing this package fails if the library is not built.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhi3moe.so")
+
+HI3_F32 = 0
+HI3_BF16 = 1
+HI3_OK = 0
+HI3_E_NULL = -1
+HI3_E_SHAPE = -2
+HI3_E_UNSUPPORTED = -3
+HI3_E_WORKSPACE = -4
+HI3_E_HIP = -5
+HI3_NUM_STAGES = 8
+
+EXPORTED = (
+    "hi3_moe_workspace_size",
+    "hi3_moe_route",
+    "hi3_moe_dispatch",
+    "hi3_moe_forward",
+    "hi3_moe_forward_instrumented",
+    "hi3_moe_stage_name",
+    "hi3_moe_status_string",
+)
+
+
+class Hi3Error(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"hi3_moe status {status}: {hi3_moe_status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run `python moe_decoder_ffn_amd/build.py` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.hi3_moe_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.hi3_moe_workspace_size.restype = sz
+    lib.hi3_moe_route.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, sz, P]
+    lib.hi3_moe_route.restype = ctypes.c_int
+    lib.hi3_moe_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.hi3_moe_dispatch.restype = ctypes.c_int
+    fwd = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.hi3_moe_forward.argtypes = fwd
+    lib.hi3_moe_forward.restype = ctypes.c_int
+    lib.hi3_moe_forward_instrumented.argtypes = fwd + [P]
+    lib.hi3_moe_forward_instrumented.restype = ctypes.c_int
+    lib.hi3_moe_stage_name.argtypes = [ctypes.c_int]
+    lib.hi3_moe_stage_name.restype = ctypes.c_char_p
+    lib.hi3_moe_status_string.argtypes = [ctypes.c_int]
+    lib.hi3_moe_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to hi3_moe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return HI3_BF16
+    if dt == torch.float32:
+        return HI3_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _check(status):
+    if status != HI3_OK:
+        raise Hi3Error(status)
+
+
+# ---------------------------------------------------------------- entry points
+
+def hi3_moe_workspace_size(T, H, E, K, I, I_shared, dtype) -> int:
+    return int(lib.hi3_moe_workspace_size(T, H, E, K, I, I_shared, dtype))
+
+
+def hi3_moe_route(x, w_router, pad_mask, K, topk_idx, topk_w, expert_counts, workspace,
+                  stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hi3_moe_route(_ptr(x), _ptr(w_router), _ptr(pad_mask), T, H, E, K,
+                             dtype_code(x.dtype), _ptr(topk_idx), _ptr(topk_w),
+                             _ptr(expert_counts), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hi3_moe_dispatch(topk_idx, pad_mask, x, E, expert_offsets, perm_token, slot_of,
+                     x_sorted, workspace, stream=None):
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hi3_moe_dispatch(_ptr(topk_idx), _ptr(pad_mask), _ptr(x), T, H, E, K,
+                                dtype_code(x.dtype), _ptr(expert_offsets), _ptr(perm_token),
+                                _ptr(slot_of), _ptr(x_sorted), _ptr(workspace), ws_bytes,
+                                _stream(stream)))
+
+
+def _forward_args(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                  pad_mask, K, out, topk_idx, topk_w, expert_counts, workspace, stream):
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = w_up_gate.shape[1] // 2
+    Is = w_shared_up_gate.shape[0] // 2
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (_ptr(x), _ptr(w_router), _ptr(w_up_gate), _ptr(w_down), _ptr(w_shared_up_gate),
+            _ptr(w_shared_down), _ptr(pad_mask), T, H, E, K, I, Is, dtype_code(x.dtype),
+            _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(expert_counts), _ptr(workspace),
+            ws_bytes, _stream(stream))
+
+
+def hi3_moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                    pad_mask, K, out, topk_idx=None, topk_w=None, expert_counts=None,
+                    workspace=None, stream=None):
+    _check(lib.hi3_moe_forward(*_forward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
+        topk_idx, topk_w, expert_counts, workspace, stream)))
+
+
+def hi3_moe_forward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_gate,
+                                 w_shared_down, pad_mask, K, out, topk_idx, topk_w,
+                                 expert_counts, workspace, stage_events, stream=None):
+    """stage_events: sequence of HI3_NUM_STAGES + 1 raw hipEvent_t handles (ints)."""
+    arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
+    _check(lib.hi3_moe_forward_instrumented(*_forward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
+        topk_idx, topk_w, expert_counts, workspace, stream), arr))
+
+
+def hi3_moe_stage_name(i) -> str:
+    return lib.hi3_moe_stage_name(i).decode()
+
+
+def hi3_moe_status_string(status) -> str:
+    return lib.hi3_moe_status_string(status).decode()
+
+
+# ---------------------------------------------------------------- convenience
+
+def workspace_for(x, E, K, I=0, I_shared=0):
+    """A device workspace (uint8) of the size hi3_moe_workspace_size asks for."""
+    T, H = x.shape
+    n = hi3_moe_workspace_size(T, H, E, K, I, I_shared, dtype_code(x.dtype))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+
+
+def moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, K,
+                pad_mask=None, out=None, workspace=None, return_routes=False):
+    """Allocates the outputs and the workspace with torch, then calls
+    hi3_moe_forward. Padding rows of a freshly allocated out are zero."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = w_up_gate.shape[1] // 2
+    Is = w_shared_up_gate.shape[0] // 2
+    if out is None:
+        out = torch.zeros_like(x)
+    if workspace is None:
+        workspace = workspace_for(x, E, K, I, Is)
+    idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, K), dtype=torch.float32, device=x.device)
+    counts = torch.empty((E,), dtype=torch.int32, device=x.device)
+    hi3_moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                    pad_mask, K, out, idx, w, counts, workspace)
+    if return_routes:
+        return out, idx, w, counts
+    return out

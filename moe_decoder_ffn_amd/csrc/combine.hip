@@ -1,0 +1,57 @@
+// Combine: out[t] = sum_k w[t,k] y[slot(t,k)] + y_shared[t] for every real
+// token (model API page, HunyuanImage3Block: routed experts plus the fused
+// shared expert; build_moe_config: renormalised top-k weights), summed in fp32
+// in k order, then the shared term, rounded once to the layer dtype.
+// Deterministic: each output element is produced by one thread in a fixed
+// order; no atomics. Padding rows are neither read nor written.
+#include "common.h"
+
+namespace hi3 {
+
+template <int DT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int64_t t = blockIdx.x;
+  if (a.pad && a.pad[t]) return;
+  const int vi = a.vidx[t];
+  if (vi < 0) return;
+  const int K = a.K;
+  const int nq = a.H / 4;
+  const f32x4_t *ys = reinterpret_cast<const f32x4_t *>(a.ys + static_cast<int64_t>(vi) * a.H);
+  for (int q = threadIdx.x; q < nq; q += blockDim.x) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < K; ++k) {
+      const int s = a.slotof[t * K + k];
+      const float w = a.wts[t * K + k];
+      const f32x4_t v =
+          reinterpret_cast<const f32x4_t *>(a.y + static_cast<int64_t>(s) * a.H)[q];
+      acc[0] = fmaf(w, v[0], acc[0]);
+      acc[1] = fmaf(w, v[1], acc[1]);
+      acc[2] = fmaf(w, v[2], acc[2]);
+      acc[3] = fmaf(w, v[3], acc[3]);
+    }
+    const f32x4_t sv = ys[q];
+    acc[0] += sv[0];
+    acc[1] += sv[1];
+    acc[2] += sv[2];
+    acc[3] += sv[3];
+    if (DT == kBF16) {
+      u32x2_t o;
+      o[0] = pack_bf16x2(acc[0], acc[1]);
+      o[1] = pack_bf16x2(acc[2], acc[3]);
+      reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(a.out) + t * a.H)[q] = o;
+    } else {
+      reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + t * a.H)[q] = acc;
+    }
+  }
+}
+
+hipError_t launch_combine(const CombineArgs &a, int dtype, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(combine_kernel<kBF16>, dim3(static_cast<unsigned>(a.T)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<kF32>, dim3(static_cast<unsigned>(a.T)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hi3

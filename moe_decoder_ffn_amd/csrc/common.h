@@ -1,0 +1,258 @@
+// Internal definitions shared by the HIP kernels and the host side of the
+// C ABI: vector types, bf16 helpers, wavefront reductions, tile constants and
+// the workspace plan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hi3 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int kWave = 64;
+constexpr int kMaxE = 64;
+
+// Router / dispatch token blocking: one router block handles 32 tokens, and
+// the per-block expert histograms that the stable counting sort scans use
+// the same blocking.
+constexpr int kRouterTB = 32;
+
+// bf16 grouped GEMM tile.
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+constexpr int kGemmBK = 64;
+// fp32 grouped GEMM tile.
+constexpr int kGemmF32BM = 64;
+constexpr int kGemmF32BN = 64;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ---------------------------------------------------------------- waves
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Butterfly sum, then lane 0's value broadcast so every lane holds the same
+// bits.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return __shfl(v, 0, kWave);
+}
+
+// Largest value over the wave; equal values resolve to the lowest index.
+// Every lane ends with the same (v, i).
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, kWave);
+    int oi = __shfl_xor(i, o, kWave);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ __forceinline__ int wave_uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// ---------------------------------------------------------------- plan
+
+// Byte offsets of every buffer inside the caller's workspace. Buffers that
+// depend on the expert sizes come last, so the route/dispatch layout
+// (I = Is = 0) is a prefix of the forward layout.
+struct Plan {
+  int64_t T;
+  int H, E, K, I, Is, dtype;
+  int NB;         // token blocks of kRouterTB rows
+  int Epad;       // E rounded up to 32 (router MFMA column tiles)
+  int BM;         // grouped-GEMM tile rows (per dtype)
+  int max_tiles;  // upper bound on grouped-GEMM row tiles
+  size_t wsplit;  // [3][Epad][H] bf16: router weight split into 3 bf16 terms
+  size_t idx;     // [T*K] int32 routes when the caller passes none
+  size_t wts;     // [T*K] fp32
+  size_t blkcnt;  // [NB][E] int32 per-block expert histogram
+  size_t blkoff;  // [NB][E] int32 first slot of each (block, expert)
+  size_t blkval;  // [NB] int32 real rows per block
+  size_t blkvoff; // [NB] int32 first real-row index of each block
+  size_t eoff;    // [E+1] int32 expert offsets
+  size_t counts;  // [E] int32
+  size_t misc;    // [16] int32: [0] real rows
+  size_t gto;     // [E+2] int32 first row tile of each group (E = shared)
+  size_t tiles;   // [max_tiles] int4: group, first row, rows, 0
+  size_t perm;    // [T*K] int32 slot -> token
+  size_t slotof;  // [T*K] int32 (token, k) -> slot
+  size_t vtok;    // [T] int32 real-row index -> token
+  size_t vidx;    // [T] int32 token -> real-row index (-1 padding)
+  size_t xs;      // [T*K, H] dtype: rows grouped by expert
+  size_t h;       // [T*K, I] dtype: SwiGLU activations of routed rows
+  size_t hs;      // [T, Is] dtype: SwiGLU activations of the shared expert
+  size_t y;       // [T*K, H] fp32: routed expert outputs by slot
+  size_t ys;      // [T, H] fp32: shared expert outputs by real-row index
+  size_t total;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) {
+  Plan p{};
+  p.T = T; p.H = H; p.E = E; p.K = K; p.I = I; p.Is = Is; p.dtype = dtype;
+  p.NB = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
+  p.Epad = (E + 31) / 32 * 32;
+  p.BM = dtype == kBF16 ? kGemmBM : kGemmF32BM;
+  const int64_t TK = T * K;
+  p.max_tiles = static_cast<int>((TK + p.BM - 1) / p.BM + E + (T + p.BM - 1) / p.BM);
+  const size_t es = dtype == kBF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  p.wsplit = take(dtype == kBF16 ? 3ull * p.Epad * H * 2 : 0);
+  p.idx = take(TK * 4);
+  p.wts = take(TK * 4);
+  p.blkcnt = take(static_cast<size_t>(p.NB) * E * 4);
+  p.blkoff = take(static_cast<size_t>(p.NB) * E * 4);
+  p.blkval = take(static_cast<size_t>(p.NB) * 4);
+  p.blkvoff = take(static_cast<size_t>(p.NB) * 4);
+  p.eoff = take((E + 1) * 4);
+  p.counts = take(E * 4);
+  p.misc = take(16 * 4);
+  p.gto = take((E + 2) * 4);
+  p.tiles = take(static_cast<size_t>(p.max_tiles) * 16);
+  p.perm = take(TK * 4);
+  p.slotof = take(TK * 4);
+  p.vtok = take(T * 4);
+  p.vidx = take(T * 4);
+  if (I > 0) {
+    p.xs = take(TK * H * es);
+    p.h = take(TK * I * es);
+    p.hs = take(T * Is * es);
+    p.y = take(TK * H * 4);
+    p.ys = take(T * H * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+// ---------------------------------------------------------------- launches
+
+struct RouterArgs {
+  const void *x;
+  const float *w_router;
+  const uint16_t *wsplit;
+  const uint8_t *pad;
+  int64_t T;
+  int H, E, K, Epad;
+  int32_t *idx;
+  float *wts;
+  int32_t *blkcnt;
+  int32_t *blkval;
+};
+
+struct ScanArgs {
+  const int32_t *blkcnt;
+  const int32_t *blkval;
+  int NB, E, BM;
+  int32_t *blkoff;
+  int32_t *blkvoff;
+  int32_t *eoff;
+  int32_t *counts_out;  // nullable (caller's expert_counts)
+  int32_t *counts;      // workspace copy
+  int32_t *misc;
+  int32_t *gto;
+  int4 *tiles;
+};
+
+struct ScatterArgs {
+  const int32_t *idx;
+  const uint8_t *pad;
+  const int32_t *blkoff;
+  const int32_t *blkvoff;
+  int64_t T;
+  int E, K;
+  int32_t *perm;
+  int32_t *slotof;
+  int32_t *vtok;   // nullable
+  int32_t *vidx;   // nullable
+};
+
+// One class of grouped-GEMM problems: the E routed experts (class 0) or the
+// shared expert (class 1).
+struct GemmClass {
+  const void *A;        // rows of the left operand, row stride lda elements
+  int64_t lda;
+  const int32_t *arow;  // nullable: row map (tile row index -> A row)
+  const void *B;        // [N, Kd] per group, row-major (weights [out, in])
+  int64_t strideB;      // elements between consecutive experts' B
+  void *C;              // output rows, row stride ldc elements
+  int64_t ldc;
+  int N;                // projection outputs (2*I for [up; gate], H for down)
+  int Kd;               // reduction length
+};
+
+struct GemmArgs {
+  GemmClass cls[2];
+  const int4 *tiles;
+  const int32_t *gto;
+  int E;
+  int NTn;  // column tiles of the widest class
+};
+
+struct CombineArgs {
+  const float *y;
+  const float *ys;
+  const int32_t *slotof;
+  const int32_t *vidx;
+  const float *wts;
+  const uint8_t *pad;
+  int64_t T;
+  int H, K;
+  void *out;
+};
+
+hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, int Epad,
+                               int H, hipStream_t s);
+hipError_t launch_router(const RouterArgs &a, int dtype, hipStream_t s);
+hipError_t launch_histogram(const int32_t *idx, const uint8_t *pad, int64_t T, int E,
+                            int K, int32_t *blkcnt, int32_t *blkval, hipStream_t s);
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
+hipError_t launch_gather(const void *x, int64_t row_bytes, const int32_t *slotof,
+                         const uint8_t *pad, int64_t T, int K, void *xs, hipStream_t s);
+hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int dtype, hipStream_t s);
+hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int dtype, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, int dtype, hipStream_t s);
+
+}  // namespace hi3

@@ -1,0 +1,265 @@
+// Host side of the C ABI declared in include/hi3_moe.h: argument validation,
+// workspace carve-up and the ordered enqueue of the kernels on the caller's
+// stream. No device memory is allocated and no device-to-host copy is made.
+#include "hi3_moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+using namespace hi3;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// need_expert: the expert sizes I and Is are used (forward).
+int check_sizes(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I, int32_t Is,
+                int32_t dtype, bool need_expert) {
+  if (T < 0 || H <= 0 || E <= 0 || K <= 0 || K > E) return HI3_E_SHAPE;
+  if (need_expert && (I <= 0 || Is <= 0)) return HI3_E_SHAPE;
+  if (!need_expert && (I < 0 || Is < 0)) return HI3_E_SHAPE;
+  if (dtype != HI3_F32 && dtype != HI3_BF16) return HI3_E_UNSUPPORTED;
+  if (E > kMaxE) return HI3_E_UNSUPPORTED;
+  if (H % 64 != 0 || I % 64 != 0 || Is % 64 != 0) return HI3_E_UNSUPPORTED;
+  if (T * static_cast<int64_t>(K) >= (int64_t{1} << 31)) return HI3_E_UNSUPPORTED;
+  return HI3_OK;
+}
+
+int all_aligned(std::initializer_list<const void *> ptrs) {
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return HI3_E_UNSUPPORTED;
+  return HI3_OK;
+}
+
+struct Recorder {
+  void *const *ev;
+  hipStream_t s;
+  bool ok = true;
+  void at(int i) {
+    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) != hipSuccess) ok = false;
+  }
+};
+
+#define HI3_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return HI3_E_HIP; \
+  } while (0)
+
+int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
+                 const void *w_down, const void *w_shared_up_gate, const void *w_shared_down,
+                 const uint8_t *pad_mask, int64_t T, int32_t H, int32_t E, int32_t K,
+                 int32_t I, int32_t Is, int32_t dtype, void *out, int32_t *topk_idx,
+                 float *topk_w, int32_t *expert_counts, void *workspace,
+                 size_t workspace_bytes, void *hip_stream, void *const *events) {
+  if (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !out)
+    return HI3_E_NULL;
+  int st = check_sizes(T, H, E, K, I, Is, dtype, true);
+  if (st != HI3_OK) return st;
+  if (T == 0) return HI3_OK;
+  if (!workspace) return HI3_E_NULL;
+  st = all_aligned({x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                    out, topk_idx, topk_w, expert_counts, workspace});
+  if (st != HI3_OK) return st;
+  const Plan p = make_plan(T, H, E, K, I, Is, dtype);
+  if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char *ws = static_cast<char *>(workspace);
+  auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  int32_t *idx = topk_idx ? topk_idx : static_cast<int32_t *>(at(p.idx));
+  float *wts = topk_w ? topk_w : static_cast<float *>(at(p.wts));
+  int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
+  int32_t *blkval = static_cast<int32_t *>(at(p.blkval));
+  int32_t *slotof = static_cast<int32_t *>(at(p.slotof));
+  int32_t *vtok = static_cast<int32_t *>(at(p.vtok));
+  int32_t *vidx = static_cast<int32_t *>(at(p.vidx));
+  const int4 *tiles = static_cast<const int4 *>(at(p.tiles));
+  const int32_t *gto = static_cast<const int32_t *>(at(p.gto));
+  const size_t es = dtype == HI3_BF16 ? 2 : 4;
+  Recorder rec{events, s};
+
+  // 0: router weight split (bf16 layers only)
+  rec.at(0);
+  if (dtype == HI3_BF16)
+    HI3_TRY(launch_split_router(w_router, static_cast<uint16_t *>(at(p.wsplit)), E, p.Epad, H, s));
+  // 1: router + per-block histogram
+  rec.at(1);
+  RouterArgs ra{x, w_router, static_cast<const uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
+                p.Epad, idx, wts, blkcnt, blkval};
+  HI3_TRY(launch_router(ra, dtype, s));
+  // 2: scans -> expert offsets, real-row list, GEMM row tiles
+  rec.at(2);
+  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
+              static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
+              static_cast<int32_t *>(at(p.eoff)), expert_counts,
+              static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
+              static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
+  HI3_TRY(launch_scan(sa, s));
+  // 3: stable slots
+  rec.at(3);
+  ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K,
+                 static_cast<int32_t *>(at(p.perm)), slotof, vtok, vidx};
+  HI3_TRY(launch_scatter(sc, s));
+  // 4: gather token rows into expert-grouped order
+  rec.at(4);
+  HI3_TRY(launch_gather(x, static_cast<int64_t>(H) * es, slotof, pad_mask, T, K, at(p.xs), s));
+  // 5: grouped [up; gate] projection + SwiGLU (routed experts and the shared expert)
+  rec.at(5);
+  GemmArgs up{};
+  up.cls[0] = GemmClass{at(p.xs), H, nullptr, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
+  up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
+  up.tiles = tiles;
+  up.gto = gto;
+  up.E = E;
+  HI3_TRY(launch_gemm_upgate(up, p.max_tiles, dtype, s));
+  // 6: grouped down projection
+  rec.at(6);
+  GemmArgs dn{};
+  dn.cls[0] = GemmClass{at(p.h), I, nullptr, w_down, int64_t{H} * I, at(p.y), H, H, I};
+  dn.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
+  dn.tiles = tiles;
+  dn.gto = gto;
+  dn.E = E;
+  HI3_TRY(launch_gemm_down(dn, p.max_tiles, dtype, s));
+  // 7: combine
+  rec.at(7);
+  CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
+                 slotof, vidx, wts, pad_mask, T, H, K, out};
+  HI3_TRY(launch_combine(ca, dtype, s));
+  rec.at(8);
+  return rec.ok ? HI3_OK : HI3_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hi3_moe_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                              int32_t I_shared, int32_t dtype) {
+  const bool expert = I > 0 || I_shared > 0;
+  if (check_sizes(T, H, E, K, I, I_shared, dtype, expert) != HI3_OK) return 0;
+  if (T == 0) return 0;
+  return make_plan(T, H, E, K, expert ? I : 0, expert ? I_shared : 0, dtype).total;
+}
+
+int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask, int64_t T,
+                  int32_t H, int32_t E, int32_t K, int32_t dtype, int32_t *topk_idx,
+                  float *topk_w, int32_t *expert_counts, void *workspace,
+                  size_t workspace_bytes, void *hip_stream) {
+  if (!x || !w_router || !topk_idx || !topk_w) return HI3_E_NULL;
+  int st = check_sizes(T, H, E, K, 0, 0, dtype, false);
+  if (st != HI3_OK) return st;
+  if (T == 0) return HI3_OK;
+  if (!workspace) return HI3_E_NULL;
+  st = all_aligned({x, w_router, pad_mask, topk_idx, topk_w, expert_counts, workspace});
+  if (st != HI3_OK) return st;
+  const Plan p = make_plan(T, H, E, K, 0, 0, dtype);
+  if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char *ws = static_cast<char *>(workspace);
+  auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  if (dtype == HI3_BF16)
+    HI3_TRY(launch_split_router(w_router, static_cast<uint16_t *>(at(p.wsplit)), E, p.Epad, H, s));
+  RouterArgs ra{x, w_router, static_cast<const uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
+                p.Epad, topk_idx, topk_w, static_cast<int32_t *>(at(p.blkcnt)),
+                static_cast<int32_t *>(at(p.blkval))};
+  HI3_TRY(launch_router(ra, dtype, s));
+  if (expert_counts) {
+    ScanArgs sa{ra.blkcnt, ra.blkval, p.NB, E, p.BM,
+                static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
+                static_cast<int32_t *>(at(p.eoff)), expert_counts,
+                static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
+                static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
+    HI3_TRY(launch_scan(sa, s));
+  }
+  return HI3_OK;
+}
+
+int hi3_moe_dispatch(const int32_t *topk_idx, const uint8_t *pad_mask, const void *x,
+                     int64_t T, int32_t H, int32_t E, int32_t K, int32_t dtype,
+                     int32_t *expert_offsets, int32_t *perm_token, int32_t *slot_of,
+                     void *x_sorted, void *workspace, size_t workspace_bytes,
+                     void *hip_stream) {
+  if (!topk_idx || !expert_offsets || !perm_token || !slot_of) return HI3_E_NULL;
+  if (x_sorted && !x) return HI3_E_NULL;
+  int st = check_sizes(T, H, E, K, 0, 0, dtype, false);
+  if (st != HI3_OK) return st;
+  if (T == 0) return HI3_OK;
+  if (!workspace) return HI3_E_NULL;
+  st = all_aligned({topk_idx, pad_mask, x, expert_offsets, perm_token, slot_of, x_sorted,
+                    workspace});
+  if (st != HI3_OK) return st;
+  const Plan p = make_plan(T, H, E, K, 0, 0, dtype);
+  if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char *ws = static_cast<char *>(workspace);
+  auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
+  int32_t *blkval = static_cast<int32_t *>(at(p.blkval));
+  HI3_TRY(launch_histogram(topk_idx, pad_mask, T, E, K, blkcnt, blkval, s));
+  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
+              static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
+              expert_offsets, nullptr, static_cast<int32_t *>(at(p.counts)),
+              static_cast<int32_t *>(at(p.misc)), static_cast<int32_t *>(at(p.gto)),
+              static_cast<int4 *>(at(p.tiles))};
+  HI3_TRY(launch_scan(sa, s));
+  ScatterArgs sc{topk_idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm_token, slot_of,
+                 nullptr, nullptr};
+  HI3_TRY(launch_scatter(sc, s));
+  if (x_sorted) {
+    const size_t es = dtype == HI3_BF16 ? 2 : 4;
+    HI3_TRY(launch_gather(x, static_cast<int64_t>(H) * es, slot_of, pad_mask, T, K, x_sorted, s));
+  }
+  return HI3_OK;
+}
+
+int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
+                    const void *w_down, const void *w_shared_up_gate,
+                    const void *w_shared_down, const uint8_t *pad_mask, int64_t T,
+                    int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                    int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
+                    int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                    void *hip_stream) {
+  return forward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                      pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx, topk_w,
+                      expert_counts, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int hi3_moe_forward_instrumented(const void *x, const float *w_router, const void *w_up_gate,
+                                 const void *w_down, const void *w_shared_up_gate,
+                                 const void *w_shared_down, const uint8_t *pad_mask,
+                                 int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                                 int32_t I_shared, int32_t dtype, void *out,
+                                 int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream,
+                                 void *const *stage_events) {
+  if (!stage_events) return HI3_E_NULL;
+  return forward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                      pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx, topk_w,
+                      expert_counts, workspace, workspace_bytes, hip_stream, stage_events);
+}
+
+const char *hi3_moe_stage_name(int stage) {
+  static const char *names[HI3_NUM_STAGES] = {
+      "router_weight_split", "router", "scan", "scatter",
+      "gather", "gemm_up_gate_swiglu", "gemm_down", "combine"};
+  if (stage < 0 || stage >= HI3_NUM_STAGES) return "?";
+  return names[stage];
+}
+
+const char *hi3_moe_status_string(int status) {
+  switch (status) {
+    case HI3_OK: return "ok";
+    case HI3_E_NULL: return "a required pointer is NULL";
+    case HI3_E_SHAPE: return "invalid sizes (T < 0, a size <= 0, or K > E)";
+    case HI3_E_UNSUPPORTED:
+      return "unsupported (dtype, E > 64, H/I/I_shared not a multiple of 64, T*K >= 2^31, "
+             "or a pointer not 16-byte aligned)";
+    case HI3_E_WORKSPACE: return "workspace smaller than hi3_moe_workspace_size";
+    case HI3_E_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

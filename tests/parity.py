@@ -1,0 +1,138 @@
+"""Helpers for the GPU parity tests: upload of generated inputs, and the
+comparison rules against the CPU oracle.
+
+Rules (all against the oracle on the same seeded inputs):
+
+* Routes. For a real row let gap = l_(K) - l_(K+1) of the oracle's fp32
+  logits sorted descending. Where gap > 1e-4 the GPU's K expert ids must be
+  exactly the oracle's (as sets), and its weights must match the oracle's
+  per expert within ROUTE_W_TOL. Where gap <= 1e-4 both selections are
+  correct: the GPU ids must be K distinct ids whose weights match the
+  oracle's probabilities at those ids, renormalised; the row's output is then
+  compared with the oracle run on the GPU's ids. Every row's ids are ordered
+  by non-increasing weight, equal weights by ascending id. Padding rows:
+  ids -1, weights 0.
+* Outputs. max |gpu - oracle| over the compared real rows must be at most
+  2e-2 * RMS(oracle output) for bf16 layers and 1e-5 * RMS for fp32 layers,
+  against the oracle's fp64 value before the final rounding.
+* Integer work (counts, offsets, permutations, gathered rows) is compared
+  bit for bit.
+
+ROUTE_W_TOL: the GPU's fp32 logits differ from the oracle's by a few 1e-6 at
+full size (fp32 accumulation over H = 4096 terms whose absolute sum is about
+50); a renormalised weight w moves by at most about 2 w dl, well below
+2e-5.
+"""
+import numpy as np
+import torch
+
+import oracle
+import workloads as wk
+
+GAP_TOL = 1e-4
+ROUTE_W_TOL = 2e-5
+OUT_TOL = {wk.BF16: 2e-2, wk.F32: 1e-5}
+
+
+def to_dev(a, device="cuda"):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f64(a):
+    if a.dtype == np.uint16:
+        return wk.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def upload(d):
+    return {k: to_dev(v) for k, v in d.items()}
+
+
+def check_routes(gpu_idx, gpu_w, ref, pad, E, K):
+    """Returns (near_rows, ref_idx_for_rows, ref_w_for_rows): the routes the
+    oracle should use per row (its own where the gap is clear, the GPU's
+    where it is not)."""
+    T = gpu_idx.shape[0]
+    valid = np.ones(T, bool) if pad is None else pad == 0
+    assert np.all(gpu_idx[~valid] == -1) and np.all(gpu_w[~valid] == 0)
+    logits = ref["logits"]
+    if K < E:
+        srt = -np.sort(-logits, axis=1)
+        gap = srt[:, K - 1].astype(np.float64) - srt[:, K].astype(np.float64)
+    else:
+        gap = np.full(T, np.inf)
+    near = valid & (gap <= GAP_TOL)
+    firm = valid & ~near
+    gi = gpu_idx.astype(np.int64)
+    # ids in range and distinct, order by non-increasing weight
+    v = gi[valid]
+    assert v.size == 0 or (v.min() >= 0 and v.max() < E)
+    assert np.all(np.sort(v, 1)[:, 1:] != np.sort(v, 1)[:, :-1]) if K > 1 else True
+    gw = gpu_w[valid].astype(np.float64)
+    assert np.all(np.diff(gw, axis=1) <= 0)
+    # firm rows: same sets, weights per id
+    bad = np.nonzero(firm & np.any(np.sort(gi, 1) != np.sort(ref["idx"], 1), axis=1))[0]
+    assert bad.size == 0, f"route mismatch at rows {bad[:10]} (gaps {gap[bad[:10]]})"
+    rows = np.nonzero(firm)[0]
+    dense_g = np.zeros((rows.size, E))
+    dense_r = np.zeros((rows.size, E))
+    np.put_along_axis(dense_g, gi[rows], gpu_w[rows].astype(np.float64), 1)
+    np.put_along_axis(dense_r, ref["idx"][rows].astype(np.int64), ref["w"][rows], 1)
+    err = np.abs(dense_g - dense_r).max() if rows.size else 0.0
+    assert err <= ROUTE_W_TOL, f"route weight error {err}"
+    # near rows: weights = oracle probabilities at the GPU's ids, renormalised
+    ref_idx = ref["idx"].copy()
+    ref_w = ref["w"].copy()
+    for t in np.nonzero(near)[0]:
+        p = ref["probs"][t, gi[t]]
+        w = p / p.sum()
+        assert np.abs(w - gpu_w[t]).max() <= ROUTE_W_TOL
+        ref_idx[t] = gi[t]
+        ref_w[t] = w
+    return near, ref_idx, ref_w
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 numbers at |v| (8 significant bits)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_output(gpu_rows, exact_rows, dtype, what=""):
+    """Asserts the output rule above; returns max |err| / RMS."""
+    g = as_f64(gpu_rows)
+    rms = float(np.sqrt(np.mean(exact_rows ** 2)))
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    if g.size == 0:
+        return 0.0
+    diff = np.abs(g - exact_rows)
+    err = float(diff.max())
+    if dtype == wk.F32:
+        tol = OUT_TOL[dtype] * rms
+        assert err <= tol, f"{what}: max err {err:.4g} > {tol:.4g} (1e-5 * RMS {rms:.4g})"
+    else:
+        bound = np.maximum(OUT_TOL[dtype] * rms, bf16_ulp(exact_rows))
+        bad = np.argwhere(diff > bound)
+        assert bad.size == 0, (f"{what}: {len(bad)} elements outside max(2e-2 * RMS, 1 ulp); "
+                               f"first {bad[:3].tolist()}, max err / RMS {err / rms:.4f}")
+        erms = float(np.sqrt(np.mean(diff ** 2)))
+        assert erms <= 5e-3 * rms, f"{what}: RMS error {erms / rms:.4g} * RMS"
+    return err / rms
+
+
+def oracle_rows(d, K, rows, idx, w, pad=None):
+    """The oracle's layer output at `rows` using the given routes for them."""
+    r = oracle.moe(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"], K=K,
+                   pad_mask=pad, rows=rows, idx=idx[rows], w=w[rows])
+    return r["exact"]

@@ -1,0 +1,211 @@
+"""GPU parity of the whole layer (hi3_moe_forward) against the CPU oracle:
+small cases compared on every row (several GEMM tiles, ragged tails,
+padding, edge cases), the full-size workloads on every row's routes and on
+sampled rows' outputs, plus determinism."""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wk
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+from parity import (as_f64, check_output, check_routes, oracle_rows, to_dev,  # noqa: E402
+                    to_host, upload)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_forward(dd, K, pad=None, sentinel=None):
+    """Runs hi3_moe_forward on device inputs dd; returns host out, idx, w,
+    counts."""
+    import moe_decoder_ffn_amd as m
+    x = dd["x"]
+    T, H = x.shape
+    E = dd["w_router"].shape[0]
+    if sentinel is None:
+        out = torch.zeros_like(x)
+    else:
+        out = torch.full_like(x, sentinel)
+    padd = to_dev(pad) if pad is not None else None
+    out, idx, w, cnt = m.moe_forward(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
+                                     dd["ws2"], K, pad_mask=padd, out=out, return_routes=True)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(idx), to_host(w), to_host(cnt)
+
+
+def full_check(d, K, pad=None, sentinel=None, rows=None):
+    """Forward on the GPU, then: routes of all rows; counts; outputs of
+    `rows` (all real rows by default) against the oracle."""
+    E = d["w_router"].shape[0]
+    dtype = wk.BF16 if d["x"].dtype == np.uint16 else wk.F32
+    out, idx, w, cnt = gpu_forward(upload(d), K, pad, sentinel)
+    ref = oracle.route(d["x"], d["w_router"], K, pad_mask=pad)
+    near, ref_idx, ref_w = check_routes(idx, w, ref, pad, E, K)
+    assert np.array_equal(cnt, np.bincount(idx[idx >= 0], minlength=E))
+    valid = np.ones(len(idx), bool) if pad is None else pad == 0
+    if rows is None:
+        rows = np.nonzero(valid)[0]
+    exact = oracle_rows(d, K, rows, ref_idx, ref_w, pad)
+    rel = check_output(out[rows], exact, dtype)
+    return out, idx, w, cnt, near, rel
+
+
+SMALL = [
+    # name, dtype, H, E, K, I, Is, seq_lens, padded_len
+    ("tiny_f32", wk.F32, 256, 8, 2, 128, 128, (64,), None),
+    ("f32_ragged", wk.F32, 192, 8, 3, 192, 64, (150, 37), 160),
+    ("bf16_tiles", wk.BF16, 512, 8, 2, 256, 192, (700,), None),
+    ("bf16_e16_pad", wk.BF16, 256, 16, 4, 320, 128, (300, 129, 7), 300),
+    ("bf16_e64_k8", wk.BF16, 512, 64, 8, 128, 256, (600,), None),
+    ("bf16_one_token", wk.BF16, 256, 8, 2, 128, 128, (1,), None),
+]
+
+
+@pytest.mark.parametrize("name,dtype,H,E,K,I,Is,seq,plen", SMALL)
+def test_forward_small_all_rows(name, dtype, H, E, K, I, Is, seq, plen):
+    _say(f"[forward] {name}")
+    shape = wk.LayerShape(H=H, E=E, K=K, I=I, Is=Is, dtype=dtype)
+    wl = wk.custom(shape, seq, plen)
+    d = wk.make_inputs(wl, 7)
+    d["w_router"] = d["w_router"] * np.float32(5.0)
+    pad = d["pad_mask"] if wl.T != wl.T_valid else None
+    sentinel = 0.75 if pad is not None else None
+    out, idx, *_ = full_check(d, K, pad, sentinel)
+    if pad is not None:
+        # padding rows keep the sentinel (never written), nothing is NaN
+        assert np.all(as_f64(out[pad == 1]) == 0.75)
+        assert np.isfinite(as_f64(out[pad == 0])).all()
+
+
+@pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
+def test_forward_k_equals_e(dtype):
+    _say(f"[forward] K=E dtype={dtype}")
+    shape = wk.LayerShape(H=256, E=8, K=8, I=128, Is=128, dtype=dtype)
+    d = wk.make_inputs(wk.custom(shape, (64,)), 3)
+    d["w_router"] = d["w_router"] * np.float32(20.0)
+    full_check(d, 8)
+
+
+@pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
+def test_forward_swiglu_up_first_worked_example(dtype):
+    g = json.load(open(os.path.join(GOLDEN, "swiglu_up_first.json")))
+    E, K, H, I = 8, 2, 256, 128
+    shape = wk.LayerShape(H=H, E=E, K=K, I=I, Is=I, dtype=dtype)
+    d = wk.make_inputs(wk.custom(shape, (5,)), 0)
+    c = (lambda v: wk.f32_to_bf16_bits(np.float32(v))) if dtype == wk.BF16 else np.float32
+    for k in ("w13", "w2", "ws13", "ws2"):
+        d[k][...] = 0
+    d["w13"][:, 0, 0] = c(1.0)
+    d["w13"][:, I, 0] = c(2.0)
+    d["w2"][:, 0, 0] = c(1.0)
+    x = np.zeros((5, H), np.float32)
+    x[:, 0] = 1.0
+    d["x"] = wk.f32_to_bf16_bits(x) if dtype == wk.BF16 else x
+    out, *_ = gpu_forward(upload(d), K)
+    out = as_f64(out)
+    want = g["expected"]["out0_bf16" if dtype == wk.BF16 else "out0_f32"]
+    if dtype == wk.BF16:
+        assert np.all(out[:, 0] == want), out[:, 0]
+    else:
+        # fp32: device expf and the fp32 gate weights, a few ulps
+        np.testing.assert_allclose(out[:, 0], want, rtol=5e-7)
+    assert np.all(np.abs(out[:, 0] - g["expected"]["swapped_layout_value"]) > 0.1)
+    assert np.all(out[:, 1:] == 0)
+
+
+def test_forward_edge_cases():
+    import moe_decoder_ffn_amd as m
+    shape = wk.LayerShape(H=256, E=16, K=2, I=128, Is=128, dtype=wk.BF16)
+    # all rows padding: nothing written, counts zero
+    _say("[forward] all padding")
+    d = wk.make_inputs(wk.custom(shape, (0, 0), padded_len=40), 0)
+    out, idx, w, cnt = gpu_forward(upload(d), 2, d["pad_mask"], sentinel=3.0)
+    assert np.all(as_f64(out) == 3.0) and np.all(idx == -1) and np.all(cnt == 0)
+    # an empty expert and a one-row expert: router rows that never / once win
+    _say("[forward] empty + one-row experts")
+    d = wk.make_inputs(wk.custom(shape, (300,)), 1)
+    wr = d["w_router"] * np.float32(3.0)
+    wr[5] = 0.0
+    wr[5, 0] = -100.0        # expert 5 loses everywhere x[:,0] > 0 ...
+    xf = wk.bf16_bits_to_f32(d["x"]).copy()
+    xf[:, 0] = np.abs(xf[:, 0]) + 0.5
+    xf[17, 0] = -3.0         # ... except token 17, where it wins
+    d["x"] = wk.f32_to_bf16_bits(xf)
+    d["w_router"] = wr
+    out, idx, w, cnt, *_ = full_check(d, 2)
+    assert cnt[5] == 1 and 5 in idx[17]
+    wr2 = wr.copy()
+    wr2[5, 0] = -1000.0
+    xf[17, 0] = 1.0
+    d["x"] = wk.f32_to_bf16_bits(xf)
+    d["w_router"] = wr2
+    out, idx, w, cnt, *_ = full_check(d, 2)
+    assert cnt[5] == 0
+
+
+def test_forward_deterministic():
+    shape = wk.LayerShape(H=512, E=64, K=8, I=256, Is=256, dtype=wk.BF16)
+    d = upload(wk.make_inputs(wk.custom(shape, (999,)), 5))
+    a = gpu_forward(d, 8)
+    b = gpu_forward(d, 8)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------- full size
+
+@pytest.fixture(scope="module")
+def full_weights():
+    _say("[forward] generating full-size expert weights")
+    w = wk.make_expert_weights(wk.FULL, 0)
+    dev = upload(w)
+    return w, dev
+
+
+def _sample_rows(valid_rows, n, seed):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(valid_rows, size=min(n, valid_rows.size), replace=False)
+    return np.unique(np.concatenate([valid_rows[:2], valid_rows[-2:], pick]))
+
+
+@pytest.mark.parametrize("name", ["image_1024", "batch8_512", "skew_16k", "padded_mixed"])
+def test_forward_full_size(full_weights, name):
+    w_host, w_dev = full_weights
+    wl = wk.workload(name, 0)
+    sh = wl.shape
+    _say(f"[forward] full size {name}: T={wl.T}, real {wl.T_valid}")
+    x, pad = wk.make_x(wl, 0)
+    wr = wk.make_router_weight(sh, 0, skew=wl.skew)
+    padarg = pad if wl.T != wl.T_valid else None
+    dd = dict(w_dev)
+    dd["x"] = to_dev(x)
+    dd["w_router"] = to_dev(wr)
+    out, idx, w, cnt = gpu_forward(dd, sh.K, padarg, sentinel=0.5 if padarg is not None else None)
+    del dd
+    ref = oracle.route(x, wr, sh.K, pad_mask=padarg)
+    near, ref_idx, ref_w = check_routes(idx, w, ref, padarg, sh.E, sh.K)
+    assert np.array_equal(cnt, np.bincount(idx[idx >= 0], minlength=sh.E))
+    valid_rows = np.nonzero(pad == 0)[0]
+    rows = _sample_rows(valid_rows, 24, 1)
+    rows = np.unique(np.concatenate([rows, np.nonzero(near)[0][:4]]))
+    d = dict(w_host)
+    d["x"] = x
+    d["w_router"] = wr
+    exact = oracle_rows(d, sh.K, rows, ref_idx, ref_w, padarg)
+    rel = check_output(out[rows], exact, sh.dtype, name)
+    _say(f"  near-tie rows {int(near.sum())}, max err / RMS = {rel:.4f}, "
+         f"load max/mean = {cnt.max() / cnt.mean():.2f}, min = {cnt.min()}")
+    if padarg is not None:
+        assert np.all(as_f64(out[pad == 1]) == 0.5)
+    if wl.skew:
+        assert cnt[:4].min() > 3.0 * cnt.mean() and cnt[-4:].max() < 0.05 * cnt.mean()

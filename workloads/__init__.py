@@ -190,37 +190,49 @@ def _normal_fill(ss: np.random.SeedSequence, n: int, scale: float,
     return out
 
 
-def make_weights(shape: LayerShape, seed: int = 0, skew: bool = False) -> dict:
-    """Router weight [E,H] fp32; fused expert projections W13 [E,2I,H]
-    (rows [0,I) up, [I,2I) gate); down projections W2 [E,H,I]; shared
-    expert Ws13 [2Is,H] and Ws2 [H,Is]. All N(0, 0.02^2).
+def make_router_weight(shape: LayerShape, seed: int = 0, skew: bool = False) -> np.ndarray:
+    """Router weight [E,H] fp32, N(0, 0.02^2).
 
     skew=True applies the load-imbalance construction: +0.5 on every
-    element of router rows 0..3 (those experts then win for roughly half of
-    all tokens), and the last four router rows scaled by 0.1, 0.1, 0.3, 0.3
-    so those experts receive almost no tokens."""
+    element of rows 0..3 (those experts then win for roughly half of all
+    tokens), and the last four rows scaled by 0.1, 0.1, 0.3, 0.3 so those
+    experts receive almost no tokens."""
     s = _streams(seed)
-    H, E, I, Is = shape.H, shape.E, shape.I, shape.Is
-    wr = _normal_fill(s["w_router"], E * H, 0.02, _W_ELEMS_PER_CHUNK, F32)
-    wr = wr.reshape(E, H)
+    H, E = shape.H, shape.E
+    wr = _normal_fill(s["w_router"], E * H, 0.02, _W_ELEMS_PER_CHUNK, F32).reshape(E, H)
     if skew:
         if E < 8:
             raise ValueError("skewed router needs E >= 8")
         wr[0:4] += np.float32(0.5)
         wr[E - 4:E - 2] *= np.float32(0.1)
         wr[E - 2:E] *= np.float32(0.3)
+    return wr
+
+
+def make_expert_weights(shape: LayerShape, seed: int = 0) -> dict:
+    """Fused expert projections W13 [E,2I,H] (rows [0,I) up, [I,2I) gate);
+    down projections W2 [E,H,I]; shared expert Ws13 [2Is,H] and Ws2 [H,Is].
+    All N(0, 0.02^2), in the layer dtype."""
+    s = _streams(seed)
+    H, E, I, Is = shape.H, shape.E, shape.I, shape.Is
     dt = shape.dtype
     w13 = _normal_fill(s["w13"], E * 2 * I * H, 0.02, _W_ELEMS_PER_CHUNK, dt)
     w2 = _normal_fill(s["w2"], E * H * I, 0.02, _W_ELEMS_PER_CHUNK, dt)
     ws13 = _normal_fill(s["ws13"], 2 * Is * H, 0.02, _W_ELEMS_PER_CHUNK, dt)
     ws2 = _normal_fill(s["ws2"], H * Is, 0.02, _W_ELEMS_PER_CHUNK, dt)
     return {
-        "w_router": wr,
         "w13": w13.reshape(E, 2 * I, H),
         "w2": w2.reshape(E, H, I),
         "ws13": ws13.reshape(2 * Is, H),
         "ws2": ws2.reshape(H, Is),
     }
+
+
+def make_weights(shape: LayerShape, seed: int = 0, skew: bool = False) -> dict:
+    """Router weight plus all expert weights (see the two functions above)."""
+    d = make_expert_weights(shape, seed)
+    d["w_router"] = make_router_weight(shape, seed, skew)
+    return d
 
 
 def make_x(wl: Workload, seed: int = 0) -> tuple:
