@@ -13,6 +13,7 @@ timed on a bounded sample of the same workload on this host's cores.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -90,6 +91,49 @@ def gemm_flops(wl):
     }
 
 
+GEMM_SOURCES = ("moe_decoder_ffn_amd/csrc/gemm.hip", "moe_decoder_ffn_amd/csrc/common.h")
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+    reading for a plain copy of known size), or None if there is none for
+    this workload or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_up_gate_swiglu_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != gemm_source_hash():
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    byte counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
 def cpu_baseline(wl, d, K, target_s):
     """The CPU oracle as it stands, on a bounded sample of real tokens."""
     import oracle
@@ -123,7 +167,12 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        copy_calibration(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is measured on one GPU's share)", file=sys.stderr)
@@ -216,7 +265,7 @@ def main():
     roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(wl.name)}
 
     cpu = None
     if args.cpu_seconds > 0:

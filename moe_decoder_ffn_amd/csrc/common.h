@@ -25,10 +25,27 @@ constexpr int kMaxE = 64;
 // the same blocking.
 constexpr int kRouterTB = 32;
 
-// bf16 grouped GEMM tile.
-constexpr int kGemmBM = 256;
+// bf16 grouped GEMM tile: rows x weight rows x k step, LDS stages.
+#ifndef HI3_GEMM_BM
+#define HI3_GEMM_BM 128
+#endif
+#ifndef HI3_GEMM_BK
+#define HI3_GEMM_BK 64
+#endif
+#ifndef HI3_GEMM_STAGES
+#define HI3_GEMM_STAGES 3
+#endif
+#ifndef HI3_GEMM_WN
+#define HI3_GEMM_WN 4
+#endif
+#ifndef HI3_GEMM_SCHED
+#define HI3_GEMM_SCHED 1
+#endif
+constexpr int kGemmBM = HI3_GEMM_BM;
 constexpr int kGemmBN = 256;
-constexpr int kGemmBK = 64;
+constexpr int kGemmBK = HI3_GEMM_BK;
+constexpr int kGemmStages = HI3_GEMM_STAGES;
+constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
 // fp32 grouped GEMM tile.
 constexpr int kGemmF32BM = 64;
 constexpr int kGemmF32BN = 64;
