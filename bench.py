@@ -75,8 +75,6 @@ def stage_bytes(wl):
     return {
         # x read once, fp32 router weight (split once into 3 bf16 terms), routes written
         "router": Tv * H * es + E * H * 4 + T * K * 8,
-        # x rows read once, written to K slots
-        "gather": Tv * H * es * (1 + K),
         # K fp32 expert rows + the fp32 shared row read, one output row written
         "combine": Tv * (K * H * 4 + H * 4 + H * es + K * 8),
     }

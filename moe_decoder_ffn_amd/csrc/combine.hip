@@ -8,28 +8,55 @@
 
 namespace hi3 {
 
-template <int DT>
+// KT > 0: K is known at compile time (the slots and weights of the token
+// stay in registers); KT = 0: any K. The fp32 expert rows are read once, so
+// their loads are marked non-temporal.
+template <int DT, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t t = blockIdx.x;
   if (a.pad && a.pad[t]) return;
   const int vi = a.vidx[t];
   if (vi < 0) return;
-  const int K = a.K;
+  const int K = KT > 0 ? KT : a.K;
   const int nq = a.H / 4;
   const f32x4_t *ys = reinterpret_cast<const f32x4_t *>(a.ys + static_cast<int64_t>(vi) * a.H);
+  int slot[KT > 0 ? KT : 1];
+  float wk[KT > 0 ? KT : 1];
+  if (KT > 0) {
+#pragma unroll
+    for (int k = 0; k < (KT > 0 ? KT : 1); ++k) {
+      slot[k] = a.slotof[t * K + k];
+      wk[k] = a.wts[t * K + k];
+    }
+  }
   for (int q = threadIdx.x; q < nq; q += blockDim.x) {
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < K; ++k) {
-      const int s = a.slotof[t * K + k];
-      const float w = a.wts[t * K + k];
-      const f32x4_t v =
-          reinterpret_cast<const f32x4_t *>(a.y + static_cast<int64_t>(s) * a.H)[q];
-      acc[0] = fmaf(w, v[0], acc[0]);
-      acc[1] = fmaf(w, v[1], acc[1]);
-      acc[2] = fmaf(w, v[2], acc[2]);
-      acc[3] = fmaf(w, v[3], acc[3]);
+    if (KT > 0) {
+      f32x4_t v[KT > 0 ? KT : 1];
+#pragma unroll
+      for (int k = 0; k < (KT > 0 ? KT : 1); ++k)
+        v[k] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t *>(a.y + static_cast<int64_t>(slot[k]) * a.H) + q);
+#pragma unroll
+      for (int k = 0; k < (KT > 0 ? KT : 1); ++k) {
+        acc[0] = fmaf(wk[k], v[k][0], acc[0]);
+        acc[1] = fmaf(wk[k], v[k][1], acc[1]);
+        acc[2] = fmaf(wk[k], v[k][2], acc[2]);
+        acc[3] = fmaf(wk[k], v[k][3], acc[3]);
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const int s = a.slotof[t * K + k];
+        const float w = a.wts[t * K + k];
+        const f32x4_t v = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t *>(a.y + static_cast<int64_t>(s) * a.H) + q);
+        acc[0] = fmaf(w, v[0], acc[0]);
+        acc[1] = fmaf(w, v[1], acc[1]);
+        acc[2] = fmaf(w, v[2], acc[2]);
+        acc[3] = fmaf(w, v[3], acc[3]);
+      }
     }
-    const f32x4_t sv = ys[q];
+    const f32x4_t sv = __builtin_nontemporal_load(ys + q);
     acc[0] += sv[0];
     acc[1] += sv[1];
     acc[2] += sv[2];
@@ -47,10 +74,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, int dtype, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(combine_kernel<kBF16>, dim3(static_cast<unsigned>(a.T)), dim3(256), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(a.T));
+  if (dtype == kBF16 && a.K == 8)
+    hipLaunchKernelGGL((combine_kernel<kBF16, 8>), grid, dim3(256), 0, s, a);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL((combine_kernel<kBF16, 0>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(combine_kernel<kF32>, dim3(static_cast<unsigned>(a.T)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<kF32, 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

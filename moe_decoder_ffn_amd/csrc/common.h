@@ -24,6 +24,8 @@ constexpr int kMaxE = 64;
 // the per-block expert histograms that the stable counting sort scans use
 // the same blocking.
 constexpr int kRouterTB = 32;
+// The bf16 router splits the hidden dimension over at most this many slices.
+constexpr int kRouterMaxSlices = 16;
 
 // bf16 grouped GEMM tile: rows x weight rows x k step, LDS stages.
 #ifndef HI3_GEMM_BM
@@ -105,6 +107,9 @@ __device__ __forceinline__ int wave_uniform(int v) {
 
 // ---------------------------------------------------------------- plan
 
+// Number of hidden-dimension slices the bf16 router splits the logits over.
+int router_slices(int64_t T, int H);
+
 // Byte offsets of every buffer inside the caller's workspace. Buffers that
 // depend on the expert sizes come last, so the route/dispatch layout
 // (I = Is = 0) is a prefix of the forward layout.
@@ -116,6 +121,7 @@ struct Plan {
   int BM;         // grouped-GEMM tile rows (per dtype)
   int max_tiles;  // upper bound on grouped-GEMM row tiles
   size_t wsplit;  // [3][Epad][H] bf16: router weight split into 3 bf16 terms
+  size_t rpart;   // [slices][E][T] fp32: router partial logits
   size_t idx;     // [T*K] int32 routes when the caller passes none
   size_t wts;     // [T*K] fp32
   size_t blkcnt;  // [NB][E] int32 per-block expert histogram
@@ -131,7 +137,6 @@ struct Plan {
   size_t slotof;  // [T*K] int32 (token, k) -> slot
   size_t vtok;    // [T] int32 real-row index -> token
   size_t vidx;    // [T] int32 token -> real-row index (-1 padding)
-  size_t xs;      // [T*K, H] dtype: rows grouped by expert
   size_t h;       // [T*K, I] dtype: SwiGLU activations of routed rows
   size_t hs;      // [T, Is] dtype: SwiGLU activations of the shared expert
   size_t y;       // [T*K, H] fp32: routed expert outputs by slot
@@ -157,6 +162,7 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) 
     return at;
   };
   p.wsplit = take(dtype == kBF16 ? 3ull * p.Epad * H * 2 : 0);
+  p.rpart = take(static_cast<size_t>(dtype == kBF16 ? router_slices(T, H) : 1) * T * E * 4);
   p.idx = take(TK * 4);
   p.wts = take(TK * 4);
   p.blkcnt = take(static_cast<size_t>(p.NB) * E * 4);
@@ -173,7 +179,6 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) 
   p.vtok = take(T * 4);
   p.vidx = take(T * 4);
   if (I > 0) {
-    p.xs = take(TK * H * es);
     p.h = take(TK * I * es);
     p.hs = take(T * Is * es);
     p.y = take(TK * H * 4);
@@ -261,7 +266,8 @@ struct CombineArgs {
 
 hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, int Epad,
                                int H, hipStream_t s);
-hipError_t launch_router(const RouterArgs &a, int dtype, hipStream_t s);
+// partial: [slices][E][T] fp32 scratch (one slice for fp32 layers).
+hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStream_t s);
 hipError_t launch_histogram(const int32_t *idx, const uint8_t *pad, int64_t T, int E,
                             int K, int32_t *blkcnt, int32_t *blkval, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);

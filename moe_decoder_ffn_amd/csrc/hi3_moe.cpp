@@ -76,7 +76,6 @@ int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
   int32_t *vidx = static_cast<int32_t *>(at(p.vidx));
   const int4 *tiles = static_cast<const int4 *>(at(p.tiles));
   const int32_t *gto = static_cast<const int32_t *>(at(p.gto));
-  const size_t es = dtype == HI3_BF16 ? 2 : 4;
   Recorder rec{events, s};
 
   // 0: router weight split (bf16 layers only)
@@ -87,7 +86,7 @@ int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
   rec.at(1);
   RouterArgs ra{x, w_router, static_cast<const uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
                 p.Epad, idx, wts, blkcnt, blkval};
-  HI3_TRY(launch_router(ra, dtype, s));
+  HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
   // 2: scans -> expert offsets, real-row list, GEMM row tiles
   rec.at(2);
   ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
@@ -98,23 +97,22 @@ int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
   HI3_TRY(launch_scan(sa, s));
   // 3: stable slots
   rec.at(3);
-  ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K,
-                 static_cast<int32_t *>(at(p.perm)), slotof, vtok, vidx};
+  int32_t *perm = static_cast<int32_t *>(at(p.perm));
+  ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm, slotof, vtok, vidx};
   HI3_TRY(launch_scatter(sc, s));
-  // 4: gather token rows into expert-grouped order
+  // 4: grouped [up; gate] projection + SwiGLU (routed experts and the shared
+  // expert); the routed rows are gathered from x through the slot -> token map
+  // by the GEMM's operand copies, so no grouped copy of x is materialised
   rec.at(4);
-  HI3_TRY(launch_gather(x, static_cast<int64_t>(H) * es, slotof, pad_mask, T, K, at(p.xs), s));
-  // 5: grouped [up; gate] projection + SwiGLU (routed experts and the shared expert)
-  rec.at(5);
   GemmArgs up{};
-  up.cls[0] = GemmClass{at(p.xs), H, nullptr, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
+  up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
   up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
   up.tiles = tiles;
   up.gto = gto;
   up.E = E;
   HI3_TRY(launch_gemm_upgate(up, p.max_tiles, dtype, s));
-  // 6: grouped down projection
-  rec.at(6);
+  // 5: grouped down projection
+  rec.at(5);
   GemmArgs dn{};
   dn.cls[0] = GemmClass{at(p.h), I, nullptr, w_down, int64_t{H} * I, at(p.y), H, H, I};
   dn.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
@@ -122,12 +120,12 @@ int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
   dn.gto = gto;
   dn.E = E;
   HI3_TRY(launch_gemm_down(dn, p.max_tiles, dtype, s));
-  // 7: combine
-  rec.at(7);
+  // 6: combine
+  rec.at(6);
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                  slotof, vidx, wts, pad_mask, T, H, K, out};
   HI3_TRY(launch_combine(ca, dtype, s));
-  rec.at(8);
+  rec.at(7);
   return rec.ok ? HI3_OK : HI3_E_HIP;
 }
 
@@ -164,7 +162,7 @@ int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask,
   RouterArgs ra{x, w_router, static_cast<const uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
                 p.Epad, topk_idx, topk_w, static_cast<int32_t *>(at(p.blkcnt)),
                 static_cast<int32_t *>(at(p.blkval))};
-  HI3_TRY(launch_router(ra, dtype, s));
+  HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
   if (expert_counts) {
     ScanArgs sa{ra.blkcnt, ra.blkval, p.NB, E, p.BM,
                 static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
@@ -243,7 +241,7 @@ int hi3_moe_forward_instrumented(const void *x, const float *w_router, const voi
 const char *hi3_moe_stage_name(int stage) {
   static const char *names[HI3_NUM_STAGES] = {
       "router_weight_split", "router", "scan", "scatter",
-      "gather", "gemm_up_gate_swiglu", "gemm_down", "combine"};
+      "gemm_up_gate_swiglu", "gemm_down", "combine"};
   if (stage < 0 || stage >= HI3_NUM_STAGES) return "?";
   return names[stage];
 }

@@ -12,11 +12,26 @@
 //
 // The same kernel also builds the per-block expert histogram that the
 // stable counting sort scans (block b covers tokens [32b, 32b + 32)).
+#include <algorithm>
+
 #include "common.h"
 
 namespace hi3 {
 
 // --------------------------------------------------------------- weight split
+
+// Output layout ("fragment order"): for split term sp, 32-expert column
+// tile n, 64-wide k chunk c and MFMA step q, the 64 lanes' 8-element pieces
+// lie next to each other (lane = 32 g + r holds expert 32 n + r, k =
+// 64 c + 32 g + 8 q + [0, 8)), so the router reads each B fragment as one
+// contiguous 1 KiB block.
+__device__ __forceinline__ int64_t wsplit_index(int sp, int e, int h, int ns, int nchunks) {
+  const int n = e >> 5, r = e & 31;
+  const int c = h >> 6, w = h & 63;
+  const int g = w >> 5, q = (w & 31) >> 3, j = w & 7;
+  const int lane = g * 32 + r;
+  return ((((static_cast<int64_t>(sp) * ns + n) * nchunks + c) * 4 + q) * 64 + lane) * 8 + j;
+}
 
 __global__ __launch_bounds__(256) void split_router_kernel(const float *__restrict__ wr,
                                                            uint16_t *__restrict__ ws,
@@ -25,15 +40,17 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int e = static_cast<int>(i / H);
+  const int h = static_cast<int>(i % H);
   const float v = e < E ? wr[i] : 0.0f;
   // Truncating to the top 8 significand bits leaves an exact remainder.
   const uint32_t hi = __float_as_uint(v) & 0xFFFF0000u;
   const float r1 = v - __uint_as_float(hi);
   const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
   const float r2 = r1 - __uint_as_float(mid);
-  ws[i] = static_cast<uint16_t>(hi >> 16);
-  ws[n + i] = static_cast<uint16_t>(mid >> 16);
-  ws[2 * n + i] = f32_to_bf16(r2);  // at most 8 significant bits: exact
+  const int ns = Epad / 32, nchunks = H / 64;
+  ws[wsplit_index(0, e, h, ns, nchunks)] = static_cast<uint16_t>(hi >> 16);
+  ws[wsplit_index(1, e, h, ns, nchunks)] = static_cast<uint16_t>(mid >> 16);
+  ws[wsplit_index(2, e, h, ns, nchunks)] = f32_to_bf16(r2);  // at most 8 significant bits: exact
 }
 
 hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, int Epad,
@@ -46,83 +63,149 @@ hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, i
 
 // --------------------------------------------------------------- selection
 
-struct RouterShared {
-  float logit[kRouterTB][kMaxE + 1];
+// Softmax over all experts, top-K and renormalisation for 32 tokens per
+// block: 8 waves, one token per wave at a time, lane = expert; then the
+// block's expert histogram and real-row count.
+// The token's logits are the slice partials summed in slice order. Every
+// lane reads all of the token's logits from LDS (broadcast reads, no
+// cross-lane shuffles) to get the maximum and its own rank in the selection
+// order (larger logit first, lower index first on equal logits; softmax is
+// strictly increasing, so this is the order of the probabilities, and fp32
+// underflow of small probabilities cannot change it). Z sums exp(l - max) in
+// ascending expert order, the selected p = exp(l - max) / Z are summed in
+// selection order, and each is divided by that sum.
+// partial: [slices][E][T] fp32. EC = 64: E is 64 (no per-expert guards);
+// EC = 0: any E <= 64.
+struct SelectShared {
+  float logit[kRouterTB][kMaxE + 4];  // 16-byte aligned rows
+  float ex[kRouterTB][kMaxE + 4];
+  float psel[kRouterTB][kMaxE];
+  int esel[kRouterTB][kMaxE];
   uint64_t selmask[kRouterTB];
 };
 
-// Softmax over all experts, top-K, renormalisation for the token in
-// LDS row rr; one wavefront, lane = expert. Writes the routes and the
-// selection bitmask.
-__device__ void select_row(const RouterArgs &a, RouterShared &sh, int rr, int lane,
-                           int64_t t) {
-  const bool is_pad = a.pad && a.pad[t];
-  if (is_pad) {
-    if (lane < a.K) {
-      a.idx[t * a.K + lane] = -1;
-      a.wts[t * a.K + lane] = 0.0f;
-    }
-    if (lane == 0) sh.selmask[rr] = 0;
-    return;
-  }
-  const bool live = lane < a.E;
-  const float l = live ? sh.logit[rr][lane] : -INFINITY;
-  const float m = wave_max(l);
-  const float ex = live ? expf(l - m) : 0.0f;
-  const float z = wave_sum_uniform(ex);
-  const float p = ex / z;
-  // Top-K is taken on the logits: softmax is strictly increasing, so this is
-  // the exact order of the probabilities, and it does not depend on which
-  // small probabilities underflow in fp32. Equal logits: lower index first.
-  bool avail = live;
-  int my_e = -1;
-  float my_p = 0.0f;
-  float s = 0.0f;
-  uint64_t mask = 0;
-  for (int k = 0; k < a.K; ++k) {
-    float bv = avail ? l : -INFINITY;
-    int be = avail ? lane : 0x7fffffff;
-    wave_argmax(bv, be);
-    const float pb = __shfl(p, be, kWave);
-    if (lane == k) {
-      my_e = be;
-      my_p = pb;
-    }
-    if (lane == be) avail = false;
-    s += pb;  // in k order
-    mask |= 1ull << be;
-  }
-  if (lane < a.K) {
-    a.idx[t * a.K + lane] = my_e;
-    a.wts[t * a.K + lane] = my_p / s;
-  }
-  if (lane == 0) sh.selmask[rr] = mask;
+// Orders this wave's LDS writes before its following LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Per-block histogram of selected experts and count of real rows.
-__device__ void block_histogram(const RouterArgs &a, RouterShared &sh, int64_t t0) {
+template <int EC>
+__global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const float *partial,
+                                                            int slices) {
+  __shared__ SelectShared sh;
+  const int E = EC > 0 ? EC : a.E;
+  const int K = a.K;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
+
+  // logits of the block's tokens: thread (expert e, token rr) sums the
+  // slices; the slice reads are issued together
+  for (int i = threadIdx.x; i < kRouterTB * E; i += blockDim.x) {
+    const int e = i / kRouterTB, rr = i % kRouterTB;
+    const int64_t tt = t0 + rr;
+    float v[kRouterMaxSlices];
+#pragma unroll
+    for (int ks = 0; ks < kRouterMaxSlices; ++ks)
+      v[ks] = (ks < slices && tt < a.T)
+                  ? partial[(static_cast<int64_t>(ks) * E + e) * a.T + tt]
+                  : 0.0f;
+    float l = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kRouterMaxSlices; ++ks)
+      if (ks < slices) l += v[ks];
+    sh.logit[rr][e] = l;
+  }
+  __syncthreads();
+
+  for (int rr = wave; rr < kRouterTB; rr += blockDim.x >> 6) {
+    const int64_t t = t0 + rr;
+    if (t >= a.T) {
+      if (lane == 0) sh.selmask[rr] = 0;
+      continue;
+    }
+    if (a.pad && a.pad[t]) {
+      if (lane < K) {
+        a.idx[t * K + lane] = -1;
+        a.wts[t * K + lane] = 0.0f;
+      }
+      if (lane == 0) sh.selmask[rr] = 0;
+      continue;
+    }
+    const bool live = lane < E;
+    const float l = live ? sh.logit[rr][lane] : -INFINITY;
+    float m = -INFINITY;
+    int rank = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 4; ++i) {
+      if (EC == 0 && 4 * i >= E) break;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&sh.logit[rr][4 * i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * i + q;
+        if (EC == 0 && e >= E) break;
+        m = fmaxf(m, v[q]);
+        rank += (v[q] > l || (v[q] == l && e < lane)) ? 1 : 0;
+      }
+    }
+    const float ex = live ? expf(l - m) : 0.0f;
+    if (live) sh.ex[rr][lane] = ex;
+    wave_lds_sync();
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 4; ++i) {
+      if (EC == 0 && 4 * i >= E) break;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&sh.ex[rr][4 * i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (EC == 0 && 4 * i + q >= E) break;
+        z += v[q];  // ascending expert order
+      }
+    }
+    const float p = ex / z;
+    const bool sel = live && rank < K;
+    if (sel) {
+      sh.psel[rr][rank] = p;
+      sh.esel[rr][rank] = lane;
+    }
+    const uint64_t mask = __ballot(sel);
+    wave_lds_sync();
+    if (lane < K) {
+      float ssum = 0.0f;
+      for (int k = 0; k < K; ++k) ssum += sh.psel[rr][k];  // selection order
+      a.idx[t * K + lane] = sh.esel[rr][lane];
+      a.wts[t * K + lane] = sh.psel[rr][lane] / ssum;
+    }
+    if (lane == 0) sh.selmask[rr] = mask;
+  }
+  __syncthreads();
+
   const int tid = threadIdx.x;
-  if (tid < a.E) {
+  if (tid < E) {
     int c = 0;
     for (int rr = 0; rr < kRouterTB; ++rr) c += static_cast<int>((sh.selmask[rr] >> tid) & 1u);
-    a.blkcnt[static_cast<int64_t>(blockIdx.x) * a.E + tid] = c;
+    a.blkcnt[static_cast<int64_t>(blockIdx.x) * E + tid] = c;
   }
-  if (tid == 64) {
-    int c = 0;
-    for (int rr = 0; rr < kRouterTB; ++rr) {
-      const int64_t t = t0 + rr;
-      c += (t < a.T && !(a.pad && a.pad[t])) ? 1 : 0;
-    }
-    a.blkval[blockIdx.x] = c;
+  if (tid >= 64 && tid < 64 + kRouterTB) {
+    const int rr = tid - 64;
+    const int64_t t = t0 + rr;
+    const bool ok = t < a.T && !(a.pad && a.pad[t]);
+    const uint64_t bal = __ballot(ok);
+    if (rr == 0) a.blkval[blockIdx.x] = __popcll(bal);
   }
 }
 
 // --------------------------------------------------------------- bf16 router
 
-// 256 threads = 4 waves; block covers 32 tokens; wave w accumulates the
-// 64-wide k chunks c = w, w+4, ... of all 32 tokens x Epad experts with
-// v_mfma_f32_32x32x16_bf16, then the 4 partial logit tiles are summed in a
-// fixed order in LDS.
+// Partial logits of 32 tokens over one slice of the hidden dimension.
+// Grid: x = blocks of 32 tokens, y = k slices (each a range of 64-wide
+// chunks). 256 threads = 4 waves; wave w accumulates the chunks
+// c = first + w, first + w + 4, ... of all 32 tokens x Epad experts with
+// v_mfma_f32_32x32x16_bf16, the 4 wave partials are summed in a fixed order
+// in LDS and written to partial[slice][e][t]. Splitting the hidden dimension
+// across blocks gives the machine enough waves at a few thousand tokens.
 //
 // MFMA operand layout used here (32x32x16): lane l supplies row (l % 32) of
 // A and column (l % 32) of B, and 8 consecutive k values; lanes 0-31 and
@@ -132,9 +215,9 @@ __device__ void block_histogram(const RouterArgs &a, RouterShared &sh, int64_t t
 // 64 contiguous bytes per operand row. Result element v of lane l is
 // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
 template <int NS>
-__global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void router_partial_kernel(RouterArgs a, float *partial, int chunks_per_slice) {
   __shared__ float part[4][kRouterTB][NS * 32 + 1];
-  __shared__ RouterShared sh;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31;
@@ -144,7 +227,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
   const bool row_ok = t < a.T && !(a.pad && a.pad[t]);
   const uint16_t *x = static_cast<const uint16_t *>(a.x);
   const uint16_t *xrow = x + (row_ok ? t : 0) * static_cast<int64_t>(a.H);
-  const int64_t plane = static_cast<int64_t>(a.Epad) * a.H;
+  const int nchunks = a.H / 64;
 
   f32x16_t acc_hi[NS], acc_lo[NS];
 #pragma unroll
@@ -155,10 +238,14 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
       acc_lo[n][v] = 0.0f;
     }
 
-  const int nchunks = a.H / 64;
-  for (int c = wave; c < nchunks; c += 4) {
+  const int c_first = blockIdx.y * chunks_per_slice;
+  const int c_end = min(nchunks, c_first + chunks_per_slice);
+  for (int c = c_first + wave; c < c_end; c += 4) {
+    // every operand of the chunk is requested before the first MFMA, so the
+    // loads are in flight together
     const int k0 = c * 64 + g * 32;
     u32x4_t av[4];
+    u32x4_t bv[NS][3][4];
     if (row_ok) {
       const u32x4_t *p = reinterpret_cast<const u32x4_t *>(xrow + k0);
 #pragma unroll
@@ -168,25 +255,31 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
       for (int q = 0; q < 4; ++q) av[q] = u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
+    for (int n = 0; n < NS; ++n)
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp) {
-        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(
-            a.wsplit + sp * plane + static_cast<int64_t>(n * 32 + r) * a.H + k0);
-        u32x4_t bv[4];
+        // fragment order: the 4 steps' 1 KiB blocks of (sp, n, c) are adjacent
+        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(a.wsplit) +
+                           (((static_cast<int64_t>(sp) * NS + n) * nchunks + c) * 4) * 64 + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bv[q] = p[q];
+        for (int q = 0; q < 4; ++q) bv[n][sp][q] = p[q * 64];
+      }
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[q]);
-          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bv[q]);
+          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bv[n][sp][q]);
           if (sp == 0)
             acc_hi[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc_hi[n], 0, 0, 0);
           else
             acc_lo[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc_lo[n], 0, 0, 0);
         }
-      }
-    }
+    // all of the chunk's loads are issued before its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, 4 + NS * 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NS * 12, 0);
   }
 #pragma unroll
   for (int n = 0; n < NS; ++n)
@@ -194,29 +287,30 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
     for (int v = 0; v < 16; ++v)
       part[wave][(v >> 2) * 8 + g * 4 + (v & 3)][n * 32 + r] = acc_hi[n][v] + acc_lo[n][v];
   __syncthreads();
+  float *out = partial + static_cast<int64_t>(blockIdx.y) * a.E * a.T;
   for (int i = threadIdx.x; i < kRouterTB * a.E; i += blockDim.x) {
-    const int rr = i / a.E, e = i % a.E;
-    sh.logit[rr][e] = ((part[0][rr][e] + part[1][rr][e]) + part[2][rr][e]) + part[3][rr][e];
-  }
-  __syncthreads();
-  for (int rr = wave; rr < kRouterTB; rr += 4) {
+    const int e = i / kRouterTB, rr = i % kRouterTB;
     const int64_t tt = t0 + rr;
-    if (tt >= a.T) {
-      if (lane == 0) sh.selmask[rr] = 0;
-      continue;
-    }
-    select_row(a, sh, rr, lane, tt);
+    if (tt < a.T)
+      out[static_cast<int64_t>(e) * a.T + tt] =
+          ((part[0][rr][e] + part[1][rr][e]) + part[2][rr][e]) + part[3][rr][e];
   }
-  __syncthreads();
-  block_histogram(a, sh, t0);
+}
+
+int router_slices(int64_t T, int H) {
+  const int nb = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
+  // at least one chunk per wave, at most kRouterMaxSlices
+  const int max_slices = std::max(1, std::min(kRouterMaxSlices, H / 256));
+  const int want = (512 + nb - 1) / nb;  // about two waves per SIMD
+  return std::max(1, std::min(max_slices, want));
 }
 
 // --------------------------------------------------------------- fp32 router
 
 // fp32 activations: plain fp32 FMA dot products (lane = expert, one token
-// per wave at a time); used for the small fp32 layers.
-__global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
-  __shared__ RouterShared sh;
+// per wave at a time), written as a single slice of partial logits for the
+// selection kernel; used for the small fp32 layers.
+__global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a, float *partial) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
@@ -229,31 +323,33 @@ __global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a) {
       const float *wrow = a.w_router + static_cast<int64_t>(lane) * a.H;
       float acc = 0.0f;
       for (int h = 0; h < a.H; ++h) acc = fmaf(xr[h], wrow[h], acc);
-      sh.logit[rr][lane] = acc;
+      partial[static_cast<int64_t>(lane) * a.T + t] = acc;
     }
   }
-  __syncthreads();
-  for (int rr = wave; rr < kRouterTB; rr += 4) {
-    const int64_t tt = t0 + rr;
-    if (tt >= a.T) {
-      if (lane == 0) sh.selmask[rr] = 0;
-      continue;
-    }
-    select_row(a, sh, rr, lane, tt);
-  }
-  __syncthreads();
-  block_histogram(a, sh, t0);
 }
 
-hipError_t launch_router(const RouterArgs &a, int dtype, hipStream_t s) {
+hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStream_t s) {
   const int nb = static_cast<int>((a.T + kRouterTB - 1) / kRouterTB);
+  int slices = 1;
   if (dtype == kF32) {
-    hipLaunchKernelGGL(router_f32_kernel, dim3(nb), dim3(256), 0, s, a);
-  } else if (a.Epad <= 32) {
-    hipLaunchKernelGGL(router_bf16_kernel<1>, dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(router_f32_kernel, dim3(nb), dim3(256), 0, s, a, partial);
   } else {
-    hipLaunchKernelGGL(router_bf16_kernel<2>, dim3(nb), dim3(256), 0, s, a);
+    slices = router_slices(a.T, a.H);
+    const int cps = (a.H / 64 + slices - 1) / slices;
+    if (a.Epad <= 32)
+      hipLaunchKernelGGL(router_partial_kernel<1>, dim3(nb, slices), dim3(256), 0, s, a,
+                         partial, cps);
+    else
+      hipLaunchKernelGGL(router_partial_kernel<2>, dim3(nb, slices), dim3(256), 0, s, a,
+                         partial, cps);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.E == kMaxE)
+    hipLaunchKernelGGL(router_select_kernel<kMaxE>, dim3(nb), dim3(512), 0, s, a, partial,
+                       slices);
+  else
+    hipLaunchKernelGGL(router_select_kernel<0>, dim3(nb), dim3(512), 0, s, a, partial, slices);
   return hipGetLastError();
 }
 
