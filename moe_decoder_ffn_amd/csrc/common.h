@@ -40,8 +40,11 @@ constexpr int kRouterMaxSlices = 16;
 #ifndef HI3_GEMM_WN
 #define HI3_GEMM_WN 4
 #endif
-#ifndef HI3_GEMM_SCHED
-#define HI3_GEMM_SCHED 1
+#ifndef HI3_GEMM_XCD_REMAP
+#define HI3_GEMM_XCD_REMAP 1
+#endif
+#ifndef HI3_GEMM_NFAST
+#define HI3_GEMM_NFAST 0
 #endif
 constexpr int kGemmBM = HI3_GEMM_BM;
 constexpr int kGemmBN = 256;

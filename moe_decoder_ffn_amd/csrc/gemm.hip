@@ -19,6 +19,7 @@
 // same time on the same XCD and its L2 serves the repeats.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -43,10 +44,14 @@ __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   const int ntiles = a.gto[a.E + 1];
   const int W = ntiles * a.NTn;
   const int bid = blockIdx.x;
+#if HI3_GEMM_XCD_REMAP
   const int xcd = bid & 7, slot = bid >> 3;
   const int per = (W + 7) >> 3;
   if (slot >= per) return false;
   const int L = xcd * per + slot;
+#else
+  const int L = bid;
+#endif
   if (L >= W) return false;
   // group: the largest g with gto[g] * NTn <= L (empty groups have empty ranges)
   int lo = 0, hi = a.E;
@@ -58,8 +63,13 @@ __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   const int first = a.gto[g];
   const int cnt = a.gto[g + 1] - first;
   const int off = L - first * a.NTn;
+#if HI3_GEMM_NFAST
+  const int nt = off % a.NTn;
+  const int mt = first + off / a.NTn;
+#else
   const int nt = off / cnt;
   const int mt = first + off % cnt;
+#endif
   const int4 tile = a.tiles[mt];
   j.g = tile.x;
   j.row0 = tile.y;
@@ -130,6 +140,16 @@ __device__ __forceinline__ void barrier_no_fence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time.
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int S, int NST>
 struct StageRing {
   static constexpr int prev = (S + NST - 1) % NST;
@@ -162,12 +182,17 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int MI = BM / 64;               // 32-row sub-tiles per wave
   constexpr int NI = BN / WN / 32;          // 32-column sub-tiles per wave
   constexpr int AE = BM * L::CPR, BE = BN * L::CPR;
-  static_assert(BN == 256 && (BM == 128 || BM == 256) && (BK == 32 || BK == 64), "tile");
-  static_assert(NST == 2 || NST == 3, "stages");
+  static_assert(BN == 256 && BM % 64 == 0 && BM <= 256 && (BK == 32 || BK == 64), "tile");
+  static_assert(NST >= 2 && NST <= 5, "stages");
+  static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
+  static_assert(BM % (L::RPC * NW) == 0 && BN % (L::RPC * NW) == 0,
+                "each wave copies a whole number of 1 KiB row groups");
   static_assert(A_CP >= 1 && B_CP >= 1 && (NST - 2) * CPW < 64, "copy counts");
   static_assert(WN == 2 || WN == 4, "wave grid");
   __shared__ u32x4_t sA0[AE], sB0[BE], sA1[AE], sB1[BE];
   __shared__ u32x4_t sA2[NST > 2 ? AE : 1], sB2[NST > 2 ? BE : 1];
+  __shared__ u32x4_t sA3[NST > 3 ? AE : 1], sB3[NST > 3 ? BE : 1];
+  __shared__ u32x4_t sA4[NST > 4 ? AE : 1], sB4[NST > 4 ? BE : 1];
 
   TileJob j;
   if (!resolve_job<MODE, BN>(a, j)) return;
@@ -200,10 +225,13 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
     const int ri = j.row0 + rr;
     arow_src[q] = arow ? arow[ri] : ri;
   }
-  auto issue = [&](int kc, u32x4_t *la, u32x4_t *lb) {
+  // Copies [q0, q1) of this wave (A copies first, then B) for k step kc.
+  auto issue_range = [&](int kc, u32x4_t *la, u32x4_t *lb, auto Q0, auto Q1) __attribute__((always_inline)) {
+    constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
     const int ko = kc * BK;
 #pragma unroll
     for (int q = 0; q < A_CP; ++q) {
+      if (q < q0 || q >= q1) continue;
       const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
       const int c = (lane % L::CPR) ^ L::swz(row);
       lds_dma16(A + static_cast<int64_t>(arow_src[q]) * lda + ko + c * 8,
@@ -211,6 +239,7 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < B_CP; ++q) {
+      if (A_CP + q < q0 || A_CP + q >= q1) continue;
       const int row = (wave * B_CP + q) * L::RPC + lane / L::CPR;
       const int c = (lane % L::CPR) ^ L::swz(row);
       int brow;
@@ -224,6 +253,10 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
       lds_dma16(B + static_cast<int64_t>(brow) * Kd + ko + c * 8,
                 lb + (wave * B_CP + q) * 64);
     }
+  };
+  auto issue = [&](int kc, u32x4_t *la, u32x4_t *lb) __attribute__((always_inline)) {
+    issue_range(kc, la, lb, std::integral_constant<int, 0>{},
+                std::integral_constant<int, CPW>{});
   };
 
   // weight rows of the wave's sub-tiles: with [up; gate] the first NI/2 are
@@ -245,92 +278,116 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-  auto compute = [&](const u32x4_t *la, const u32x4_t *lb) {
+
+  // One k step from LDS stage (la, lb): NSUB = BK / 16 sub-steps; sub-step
+  // s multiplies fragments read during sub-step s - 1, in MI groups of NI
+  // MFMAs (one group per 32-row A fragment), and reads the fragments of
+  // sub-step s + 1 between those MFMAs. The copies of step kn (into stage
+  // pa, pb) are issued one per group, from the second group on: a copy
+  // waits in the vector-memory queue while the MFMAs just issued keep the
+  // matrix unit busy, whereas a burst of copies would stall the wave (and
+  // its matrix work) until the whole burst was accepted.
+  constexpr int NSUB = BK / 16;
+  constexpr int NR = MI + NI;   // fragment reads per sub-step
+  constexpr int NG = NSUB * MI; // MFMA groups per step
+  static_assert(CPW <= NG - 1, "one copy per MFMA group after the first");
+  auto compute = [&](const u32x4_t *la, const u32x4_t *lb, bool pre, int kn, u32x4_t *pa,
+                     u32x4_t *pb) __attribute__((always_inline)) {
     bf16x8_t af[2][MI], bf[2][NI];
-    auto load = [&](int buf, int s) {
+    // fragment read i (A fragments first, then B) of sub-step s into buffer buf
+    auto read = [&](int buf, int s, int i) __attribute__((always_inline)) {
       const int ch = 2 * s + g;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[buf][mi] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + mi * 32 + r, ch)]);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        bf[buf][ni] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[ni] + r, ch)]);
+      if (i < MI)
+        af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
+      else
+        bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
     };
-    load(0, 0);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < BK / 16) load(cur ^ 1, s + 1);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+    for (int i = 0; i < NR; ++i) read(0, 0, i);
+    static_for<NSUB>([&](auto Sv) __attribute__((always_inline)) {
+      constexpr int s = decltype(Sv)::value;
+      constexpr int cur = s & 1;
+      static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
+        constexpr int mi = decltype(Mv)::value;
+        constexpr int grp = s * MI + mi;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
                                                                 acc[mi][ni], 0, 0, 0);
-    }
-#if HI3_GEMM_SCHED
-    // Issue order: the first sub-step's fragment reads, then for each later
-    // sub-step its reads one by one between the MFMAs of the sub-step before,
-    // so LDS latency hides behind matrix work.
-    constexpr int NR = MI + NI;       // fragment reads per sub-step
-    constexpr int NM = MI * NI;       // MFMAs per sub-step
-    static_assert(NR <= NM, "reads fit between MFMAs");
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        if constexpr (s + 1 < NSUB) {
+          constexpr int i0 = mi * NR / MI, i1 = (mi + 1) * NR / MI;
 #pragma unroll
-    for (int s = 0; s + 1 < BK / 16; ++s) {
+          for (int i = i0; i < i1; ++i) read(cur ^ 1, s + 1, i);
+          // MFMA, read, MFMA, read, ...
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-#endif
+          for (int t = 0; t < (NI > i1 - i0 ? NI : i1 - i0); ++t) {
+            if (t < NI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (t < i1 - i0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (grp >= 1 && grp <= CPW) {
+          if (pre)
+            issue_range(kn, pa, pb, std::integral_constant<int, grp - 1>{},
+                        std::integral_constant<int, grp>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    });
   };
 
-  auto stage_a = [&](auto S) -> u32x4_t * {
-    if constexpr (decltype(S)::value == 0) return sA0;
-    else if constexpr (decltype(S)::value == 1) return sA1;
-    else return sA2;
+  auto stage_a = [&](auto S) __attribute__((always_inline)) -> u32x4_t * {
+    constexpr int v = decltype(S)::value;
+    if constexpr (v == 0) return sA0;
+    else if constexpr (v == 1) return sA1;
+    else if constexpr (v == 2) return sA2;
+    else if constexpr (v == 3) return sA3;
+    else return sA4;
   };
-  auto stage_b = [&](auto S) -> u32x4_t * {
-    if constexpr (decltype(S)::value == 0) return sB0;
-    else if constexpr (decltype(S)::value == 1) return sB1;
-    else return sB2;
+  auto stage_b = [&](auto S) __attribute__((always_inline)) -> u32x4_t * {
+    constexpr int v = decltype(S)::value;
+    if constexpr (v == 0) return sB0;
+    else if constexpr (v == 1) return sB1;
+    else if constexpr (v == 2) return sB2;
+    else if constexpr (v == 3) return sB3;
+    else return sB4;
+  };
+  // Wait until at most n (0 <= n <= NST - 2) later stages of this wave's
+  // copies are still in flight; copies complete in issue order.
+  auto wait_stages = [&](int n) __attribute__((always_inline)) {
+    if constexpr (NST > 4) if (n >= 3) { wait_vmem<3 * CPW>(); return; }
+    if constexpr (NST > 3) if (n >= 2) { wait_vmem<2 * CPW>(); return; }
+    if constexpr (NST > 2) if (n >= 1) { wait_vmem<CPW>(); return; }
+    wait_vmem<0>();
   };
 
   const int nk = Kd / BK;
   // One k step from stage S: start the copy NST - 1 steps ahead into the
   // stage read in the previous step, multiply, then wait for the next
-  // step's copy (counted: later copies may stay in flight) and synchronise.
-  auto step = [&](auto S, int k) {
+  // step's copy (the copies of the steps after it may stay in flight) and
+  // synchronise.
+  auto step = [&](auto S, int k) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     constexpr int p = StageRing<s, NST>::prev;
-    if (k + NST - 1 < nk)
-      issue(k + NST - 1, stage_a(std::integral_constant<int, p>{}),
-            stage_b(std::integral_constant<int, p>{}));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(stage_a(S), stage_b(S));
-    if (NST == 3 && k + 2 < nk)
-      wait_vmem<(NST - 2) * CPW>();
-    else
-      wait_vmem<0>();
+    compute(stage_a(S), stage_b(S), k + NST - 1 < nk, k + NST - 1,
+            stage_a(std::integral_constant<int, p>{}), stage_b(std::integral_constant<int, p>{}));
+    wait_stages(max(min(k + NST - 1, nk - 1) - (k + 1), 0));
     barrier_no_fence();
   };
 
-  issue(0, sA0, sB0);
-  if (NST == 3 && nk > 1) issue(1, sA1, sB1);
-  wait_vmem<NST == 3 ? CPW : 0>();  // stage 0 landed (stage 1 may be in flight)
+  // prologue: stages 0 .. NST - 2 (those that exist), then stage 0 landed
+  static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
+    constexpr int v = decltype(S)::value;
+    if (v < nk) issue(v, stage_a(S), stage_b(S));
+  });
+  wait_stages(min(NST - 2, nk - 1));
   barrier_no_fence();
   int kc = 0;
-  for (; kc + NST <= nk; kc += NST) {
-    step(std::integral_constant<int, 0>{}, kc);
-    step(std::integral_constant<int, 1>{}, kc + 1);
-    if constexpr (NST == 3) step(std::integral_constant<int, 2>{}, kc + 2);
-  }
-  if (kc < nk) step(std::integral_constant<int, 0>{}, kc);
-  if (kc + 1 < nk) step(std::integral_constant<int, 1>{}, kc + 1);
+  for (; kc + NST <= nk; kc += NST)
+    static_for<NST>([&](auto S) __attribute__((always_inline)) { step(S, kc + decltype(S)::value); });
+  static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
+    if (kc + decltype(S)::value < nk) step(S, kc + decltype(S)::value);
+  });
 
   if (MODE == 0) {
     const int Ih = N / 2;
