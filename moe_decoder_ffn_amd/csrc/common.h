@@ -27,29 +27,34 @@ constexpr int kRouterTB = 32;
 // The bf16 router splits the hidden dimension over at most this many slices.
 constexpr int kRouterMaxSlices = 16;
 
-// bf16 grouped GEMM tile: rows x weight rows x k step, LDS stages.
+// bf16 grouped GEMM tiles: rows x 256 weight rows x k step, LDS stages.
+// The row-tile list holds tiles of HI3_GEMM_BM rows (the up/gate tile); the
+// down projection runs each listed tile as HI3_GEMM_DOWN_SPLIT blocks.
 #ifndef HI3_GEMM_BM
-#define HI3_GEMM_BM 128
+#define HI3_GEMM_BM 256
 #endif
 #ifndef HI3_GEMM_BK
 #define HI3_GEMM_BK 64
 #endif
 #ifndef HI3_GEMM_STAGES
-#define HI3_GEMM_STAGES 3
+#define HI3_GEMM_STAGES 2
+#endif
+#ifndef HI3_GEMM_DOWN_SPLIT
+#define HI3_GEMM_DOWN_SPLIT 2
+#endif
+#ifndef HI3_GEMM_DOWN_STAGES
+#define HI3_GEMM_DOWN_STAGES 3
 #endif
 #ifndef HI3_GEMM_WN
 #define HI3_GEMM_WN 4
-#endif
-#ifndef HI3_GEMM_XCD_REMAP
-#define HI3_GEMM_XCD_REMAP 1
-#endif
-#ifndef HI3_GEMM_NFAST
-#define HI3_GEMM_NFAST 0
 #endif
 constexpr int kGemmBM = HI3_GEMM_BM;
 constexpr int kGemmBN = 256;
 constexpr int kGemmBK = HI3_GEMM_BK;
 constexpr int kGemmStages = HI3_GEMM_STAGES;
+constexpr int kGemmDownSplit = HI3_GEMM_DOWN_SPLIT;
+constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
+static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
 constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
 // fp32 grouped GEMM tile.
 constexpr int kGemmF32BM = 64;
@@ -252,7 +257,9 @@ struct GemmArgs {
   const int4 *tiles;
   const int32_t *gto;
   int E;
-  int NTn;  // column tiles of the widest class
+  int NTn;    // column tiles of the widest class
+  int split;     // blocks per listed row tile; set by the launcher
+  int sub_rows;  // rows per block when split > 1 (block p takes rows [p sub_rows, ...))
 };
 
 struct CombineArgs {

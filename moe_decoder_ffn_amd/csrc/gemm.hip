@@ -11,12 +11,16 @@
 // so every MFMA operand fragment is one 16-byte LDS read.
 //
 // Work list: the row tiles of all groups (written on the device by the scan
-// kernel, expert-major, the shared expert last) times the column tiles. The
-// grid is sized for the largest possible tile count; surplus blocks exit.
-// Schedule: hardware block b runs on XCD b % 8; each XCD is given one
-// contiguous range of the work list, and inside a group the row tiles are
-// the fastest index, so the blocks that share one weight slice run at the
-// same time on the same XCD and its L2 serves the repeats.
+// kernel, expert-major, the shared expert last) times the column tiles; the
+// down projection may run each listed row tile as `split` blocks of
+// sub_rows rows (a smaller tile suits its shape better). The grid is sized
+// for the largest possible tile count; surplus blocks exit.
+// Schedule: the column tile is the fastest index of the work list and block
+// b runs on XCD b % 8 (the hardware's round-robin). The blocks of one row
+// tile run at the same time, spread over the XCDs; when the column-tile
+// count is a multiple of 8 (24 and 16 at H = 4096, I = 3072) each column
+// tile of a group always lands on the same XCD, whose L2 serves its weight
+// slice to all of the group's row tiles, which run close together in time.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -42,38 +46,28 @@ __device__ __forceinline__ int class_col_tiles(const GemmClass &c) {
 template <int MODE, int BN>
 __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   const int ntiles = a.gto[a.E + 1];
-  const int W = ntiles * a.NTn;
-  const int bid = blockIdx.x;
-#if HI3_GEMM_XCD_REMAP
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = (W + 7) >> 3;
-  if (slot >= per) return false;
-  const int L = xcd * per + slot;
-#else
-  const int L = bid;
-#endif
+  const int SP = a.split;
+  const int W = ntiles * SP * a.NTn;
+  const int L = blockIdx.x;
   if (L >= W) return false;
-  // group: the largest g with gto[g] * NTn <= L (empty groups have empty ranges)
+  // group: the largest g with gto[g] * SP * NTn <= L (empty groups have
+  // empty ranges)
   int lo = 0, hi = a.E;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.gto[mid] * a.NTn <= L) lo = mid; else hi = mid - 1;
+    if (a.gto[mid] * SP * a.NTn <= L) lo = mid; else hi = mid - 1;
   }
   const int g = lo;
-  const int first = a.gto[g];
-  const int cnt = a.gto[g + 1] - first;
+  const int first = a.gto[g] * SP;              // first row sub-tile of the group
   const int off = L - first * a.NTn;
-#if HI3_GEMM_NFAST
   const int nt = off % a.NTn;
-  const int mt = first + off / a.NTn;
-#else
-  const int nt = off / cnt;
-  const int mt = first + off % cnt;
-#endif
-  const int4 tile = a.tiles[mt];
+  const int ms = first + off / a.NTn;
+  const int4 tile = a.tiles[ms / SP];
+  const int part = ms % SP;
   j.g = tile.x;
-  j.row0 = tile.y;
-  j.rows = tile.z;
+  j.row0 = tile.y + part * a.sub_rows;
+  j.rows = min(a.sub_rows, tile.z - part * a.sub_rows);
+  if (j.rows <= 0) return false;  // a short tile's empty part
   j.nt = nt;
   j.cls = tile.x == a.E ? 1 : 0;
   const GemmClass &c = j.cls ? a.cls[1] : a.cls[0];
@@ -171,8 +165,13 @@ struct StageRing {
 // weight column 8 (v / 4) + 4 (l / 32) + v % 4 of the 32 x 32 sub-tile, so
 // every lane holds runs of 4 adjacent output columns and stores them with
 // one 8-byte (bf16) or 16-byte (fp32) write.
+// The tile body: BM is the row capacity of this body (the LDS stages may be
+// larger); the stage arrays are the kernel's.
 template <int MODE, int BM, int BK, int NST, int WN>
-__global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u32x4_t *sA0,
+                                          u32x4_t *sB0, u32x4_t *sA1, u32x4_t *sB1,
+                                          u32x4_t *sA2, u32x4_t *sB2, u32x4_t *sA3,
+                                          u32x4_t *sB3, u32x4_t *sA4, u32x4_t *sB4) {
   constexpr int BN = kGemmBN;
   using L = LdsLayout<BK>;
   constexpr int NW = 2 * WN;                // waves: 2 along rows x WN along columns
@@ -181,21 +180,13 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int CPW = A_CP + B_CP;
   constexpr int MI = BM / 64;               // 32-row sub-tiles per wave
   constexpr int NI = BN / WN / 32;          // 32-column sub-tiles per wave
-  constexpr int AE = BM * L::CPR, BE = BN * L::CPR;
   static_assert(BN == 256 && BM % 64 == 0 && BM <= 256 && (BK == 32 || BK == 64), "tile");
   static_assert(NST >= 2 && NST <= 5, "stages");
-  static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
   static_assert(BM % (L::RPC * NW) == 0 && BN % (L::RPC * NW) == 0,
                 "each wave copies a whole number of 1 KiB row groups");
   static_assert(A_CP >= 1 && B_CP >= 1 && (NST - 2) * CPW < 64, "copy counts");
   static_assert(WN == 2 || WN == 4, "wave grid");
-  __shared__ u32x4_t sA0[AE], sB0[BE], sA1[AE], sB1[BE];
-  __shared__ u32x4_t sA2[NST > 2 ? AE : 1], sB2[NST > 2 ? BE : 1];
-  __shared__ u32x4_t sA3[NST > 3 ? AE : 1], sB3[NST > 3 ? BE : 1];
-  __shared__ u32x4_t sA4[NST > 4 ? AE : 1], sB4[NST > 4 ? BE : 1];
 
-  TileJob j;
-  if (!resolve_job<MODE, BN>(a, j)) return;
   const bool shared_cls = j.cls != 0;
   const uint16_t *A = static_cast<const uint16_t *>(shared_cls ? a.cls[1].A : a.cls[0].A);
   const int64_t lda = shared_cls ? a.cls[1].lda : a.cls[0].lda;
@@ -283,14 +274,18 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   // s multiplies fragments read during sub-step s - 1, in MI groups of NI
   // MFMAs (one group per 32-row A fragment), and reads the fragments of
   // sub-step s + 1 between those MFMAs. The copies of step kn (into stage
-  // pa, pb) are issued one per group, from the second group on: a copy
-  // waits in the vector-memory queue while the MFMAs just issued keep the
-  // matrix unit busy, whereas a burst of copies would stall the wave (and
-  // its matrix work) until the whole burst was accepted.
+  // pa, pb) are issued one per group (more if there are more copies than
+  // groups), from the second group on: a copy waits in the vector-memory
+  // queue while the MFMAs just issued keep the matrix unit busy, whereas a
+  // burst of copies would stall the wave (and its matrix work) until the
+  // whole burst was accepted.
   constexpr int NSUB = BK / 16;
   constexpr int NR = MI + NI;   // fragment reads per sub-step
   constexpr int NG = NSUB * MI; // MFMA groups per step
-  static_assert(CPW <= NG - 1, "one copy per MFMA group after the first");
+  static_assert(NG >= 2, "copies go after the first MFMA group");
+  // copies per group: one while they last (PER = 1) unless there are more
+  // copies than groups after the first
+  constexpr int PER = (CPW + NG - 2) / (NG - 1);
   auto compute = [&](const u32x4_t *la, const u32x4_t *lb, bool pre, int kn, u32x4_t *pa,
                      u32x4_t *pb) __attribute__((always_inline)) {
     bf16x8_t af[2][MI], bf[2][NI];
@@ -326,10 +321,12 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (grp >= 1 && grp <= CPW) {
+        constexpr int q0 = (grp - 1) * PER < CPW ? (grp - 1) * PER : CPW;
+        constexpr int q1 = grp * PER < CPW ? grp * PER : CPW;
+        if constexpr (grp >= 1 && q0 < q1) {
           if (pre)
-            issue_range(kn, pa, pb, std::integral_constant<int, grp - 1>{},
-                        std::integral_constant<int, grp>{});
+            issue_range(kn, pa, pb, std::integral_constant<int, q0>{},
+                        std::integral_constant<int, q1>{});
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -438,6 +435,34 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+// Block: one (row tile, column tile) job. Row tiles hold up to BM rows; a
+// group's last tile is often much shorter, and one with at most BM / 2 rows
+// (for BM >= 128) runs the half-height body: half the MFMAs and A copies,
+// the same B copies. Both bodies are straight-line code over the same LDS
+// ring.
+template <int MODE, int BM, int BK, int NST, int WN>
+__global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BN = kGemmBN;
+  using L = LdsLayout<BK>;
+  constexpr int AE = BM * L::CPR, BE = BN * L::CPR;
+  static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
+  __shared__ u32x4_t sA0[AE], sB0[BE], sA1[AE], sB1[BE];
+  __shared__ u32x4_t sA2[NST > 2 ? AE : 1], sB2[NST > 2 ? BE : 1];
+  __shared__ u32x4_t sA3[NST > 3 ? AE : 1], sB3[NST > 3 ? BE : 1];
+  __shared__ u32x4_t sA4[NST > 4 ? AE : 1], sB4[NST > 4 ? BE : 1];
+
+  TileJob j;
+  if (!resolve_job<MODE, BN>(a, j)) return;
+  constexpr int BMS = BM / 2;
+  if constexpr (BMS >= 64 && BMS % 64 == 0) {
+    if (j.rows <= BMS) {
+      gemm_tile<MODE, BMS, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+      return;
+    }
+  }
+  gemm_tile<MODE, BM, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+}
+
 // --------------------------------------------------------------- fp32
 
 // fp32 layers: LDS-tiled FMA, 64 rows x 64 weight rows per block ([up; gate]:
@@ -542,7 +567,9 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int dtype, bool upgate,
                               hipStream_t s) {
   const int BN = dtype == kBF16 ? kGemmBN : kGemmF32BN;
   a.NTn = std::max(col_tiles_host(a.cls[0].N, BN, upgate), col_tiles_host(a.cls[1].N, BN, upgate));
-  const int64_t work = static_cast<int64_t>(max_tiles) * a.NTn;
+  a.split = dtype == kBF16 && !upgate ? kGemmDownSplit : 1;
+  a.sub_rows = a.split > 1 ? kGemmBM / a.split : 1 << 30;
+  const int64_t work = static_cast<int64_t>(max_tiles) * a.split * a.NTn;
   const unsigned grid = static_cast<unsigned>((work + 7) / 8 * 8);
   if (grid == 0) return hipSuccess;
   if (dtype == kBF16) {
@@ -550,7 +577,8 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int dtype, bool upgate,
       hipLaunchKernelGGL((gemm_bf16_kernel<0, kGemmBM, kGemmBK, kGemmStages, kGemmWN>),
                          dim3(grid), dim3(128 * kGemmWN), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_kernel<1, kGemmBM, kGemmBK, kGemmStages, kGemmWN>),
+      hipLaunchKernelGGL((gemm_bf16_kernel<1, kGemmBM / kGemmDownSplit, kGemmBK, kGemmDownStages,
+                                           kGemmWN>),
                          dim3(grid), dim3(128 * kGemmWN), 0, s, a);
   } else {
     if (upgate)
