@@ -38,6 +38,8 @@ def _load():
         lib.orc_moe_dense_rows.argtypes = [P, i32, P, P, P, P, P, i64, i32, i32,
                                            i64, i64, P, i64, P, P, P]
         lib.orc_moe_dense_rows.restype = None
+        lib.orc_rmsnorm.argtypes = [P, i32, P, ctypes.c_double, P, i64, i64, P]
+        lib.orc_rmsnorm.restype = None
         lib.orc_round_bf16_array.argtypes = [P, i64, P]
         lib.orc_round_bf16_array.restype = None
         _lib = lib
@@ -172,3 +174,44 @@ def round_bf16(v):
     out = np.empty(v.shape, np.uint16)
     lib.orc_round_bf16_array(_ptr(v), v.size, _ptr(out))
     return out
+
+
+def rmsnorm(x, weight, eps=1e-5, pad_mask=None):
+    """The block's RMSNorm in front of the layer (moe_oracle.c, orc_rmsnorm):
+    x [T,H] and weight [H] in the layer dtype. Padding rows of the result are
+    zero (never computed)."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    weight = np.ascontiguousarray(weight)
+    T, H = x.shape
+    assert weight.shape == (H,) and weight.dtype == x.dtype
+    pad = None if pad_mask is None else np.ascontiguousarray(pad_mask, np.uint8)
+    xn = np.zeros_like(x)
+    lib.orc_rmsnorm(_ptr(x), dt, _ptr(weight), float(eps), _ptr(pad), T, H, _ptr(xn))
+    return xn
+
+
+def _as_f64(a):
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def moe_norm_residual(h, norm_weight, w_router, w13, w2, ws13, ws2, K, eps=1e-5,
+                      pad_mask=None, rows=None, idx=None, w=None):
+    """The layer inside its block: out = h + layer(RMSNorm(h)) (model API
+    page, HunyuanImage3Block: pre-norm, residual around the experts). The
+    layer's fp64 value (before its rounding) plus the residual is rounded once
+    to the dtype. Returns dict(out [n,H] (zero rows for padding), exact (fp64,
+    NaN rows for padding), xn [T,H], idx, w)."""
+    h = np.ascontiguousarray(h)
+    xn = rmsnorm(h, norm_weight, eps, pad_mask)
+    r = moe(xn, w_router, w13, w2, ws13, ws2, K, pad_mask=pad_mask, rows=rows, idx=idx, w=w)
+    rows_ = _rows(rows, h.shape[0])
+    exact = r["exact"] + _as_f64(h[rows_])
+    fin = np.nan_to_num(exact)
+    out = round_bf16(fin) if h.dtype == np.uint16 else fin.astype(np.float32)
+    if pad_mask is not None:
+        out[np.asarray(pad_mask)[rows_] != 0] = 0
+    return {"out": out, "exact": exact, "xn": xn, "idx": r["idx"], "w": r["w"]}

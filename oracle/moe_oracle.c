@@ -52,6 +52,9 @@
  *      HunyuanImage3Block.forward): x is not read, out is not written, and the
  *      route outputs are idx = -1, w = 0.
  *
+ * orc_rmsnorm adds the block's normalisation in front of the layer (the
+ * residual add after the layer is composed in the Python wrapper).
+ *
  * dtype codes: 0 = fp32, 1 = bf16 (uint16 bit patterns).
  */
 #include <math.h>
@@ -364,6 +367,44 @@ void orc_moe_dense_rows(const void *x, int dtype, const void *w13, const void *w
 
 /* Round an fp64 array to bf16 bit patterns (used by tests for the
  * tolerance-attainability check). */
+/*
+ * The block's normalisation before the experts (model API page,
+ * HunyuanImage3Block: a pre-norm decoder layer, post_attention_layernorm
+ * ahead of the routed and shared experts; layers API page, HunyuanRMSNorm:
+ * normalizes in fp32 over the last axis and returns weight * x in the input
+ * dtype, eps 1e-5 by default). For every real row t:
+ *   m   = mean over h of x[t,h]^2: accumulated in fp64 (the squares are
+ *         exact), divided by H and rounded to fp32
+ *   d   = m + eps in fp32 (eps taken as an fp32 number)
+ *   r   = 1 / sqrt(d), rounded once to fp32
+ *   n_h = x[t,h] * r in fp32, then converted to the input dtype
+ *   xn  = weight[h] * n_h in the input dtype (the product of two dtype
+ *         values is exact in fp64 and rounded once)
+ * Padding rows are neither read nor written.
+ */
+void orc_rmsnorm(const void *x, int dtype, const void *weight, double eps,
+                 const uint8_t *pad, int64_t T, int64_t H, void *xn)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        if (pad && pad[t])
+            continue;
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            double v = elem(x, dtype, t * H + h);
+            ss += v * v;
+        }
+        float m = (float)(ss / (double)H);
+        float d = m + (float)eps;
+        float r = (float)(1.0 / sqrt((double)d));
+        for (int64_t h = 0; h < H; h++) {
+            float p = (float)(elem(x, dtype, t * H + h) * (double)r);
+            double n = round_dtype((double)p, dtype);
+            store_dtype(xn, dtype, t * H + h, round_dtype(elem(weight, dtype, h) * n, dtype));
+        }
+    }
+}
+
 void orc_round_bf16_array(const double *v, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; i++)

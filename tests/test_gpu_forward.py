@@ -87,6 +87,20 @@ def test_forward_small_all_rows(name, dtype, H, E, K, I, Is, seq, plen):
         assert np.isfinite(as_f64(out[pad == 0])).all()
 
 
+@pytest.mark.parametrize("T", [1, 64, 65, 128, 129, 256, 257, 513])
+def test_forward_tile_boundaries(T):
+    """One expert (E = K = 1), so every row goes to it and the row-tile
+    edges are hit by construction: the up/gate tile holds 256 rows and runs
+    a half-height body at <= 128 rows; the down projection runs each tile as
+    two 128-row halves (the second empty below 129 rows) with a half-height
+    body at <= 64 rows."""
+    _say(f"[forward] tile boundaries T={T}")
+    shape = wk.LayerShape(H=256, E=1, K=1, I=128, Is=192, dtype=wk.BF16)
+    d = wk.make_inputs(wk.custom(shape, (T,)), 11)
+    out, idx, w, cnt, *_ = full_check(d, 1)
+    assert np.all(idx == 0) and np.all(w == 1.0) and cnt[0] == T
+
+
 @pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
 def test_forward_k_equals_e(dtype):
     _say(f"[forward] K=E dtype={dtype}")

@@ -235,6 +235,15 @@ def make_weights(shape: LayerShape, seed: int = 0, skew: bool = False) -> dict:
     return d
 
 
+def make_norm_weight(shape: LayerShape, seed: int = 0) -> np.ndarray:
+    """Weight [H] of the block's RMSNorm in front of the layer: 1 + 0.1 N(0,1)
+    in the layer dtype (the module initialises it to ones; the spread makes
+    the multiply by the weight visible)."""
+    s = _streams(seed)
+    v = _normal_fill(s["spare"], shape.H, 0.1, shape.H, F32) + np.float32(1.0)
+    return f32_to_bf16_bits(v) if shape.dtype == BF16 else v
+
+
 def make_x(wl: Workload, seed: int = 0) -> tuple:
     """Activations [T,H] ~ N(0,1) (the layer's input after RMSNorm), with
     padding rows set to NaN so that any read of them shows; and the uint8
