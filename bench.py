@@ -156,6 +156,67 @@ def cpu_baseline(wl, d, K, target_s):
                       f"OpenMP over tokens), {total_t:.1f} s"}
 
 
+def norm_residual_bench(args, m, wl, d, dd, pad, ws, stream):
+    """Times h + layer(RMSNorm(h)) per step (whole call), and the RMSNorm
+    kernel alone against the HBM roofline (x read, normalised rows written)."""
+    import torch
+    sh = wl.shape
+    nw = torch.from_numpy(wk.make_norm_weight(sh, args.seed).view(np.int16)).cuda().view(
+        torch.bfloat16) if sh.dtype == wk.BF16 else torch.from_numpy(
+        wk.make_norm_weight(sh, args.seed)).cuda()
+    h = dd["x"]
+    out = torch.zeros_like(h)
+    xn = torch.empty_like(h)
+    idx = torch.empty((wl.T, sh.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((wl.T, sh.K), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((sh.E,), dtype=torch.int32, device="cuda")
+
+    def step():
+        m.hi3_moe_forward_norm_residual(h, nw, 1e-5, dd["w_router"], dd["w13"], dd["w2"],
+                                        dd["ws13"], dd["ws2"], pad, sh.K, out, idx, wts, cnt,
+                                        ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"[bench] {args.steps} timed steps done")
+    hip = HipEvents()
+    ev = hip.create(2)
+    reps = 20
+    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hip.hipEventRecord(ev[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(reps):
+        m.hi3_moe_rmsnorm(h, nw, 1e-5, pad, xn, stream)
+    hip.hip.hipEventRecord(ev[1], ctypes.c_void_p(stream.cuda_stream))
+    norm_ms = hip.elapsed_ms(ev[0], ev[1]) / reps
+    hip.destroy(ev)
+    es = 2 if sh.dtype == wk.BF16 else 4
+    norm_bytes = 2 * wl.T_valid * sh.H * es + sh.H * es
+    gbs = norm_bytes / (norm_ms * 1e-3) / 1e9
+    tokens_s = wl.T_valid / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == wk.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "entry": "norm_residual", "T": wl.T,
+                   "T_valid": wl.T_valid, "H": sh.H, "E": sh.E, "K": sh.K, "I": sh.I,
+                   "I_shared": sh.Is, "eps": 1e-5, "seed": args.seed},
+        "stages": {"rmsnorm": {"us": round(norm_ms * 1e3, 2), "gbs": round(gbs, 1),
+                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}},
+        "roofline": {"kernel": "rmsnorm_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +228,10 @@ def main():
                     help="wall-time budget of the CPU oracle sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--entry", default="forward", choices=("forward", "norm_residual"),
+                    help="forward: the layer (hi3_moe_forward); norm_residual: the layer "
+                         "inside its block, h + layer(RMSNorm(h)) "
+                         "(hi3_moe_forward_norm_residual)")
     args = ap.parse_args()
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy)
@@ -211,6 +276,10 @@ def main():
             m.hi3_moe_forward_instrumented(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
                                            dd["ws2"], pad, sh.K, out, idx, wts, cnt, ws,
                                            events, stream)
+
+    if args.entry == "norm_residual":
+        norm_residual_bench(args, m, wl, d, dd, pad, ws, stream)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -77,10 +77,11 @@ extern "C" {
 #define HI3_NUM_STAGES 7
 
 /*
- * Workspace bytes that hi3_moe_forward needs for these sizes (host-only, no
- * HIP call). With I = I_shared = 0 it returns the smaller amount that
- * hi3_moe_route and hi3_moe_dispatch need; the forward amount also serves
- * them. Returns 0 for invalid sizes and for T = 0.
+ * Workspace bytes that hi3_moe_forward and hi3_moe_forward_norm_residual
+ * need for these sizes (host-only, no HIP call). With I = I_shared = 0 it
+ * returns the smaller amount that hi3_moe_route and hi3_moe_dispatch need;
+ * the forward amount also serves them. Returns 0 for invalid sizes and for
+ * T = 0.
  */
 size_t hi3_moe_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K,
                               int32_t I, int32_t I_shared, int32_t dtype);
@@ -168,6 +169,49 @@ int hi3_moe_forward_instrumented(const void *x, const float *w_router,
                                  int32_t *expert_counts, void *workspace,
                                  size_t workspace_bytes, void *hip_stream,
                                  void *const *stage_events);
+
+/*
+ * The block's RMSNorm ahead of the layer (layers API page, HunyuanRMSNorm:
+ * normalize in fp32 over the hidden axis, return weight * x in the input
+ * dtype, eps 1e-5 by default; model API page, HunyuanImage3Block:
+ * post_attention_layernorm before the experts). For every real row:
+ *   m = mean of x^2 (accumulated in fp64, rounded to fp32), d = m + eps in
+ *   fp32, r = 1 / sqrt(d) rounded once to fp32, n = x * r as an fp32 product
+ *   converted to dtype, xn = weight * n rounded once to dtype.
+ *   x        [T, H] dtype.
+ *   weight   [H] dtype.
+ *   eps      finite, >= 0 (HI3_E_UNSUPPORTED otherwise).
+ *   pad_mask [T] uint8 or NULL; padding rows of xn are not written.
+ *   xn       [T, H] dtype out; may be x itself.
+ * H must be a multiple of 64. No workspace.
+ */
+int hi3_moe_rmsnorm(const void *x, const void *weight, float eps, const uint8_t *pad_mask,
+                    int64_t T, int32_t H, int32_t dtype, void *xn, void *hip_stream);
+
+/*
+ * The layer inside its decoder block (model API page, HunyuanImage3Block:
+ * a pre-norm layer; its MoE half is h + layer(post_attention_layernorm(h))):
+ *   out[t] = h[t] + layer(RMSNorm(h)[t])
+ * with RMSNorm as in hi3_moe_rmsnorm and the layer as in hi3_moe_forward;
+ * the residual is added in fp32 after the shared term, before the one
+ * rounding to dtype. Arguments as in hi3_moe_forward, plus:
+ *   h            [T, H] dtype: the residual stream (takes the place of x).
+ *   norm_weight  [H] dtype, must not be NULL.
+ *   eps          finite, >= 0.
+ *   out          [T, H] dtype out; may be h itself (updated in place), must
+ *                not overlap it otherwise. Padding rows are not written.
+ * Routes (topk_idx, topk_w, expert_counts) are those of the normalised rows.
+ * Same workspace size as hi3_moe_forward.
+ */
+int hi3_moe_forward_norm_residual(const void *h, const void *norm_weight, float eps,
+                                  const float *w_router, const void *w_up_gate,
+                                  const void *w_down, const void *w_shared_up_gate,
+                                  const void *w_shared_down, const uint8_t *pad_mask,
+                                  int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                                  int32_t I_shared, int32_t dtype, void *out,
+                                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *hip_stream);
 
 /* Static name of timed stage i (0 <= i < HI3_NUM_STAGES), else "?". */
 const char *hi3_moe_stage_name(int stage);

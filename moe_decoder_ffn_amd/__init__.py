@@ -31,6 +31,8 @@ EXPORTED = (
     "hi3_moe_dispatch",
     "hi3_moe_forward",
     "hi3_moe_forward_instrumented",
+    "hi3_moe_rmsnorm",
+    "hi3_moe_forward_norm_residual",
     "hi3_moe_stage_name",
     "hi3_moe_status_string",
 )
@@ -60,6 +62,11 @@ def _load():
     lib.hi3_moe_forward.restype = ctypes.c_int
     lib.hi3_moe_forward_instrumented.argtypes = fwd + [P]
     lib.hi3_moe_forward_instrumented.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.hi3_moe_rmsnorm.argtypes = [P, P, f32, P, i64, i32, i32, P, P]
+    lib.hi3_moe_rmsnorm.restype = ctypes.c_int
+    lib.hi3_moe_forward_norm_residual.argtypes = [P, P, f32] + fwd[1:]
+    lib.hi3_moe_forward_norm_residual.restype = ctypes.c_int
     lib.hi3_moe_stage_name.argtypes = [ctypes.c_int]
     lib.hi3_moe_stage_name.restype = ctypes.c_char_p
     lib.hi3_moe_status_string.argtypes = [ctypes.c_int]
@@ -161,6 +168,22 @@ def hi3_moe_forward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_gat
         topk_idx, topk_w, expert_counts, workspace, stream), arr))
 
 
+def hi3_moe_rmsnorm(x, weight, eps, pad_mask, xn, stream=None):
+    T, H = x.shape
+    _check(lib.hi3_moe_rmsnorm(_ptr(x), _ptr(weight), float(eps), _ptr(pad_mask), T, H,
+                               dtype_code(x.dtype), _ptr(xn), _stream(stream)))
+
+
+def hi3_moe_forward_norm_residual(h, norm_weight, eps, w_router, w_up_gate, w_down,
+                                  w_shared_up_gate, w_shared_down, pad_mask, K, out,
+                                  topk_idx=None, topk_w=None, expert_counts=None,
+                                  workspace=None, stream=None):
+    args = _forward_args(h, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                         pad_mask, K, out, topk_idx, topk_w, expert_counts, workspace, stream)
+    _check(lib.hi3_moe_forward_norm_residual(args[0], _ptr(norm_weight), float(eps),
+                                             *args[1:]))
+
+
 def hi3_moe_stage_name(i) -> str:
     return lib.hi3_moe_stage_name(i).decode()
 
@@ -195,6 +218,30 @@ def moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
     counts = torch.empty((E,), dtype=torch.int32, device=x.device)
     hi3_moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
                     pad_mask, K, out, idx, w, counts, workspace)
+    if return_routes:
+        return out, idx, w, counts
+    return out
+
+
+def moe_forward_norm_residual(h, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate,
+                              w_shared_down, K, eps=1e-5, pad_mask=None, out=None,
+                              workspace=None, return_routes=False):
+    """h + layer(RMSNorm(h)) with torch-allocated outputs and workspace; out
+    may be h itself. Padding rows of a freshly allocated out are zero."""
+    T, H = h.shape
+    E = w_router.shape[0]
+    I = w_up_gate.shape[1] // 2
+    Is = w_shared_up_gate.shape[0] // 2
+    if out is None:
+        out = torch.zeros_like(h)
+    if workspace is None:
+        workspace = workspace_for(h, E, K, I, Is)
+    idx = torch.empty((T, K), dtype=torch.int32, device=h.device)
+    w = torch.empty((T, K), dtype=torch.float32, device=h.device)
+    counts = torch.empty((E,), dtype=torch.int32, device=h.device)
+    hi3_moe_forward_norm_residual(h, norm_weight, eps, w_router, w_up_gate, w_down,
+                                  w_shared_up_gate, w_shared_down, pad_mask, K, out, idx, w,
+                                  counts, workspace)
     if return_routes:
         return out, idx, w, counts
     return out

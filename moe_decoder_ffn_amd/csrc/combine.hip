@@ -1,7 +1,11 @@
 // Combine: out[t] = sum_k w[t,k] y[slot(t,k)] + y_shared[t] for every real
 // token (model API page, HunyuanImage3Block: routed experts plus the fused
 // shared expert; build_moe_config: renormalised top-k weights), summed in fp32
-// in k order, then the shared term, rounded once to the layer dtype.
+// in k order, then the shared term, rounded once to the layer dtype. With a
+// residual (the block's residual around the layer, HunyuanImage3Block being a
+// pre-norm layer) the residual row is added last, before that one rounding;
+// out may be the residual itself (each element is read, then written, by the
+// same thread).
 // Deterministic: each output element is produced by one thread in a fixed
 // order; no atomics. Padding rows are neither read nor written.
 #include "common.h"
@@ -61,6 +65,23 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     acc[1] += sv[1];
     acc[2] += sv[2];
     acc[3] += sv[3];
+    if (a.resid) {
+      if (DT == kBF16) {
+        const u32x2_t rv =
+            reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(a.resid) + t * a.H)[q];
+        acc[0] += __uint_as_float(rv[0] << 16);
+        acc[1] += __uint_as_float(rv[0] & 0xffff0000u);
+        acc[2] += __uint_as_float(rv[1] << 16);
+        acc[3] += __uint_as_float(rv[1] & 0xffff0000u);
+      } else {
+        const f32x4_t rv =
+            reinterpret_cast<const f32x4_t *>(static_cast<const float *>(a.resid) + t * a.H)[q];
+        acc[0] += rv[0];
+        acc[1] += rv[1];
+        acc[2] += rv[2];
+        acc[3] += rv[3];
+      }
+    }
     if (DT == kBF16) {
       u32x2_t o;
       o[0] = pack_bf16x2(acc[0], acc[1]);

@@ -145,6 +145,7 @@ struct Plan {
   size_t slotof;  // [T*K] int32 (token, k) -> slot
   size_t vtok;    // [T] int32 real-row index -> token
   size_t vidx;    // [T] int32 token -> real-row index (-1 padding)
+  size_t xn;      // [T,H] dtype: rows after the block's RMSNorm (norm + residual entry)
   size_t h;       // [T*K, I] dtype: SwiGLU activations of routed rows
   size_t hs;      // [T, Is] dtype: SwiGLU activations of the shared expert
   size_t y;       // [T*K, H] fp32: routed expert outputs by slot
@@ -187,6 +188,7 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) 
   p.vtok = take(T * 4);
   p.vidx = take(T * 4);
   if (I > 0) {
+    p.xn = take(T * H * es);
     p.h = take(TK * I * es);
     p.hs = take(T * Is * es);
     p.y = take(TK * H * 4);
@@ -272,7 +274,19 @@ struct CombineArgs {
   int64_t T;
   int H, K;
   void *out;
+  const void *resid;  // [T,H] dtype residual added before the rounding, or null
 };
+
+struct NormArgs {
+  const void *x;       // [T,H] dtype
+  const void *weight;  // [H] dtype
+  const uint8_t *pad;  // [T] or null
+  int64_t T;
+  int H;
+  float eps;
+  void *xn;            // [T,H] dtype
+};
+hipError_t launch_rmsnorm(const NormArgs &a, int dtype, hipStream_t s);
 
 hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, int Epad,
                                int H, hipStream_t s);

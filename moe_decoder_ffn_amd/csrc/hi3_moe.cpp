@@ -46,20 +46,26 @@ struct Recorder {
     if ((expr) != hipSuccess) return HI3_E_HIP; \
   } while (0)
 
-int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
-                 const void *w_down, const void *w_shared_up_gate, const void *w_shared_down,
-                 const uint8_t *pad_mask, int64_t T, int32_t H, int32_t E, int32_t K,
-                 int32_t I, int32_t Is, int32_t dtype, void *out, int32_t *topk_idx,
-                 float *topk_w, int32_t *expert_counts, void *workspace,
+// eps must be a finite number >= 0.
+bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }
+
+// norm_weight != null: the block's RMSNorm runs first (x is the residual
+// stream h) and the combine adds h back; otherwise x feeds the layer directly.
+int forward_impl(const void *x, const void *norm_weight, float eps, const float *w_router,
+                 const void *w_up_gate, const void *w_down, const void *w_shared_up_gate,
+                 const void *w_shared_down, const uint8_t *pad_mask, int64_t T, int32_t H,
+                 int32_t E, int32_t K, int32_t I, int32_t Is, int32_t dtype, void *out,
+                 int32_t *topk_idx, float *topk_w, int32_t *expert_counts, void *workspace,
                  size_t workspace_bytes, void *hip_stream, void *const *events) {
   if (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !out)
     return HI3_E_NULL;
   int st = check_sizes(T, H, E, K, I, Is, dtype, true);
   if (st != HI3_OK) return st;
+  if (norm_weight && !eps_ok(eps)) return HI3_E_UNSUPPORTED;
   if (T == 0) return HI3_OK;
   if (!workspace) return HI3_E_NULL;
-  st = all_aligned({x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
-                    out, topk_idx, topk_w, expert_counts, workspace});
+  st = all_aligned({x, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate,
+                    w_shared_down, pad_mask, out, topk_idx, topk_w, expert_counts, workspace});
   if (st != HI3_OK) return st;
   const Plan p = make_plan(T, H, E, K, I, Is, dtype);
   if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
@@ -67,6 +73,13 @@ int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  const void *resid = nullptr;
+  if (norm_weight) {
+    NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
+    HI3_TRY(launch_rmsnorm(na, dtype, s));
+    resid = x;
+    x = at(p.xn);
+  }
   int32_t *idx = topk_idx ? topk_idx : static_cast<int32_t *>(at(p.idx));
   float *wts = topk_w ? topk_w : static_cast<float *>(at(p.wts));
   int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
@@ -123,7 +136,7 @@ int forward_impl(const void *x, const float *w_router, const void *w_up_gate,
   // 6: combine
   rec.at(6);
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
-                 slotof, vidx, wts, pad_mask, T, H, K, out};
+                 slotof, vidx, wts, pad_mask, T, H, K, out, resid};
   HI3_TRY(launch_combine(ca, dtype, s));
   rec.at(7);
   return rec.ok ? HI3_OK : HI3_E_HIP;
@@ -219,9 +232,9 @@ int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
                     int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
                     int32_t *expert_counts, void *workspace, size_t workspace_bytes,
                     void *hip_stream) {
-  return forward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
-                      pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx, topk_w,
-                      expert_counts, workspace, workspace_bytes, hip_stream, nullptr);
+  return forward_impl(x, nullptr, 0.0f, w_router, w_up_gate, w_down, w_shared_up_gate,
+                      w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
+                      topk_w, expert_counts, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 int hi3_moe_forward_instrumented(const void *x, const float *w_router, const void *w_up_gate,
@@ -233,9 +246,38 @@ int hi3_moe_forward_instrumented(const void *x, const float *w_router, const voi
                                  void *workspace, size_t workspace_bytes, void *hip_stream,
                                  void *const *stage_events) {
   if (!stage_events) return HI3_E_NULL;
-  return forward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
-                      pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx, topk_w,
-                      expert_counts, workspace, workspace_bytes, hip_stream, stage_events);
+  return forward_impl(x, nullptr, 0.0f, w_router, w_up_gate, w_down, w_shared_up_gate,
+                      w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
+                      topk_w, expert_counts, workspace, workspace_bytes, hip_stream,
+                      stage_events);
+}
+
+int hi3_moe_forward_norm_residual(const void *h, const void *norm_weight, float eps,
+                                  const float *w_router, const void *w_up_gate,
+                                  const void *w_down, const void *w_shared_up_gate,
+                                  const void *w_shared_down, const uint8_t *pad_mask,
+                                  int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                                  int32_t I_shared, int32_t dtype, void *out,
+                                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *hip_stream) {
+  if (!norm_weight) return HI3_E_NULL;
+  return forward_impl(h, norm_weight, eps, w_router, w_up_gate, w_down, w_shared_up_gate,
+                      w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
+                      topk_w, expert_counts, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int hi3_moe_rmsnorm(const void *x, const void *weight, float eps, const uint8_t *pad_mask,
+                    int64_t T, int32_t H, int32_t dtype, void *xn, void *hip_stream) {
+  if (!x || !weight || !xn) return HI3_E_NULL;
+  if (T < 0 || H <= 0) return HI3_E_SHAPE;
+  if (dtype != HI3_F32 && dtype != HI3_BF16) return HI3_E_UNSUPPORTED;
+  if (H % 64 != 0 || !eps_ok(eps)) return HI3_E_UNSUPPORTED;
+  if (all_aligned({x, weight, pad_mask, xn}) != HI3_OK) return HI3_E_UNSUPPORTED;
+  if (T == 0) return HI3_OK;
+  NormArgs na{x, weight, pad_mask, T, H, eps, xn};
+  HI3_TRY(launch_rmsnorm(na, dtype, static_cast<hipStream_t>(hip_stream)));
+  return HI3_OK;
 }
 
 const char *hi3_moe_stage_name(int stage) {

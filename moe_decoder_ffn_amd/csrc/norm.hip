@@ -1,0 +1,134 @@
+// The decoder block's normalisation in front of the layer (layers API page,
+// HunyuanRMSNorm: normalize in fp32 over the hidden axis, return weight * x
+// in the input dtype, eps 1e-5 by default; model API page,
+// HunyuanImage3Block: a pre-norm layer, post_attention_layernorm ahead of the
+// routed and shared experts). For every real row t:
+//   m  = mean of x[t,h]^2, accumulated in fp64 (the squares are exact) and
+//        rounded to fp32 after the division by H
+//   d  = m + eps in fp32
+//   r  = 1 / sqrt(d), evaluated in fp64 and rounded once to fp32
+//   n  = x * r as an fp32 product, converted to the layer dtype
+//   xn = weight * n, rounded once to the layer dtype (for bf16 the product
+//        of two bf16 values is exact in fp32)
+// The bf16 roundings decide the router's inputs, so every step is spelled
+// out to the rounding. Padding rows are neither read nor written.
+// One wave per row, four rows per block: each lane keeps its 16-byte chunks
+// of the row (CPL of them, 8 or 16) in registers, so the row is read once;
+// the sum of squares is a wave reduction. Longer rows (CPL = 0) take a
+// two-pass loop that reads the row again (from L2).
+#include "common.h"
+
+namespace hi3 {
+
+template <int DT>
+__device__ __forceinline__ void unpack16(const u32x4_t &v, float *f) {
+  if (DT == kBF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(v[e] << 16);
+      f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+  }
+}
+
+// n = dtype(x * r), xn = dtype(w * n) for the elements of one chunk.
+template <int DT>
+__device__ __forceinline__ u32x4_t norm_chunk(const u32x4_t &xv, const u32x4_t &wv, float r) {
+  constexpr int PER = DT == kBF16 ? 8 : 4;
+  float f[PER], w[PER];
+  unpack16<DT>(xv, f);
+  unpack16<DT>(wv, w);
+  u32x4_t o;
+  if (DT == kBF16) {
+    uint16_t q[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float n = bf16_to_f32(f32_to_bf16(f[e] * r));
+      q[e] = f32_to_bf16(w[e] * n);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = static_cast<uint32_t>(q[2 * e]) | (static_cast<uint32_t>(q[2 * e + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = __float_as_uint(w[e] * (f[e] * r));
+  }
+  return o;
+}
+
+template <int DT>
+__device__ __forceinline__ double chunk_sq(const u32x4_t &v) {
+  constexpr int PER = DT == kBF16 ? 8 : 4;
+  float f[PER];
+  unpack16<DT>(v, f);
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) ss += static_cast<double>(f[e]) * static_cast<double>(f[e]);
+  return ss;
+}
+
+template <int DT, int CPL>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  if (a.pad && a.pad[t]) return;
+  constexpr int PER = DT == kBF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int nc = a.H / PER;
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * (DT == kBF16 ? 2 : 4);
+  const u32x4_t *xr =
+      reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a.x) + t * row_bytes);
+  const u32x4_t *wr = static_cast<const u32x4_t *>(a.weight);
+  u32x4_t *outr = reinterpret_cast<u32x4_t *>(static_cast<char *>(a.xn) + t * row_bytes);
+
+  // m = mean of x^2 (fp64 sum, fixed butterfly order), d = m + eps in fp32,
+  // r = 1 / sqrt(d) rounded once to fp32; every lane computes the same r.
+  auto finish = [&](double ss) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    const float m = static_cast<float>(ss / static_cast<double>(a.H));
+    const float d = m + a.eps;
+    return static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+  };
+
+  if constexpr (CPL > 0) {
+    u32x4_t v[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + 64 * i < nc) v[i] = xr[lane + 64 * i];
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + 64 * i < nc) ss += chunk_sq<DT>(v[i]);
+    const float r = finish(ss);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + 64 * i < nc) outr[lane + 64 * i] = norm_chunk<DT>(v[i], wr[lane + 64 * i], r);
+  } else {
+    double ss = 0.0;
+    for (int c = lane; c < nc; c += 64) ss += chunk_sq<DT>(xr[c]);
+    const float r = finish(ss);
+    for (int c = lane; c < nc; c += 64) outr[c] = norm_chunk<DT>(xr[c], wr[c], r);
+  }
+}
+
+hipError_t launch_rmsnorm(const NormArgs &a, int dtype, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((a.T + 3) / 4)), block(256);
+  const int nc = a.H / (dtype == kBF16 ? 8 : 4);
+  if (dtype == kBF16) {
+    if (nc <= 64 * 8) hipLaunchKernelGGL((rmsnorm_kernel<kBF16, 8>), grid, block, 0, s, a);
+    else if (nc <= 64 * 16) hipLaunchKernelGGL((rmsnorm_kernel<kBF16, 16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((rmsnorm_kernel<kBF16, 0>), grid, block, 0, s, a);
+  } else {
+    if (nc <= 64 * 8) hipLaunchKernelGGL((rmsnorm_kernel<kF32, 8>), grid, block, 0, s, a);
+    else if (nc <= 64 * 16) hipLaunchKernelGGL((rmsnorm_kernel<kF32, 16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((rmsnorm_kernel<kF32, 0>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hi3

@@ -151,3 +151,45 @@ def test_package_has_no_fallback():
     src = open(os.path.join(ROOT, "moe_decoder_ffn_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
     assert "numpy" not in src
+
+
+def test_rmsnorm_validation():
+    f = m.lib.hi3_moe_rmsnorm
+    assert f(None, P, 1e-5, None, 64, 256, 1, P, None) == m.HI3_E_NULL
+    assert f(P, None, 1e-5, None, 64, 256, 1, P, None) == m.HI3_E_NULL
+    assert f(P, P, 1e-5, None, 64, 256, 1, None, None) == m.HI3_E_NULL
+    assert f(P, P, 1e-5, None, -1, 256, 1, P, None) == m.HI3_E_SHAPE
+    assert f(P, P, 1e-5, None, 64, 0, 1, P, None) == m.HI3_E_SHAPE
+    assert f(P, P, 1e-5, None, 64, 250, 1, P, None) == m.HI3_E_UNSUPPORTED
+    assert f(P, P, 1e-5, None, 64, 256, 2, P, None) == m.HI3_E_UNSUPPORTED
+    assert f(P, P, -1.0, None, 64, 256, 1, P, None) == m.HI3_E_UNSUPPORTED
+    assert f(P, P, float("nan"), None, 64, 256, 1, P, None) == m.HI3_E_UNSUPPORTED
+    assert f(P, P, float("inf"), None, 64, 256, 1, P, None) == m.HI3_E_UNSUPPORTED
+    assert f(UNALIGNED, P, 1e-5, None, 64, 256, 1, P, None) == m.HI3_E_UNSUPPORTED
+    assert f(P, P, 1e-5, None, 0, 256, 1, P, None) == m.HI3_OK
+
+
+def _fwd_nr(**kw):
+    a = dict(h=P, nw=P, eps=1e-5, wr=P, w13=P, w2=P, ws13=P, ws2=P, pad=None, T=64, H=256,
+             E=8, K=2, I=128, Is=128, dt=m.HI3_BF16, out=P, idx=None, w=None, cnt=None, ws=P,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return m.lib.hi3_moe_forward_norm_residual(
+        a["h"], a["nw"], a["eps"], a["wr"], a["w13"], a["w2"], a["ws13"], a["ws2"], a["pad"],
+        a["T"], a["H"], a["E"], a["K"], a["I"], a["Is"], a["dt"], a["out"], a["idx"], a["w"],
+        a["cnt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), m.HI3_E_NULL),
+    (dict(nw=None), m.HI3_E_NULL),
+    (dict(out=None), m.HI3_E_NULL),
+    (dict(K=9), m.HI3_E_SHAPE),
+    (dict(eps=-1e-5), m.HI3_E_UNSUPPORTED),
+    (dict(eps=float("nan")), m.HI3_E_UNSUPPORTED),
+    (dict(nw=UNALIGNED), m.HI3_E_UNSUPPORTED),
+    (dict(wsb=1000), m.HI3_E_WORKSPACE),
+    (dict(T=0), m.HI3_OK),
+])
+def test_forward_norm_residual_validation(kw, status):
+    assert _fwd_nr(**kw) == status
