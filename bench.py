@@ -80,6 +80,24 @@ def stage_bytes(wl):
     }
 
 
+# Rows per expert below which the grouped GEMMs are bound by reading their
+# weights rather than by MFMA: the bf16 ridge, 2.5 PFLOP/s / 8 TB/s = 312
+# FLOP per byte, is reached at about 312 rows per expert (each weight byte
+# is used for 2 FLOP per row, two bytes per weight).
+RIDGE_ROWS = 312
+
+
+def upgate_bytes(wl):
+    """Algorithmic HBM bytes of the [up; gate] GEMM: every expert's and the
+    shared expert's [up; gate] weights once, each routed or shared row of x
+    once per use, h written once."""
+    sh = wl.shape
+    es = 2 if sh.dtype == wk.BF16 else 4
+    rows = wl.T_valid * (sh.K + 1)
+    return (sh.E * 2 * sh.I * sh.H + 2 * sh.Is * sh.H) * es + rows * sh.H * es + \
+        (wl.T_valid * sh.K * sh.I + wl.T_valid * sh.Is) * es
+
+
 def gemm_flops(wl):
     sh = wl.shape
     Tv = wl.T_valid
@@ -328,11 +346,20 @@ def main():
 
     dom = "gemm_up_gate_swiglu"
     dom_ms = stage_ms[names.index(dom)]
-    achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
-                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(wl.name)}
+    if sh.dtype == wk.BF16 and wl.T_valid * sh.K <= RIDGE_ROWS * sh.E:
+        # few rows per expert: the weights are the traffic (HBM roofline)
+        gb = upgate_bytes(wl)
+        achieved = gb / (dom_ms * 1e-3) / 1e9
+        roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
+                    "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic(wl.name)}
+    else:
+        achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
+        roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
+                    "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(wl.name)}
 
     cpu = None
     if args.cpu_seconds > 0:

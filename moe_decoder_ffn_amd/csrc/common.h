@@ -52,6 +52,23 @@ constexpr int kGemmBM = HI3_GEMM_BM;
 constexpr int kGemmBN = 256;
 constexpr int kGemmBK = HI3_GEMM_BK;
 constexpr int kGemmStages = HI3_GEMM_STAGES;
+// Streaming configuration for small batches (few rows per expert, the
+// weights dominate the traffic): 64-row tiles for both projections with a
+// 4-stage ring (the whole 160 KiB of LDS), so more weight bytes are in flight
+// per CU. Chosen per call when T * K / E is at most kGemmStreamMaxRows.
+#ifndef HI3_GEMM_STREAM_MAX_ROWS
+#define HI3_GEMM_STREAM_MAX_ROWS 112
+#endif
+#ifndef HI3_GEMM_STREAM_STAGES
+#define HI3_GEMM_STREAM_STAGES 4
+#endif
+#ifndef HI3_GEMM_STREAM_BK
+#define HI3_GEMM_STREAM_BK 64
+#endif
+constexpr int kGemmStreamBM = 64;
+constexpr int kGemmStreamStages = HI3_GEMM_STREAM_STAGES;
+constexpr int kGemmStreamBK = HI3_GEMM_STREAM_BK;
+constexpr int kGemmStreamMaxRows = HI3_GEMM_STREAM_MAX_ROWS;
 constexpr int kGemmDownSplit = HI3_GEMM_DOWN_SPLIT;
 constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
 static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
@@ -160,7 +177,10 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) 
   p.T = T; p.H = H; p.E = E; p.K = K; p.I = I; p.Is = Is; p.dtype = dtype;
   p.NB = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
   p.Epad = (E + 31) / 32 * 32;
-  p.BM = dtype == kBF16 ? kGemmBM : kGemmF32BM;
+  if (dtype != kBF16)
+    p.BM = kGemmF32BM;
+  else
+    p.BM = T * K <= static_cast<int64_t>(kGemmStreamMaxRows) * E ? kGemmStreamBM : kGemmBM;
   const int64_t TK = T * K;
   p.max_tiles = static_cast<int>((TK + p.BM - 1) / p.BM + E + (T + p.BM - 1) / p.BM);
   const size_t es = dtype == kBF16 ? 2 : 4;
@@ -298,8 +318,12 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
 hipError_t launch_gather(const void *x, int64_t row_bytes, const int32_t *slotof,
                          const uint8_t *pad, int64_t T, int K, void *xs, hipStream_t s);
-hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int dtype, hipStream_t s);
-hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int dtype, hipStream_t s);
+// tile_rows: rows per listed row tile (the plan's BM); it selects the bf16
+// configuration (kGemmStreamBM: streaming tiles, else the default tiles).
+hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
+                              hipStream_t s);
+hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
+                            hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int dtype, hipStream_t s);
 
 }  // namespace hi3

@@ -436,9 +436,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 }
 
 // Block: one (row tile, column tile) job. Row tiles hold up to BM rows; a
-// group's last tile is often much shorter, and one with at most BM / 2 rows
-// (for BM >= 128) runs the half-height body: half the MFMAs and A copies,
-// the same B copies. Both bodies are straight-line code over the same LDS
+// group's last tile is often much shorter: one with at most BM / 2 rows runs
+// the half-height body (half the MFMAs and A copies, the same B copies), one
+// with at most 3 BM / 4 rows the three-quarter body (when those heights are
+// multiples of 64). The bodies are straight-line code over the same LDS
 // ring.
 template <int MODE, int BM, int BK, int NST, int WN>
 __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
@@ -453,10 +454,16 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
 
   TileJob j;
   if (!resolve_job<MODE, BN>(a, j)) return;
-  constexpr int BMS = BM / 2;
+  constexpr int BMS = BM / 2, BM3 = BM / 4 * 3;
   if constexpr (BMS >= 64 && BMS % 64 == 0) {
     if (j.rows <= BMS) {
       gemm_tile<MODE, BMS, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+      return;
+    }
+  }
+  if constexpr (BM3 > BMS && BM3 % 64 == 0) {
+    if (j.rows <= BM3) {
+      gemm_tile<MODE, BM3, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
       return;
     }
   }
@@ -563,23 +570,32 @@ static int col_tiles_host(int N, int BN, bool upgate) {
   return upgate ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
 }
 
-static hipError_t launch_gemm(GemmArgs a, int max_tiles, int dtype, bool upgate,
-                              hipStream_t s) {
+static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtype,
+                              bool upgate, hipStream_t s) {
   const int BN = dtype == kBF16 ? kGemmBN : kGemmF32BN;
+  const bool stream = dtype == kBF16 && tile_rows == kGemmStreamBM;
   a.NTn = std::max(col_tiles_host(a.cls[0].N, BN, upgate), col_tiles_host(a.cls[1].N, BN, upgate));
-  a.split = dtype == kBF16 && !upgate ? kGemmDownSplit : 1;
+  a.split = dtype == kBF16 && !upgate && !stream ? kGemmDownSplit : 1;
   a.sub_rows = a.split > 1 ? kGemmBM / a.split : 1 << 30;
   const int64_t work = static_cast<int64_t>(max_tiles) * a.split * a.NTn;
   const unsigned grid = static_cast<unsigned>((work + 7) / 8 * 8);
   if (grid == 0) return hipSuccess;
-  if (dtype == kBF16) {
+  const dim3 block(128 * kGemmWN);
+  if (stream) {
+    if (upgate)
+      hipLaunchKernelGGL((gemm_bf16_kernel<0, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages, kGemmWN>),
+                         dim3(grid), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<1, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages, kGemmWN>),
+                         dim3(grid), block, 0, s, a);
+  } else if (dtype == kBF16) {
     if (upgate)
       hipLaunchKernelGGL((gemm_bf16_kernel<0, kGemmBM, kGemmBK, kGemmStages, kGemmWN>),
-                         dim3(grid), dim3(128 * kGemmWN), 0, s, a);
+                         dim3(grid), block, 0, s, a);
     else
       hipLaunchKernelGGL((gemm_bf16_kernel<1, kGemmBM / kGemmDownSplit, kGemmBK, kGemmDownStages,
                                            kGemmWN>),
-                         dim3(grid), dim3(128 * kGemmWN), 0, s, a);
+                         dim3(grid), block, 0, s, a);
   } else {
     if (upgate)
       hipLaunchKernelGGL(gemm_f32_kernel<0>, dim3(grid), dim3(256), 0, s, a);
@@ -589,12 +605,14 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int dtype, bool upgate,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int dtype, hipStream_t s) {
-  return launch_gemm(a, max_tiles, dtype, true, s);
+hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
+                              hipStream_t s) {
+  return launch_gemm(a, max_tiles, tile_rows, dtype, true, s);
 }
 
-hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int dtype, hipStream_t s) {
-  return launch_gemm(a, max_tiles, dtype, false, s);
+hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
+                            hipStream_t s) {
+  return launch_gemm(a, max_tiles, tile_rows, dtype, false, s);
 }
 
 }  // namespace hi3

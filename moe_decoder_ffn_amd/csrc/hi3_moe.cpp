@@ -123,7 +123,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   up.tiles = tiles;
   up.gto = gto;
   up.E = E;
-  HI3_TRY(launch_gemm_upgate(up, p.max_tiles, dtype, s));
+  HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
   // 5: grouped down projection
   rec.at(5);
   GemmArgs dn{};
@@ -132,7 +132,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   dn.tiles = tiles;
   dn.gto = gto;
   dn.E = E;
-  HI3_TRY(launch_gemm_down(dn, p.max_tiles, dtype, s));
+  HI3_TRY(launch_gemm_down(dn, p.max_tiles, p.BM, dtype, s));
   // 6: combine
   rec.at(6);
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),

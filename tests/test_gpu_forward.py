@@ -87,13 +87,14 @@ def test_forward_small_all_rows(name, dtype, H, E, K, I, Is, seq, plen):
         assert np.isfinite(as_f64(out[pad == 0])).all()
 
 
-@pytest.mark.parametrize("T", [1, 64, 65, 128, 129, 256, 257, 513])
+@pytest.mark.parametrize("T", [1, 64, 65, 112, 113, 128, 129, 192, 193, 256, 257, 513])
 def test_forward_tile_boundaries(T):
     """One expert (E = K = 1), so every row goes to it and the row-tile
-    edges are hit by construction: the up/gate tile holds 256 rows and runs
-    a half-height body at <= 128 rows; the down projection runs each tile as
-    two 128-row halves (the second empty below 129 rows) with a half-height
-    body at <= 64 rows."""
+    edges are hit by construction. Up to 112 rows per expert the layer runs
+    the streaming tiles (64 rows). Above, the up/gate tile holds 256 rows and
+    runs a half-height body at <= 128 rows and a three-quarter body at <= 192;
+    the down projection runs each tile as two 128-row halves (the second
+    empty below 129 rows) with a half-height body at <= 64 rows."""
     _say(f"[forward] tile boundaries T={T}")
     shape = wk.LayerShape(H=256, E=1, K=1, I=128, Is=192, dtype=wk.BF16)
     d = wk.make_inputs(wk.custom(shape, (T,)), 11)
@@ -192,7 +193,8 @@ def _sample_rows(valid_rows, n, seed):
     return np.unique(np.concatenate([valid_rows[:2], valid_rows[-2:], pick]))
 
 
-@pytest.mark.parametrize("name", ["image_1024", "batch8_512", "skew_16k", "padded_mixed"])
+@pytest.mark.parametrize("name", ["image_1024", "batch8_512", "skew_16k", "padded_mixed",
+                                  "image_512", "prompt_512"])
 def test_forward_full_size(full_weights, name):
     w_host, w_dev = full_weights
     wl = wk.workload(name, 0)

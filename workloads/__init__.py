@@ -122,10 +122,22 @@ def workload(name: str, seed: int = 0) -> Workload:
         return Workload(name, FULL, lens, L,
                         description="4 right-padded sequences, grids 48x80, "
                                     "64x64, 80x48, 32x128, prompts 64..200")
+    if name == "image_512":
+        # one 512x512 image: 32 prompt + 1 timestep + 32*32 image + 2 suffix
+        # tokens; about 132 rows per expert, below the weight-bandwidth ridge
+        n = 32 + 1 + 32 * 32 + 2
+        return Workload(name, FULL, (n,), n,
+                        description="one 512x512 image sequence, T=1059")
+    if name == "prompt_512":
+        # a text-only sequence of 512 tokens (the causal text path), about 64
+        # rows per expert: the layer streams its weights
+        return Workload(name, FULL, (512,), 512,
+                        description="one 512-token text sequence, T=512")
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny_f32", "image_1024", "batch8_512", "skew_16k", "padded_mixed")
+WORKLOADS = ("tiny_f32", "image_1024", "batch8_512", "skew_16k", "padded_mixed",
+             "image_512", "prompt_512")
 
 
 def custom(shape: LayerShape, seq_lens, padded_len=None, skew=False,
