@@ -74,7 +74,7 @@ extern "C" {
 #define HI3_E_HIP (-5)         /* a HIP launch failed */
 
 /* Number of timed stages of hi3_moe_forward_instrumented. */
-#define HI3_NUM_STAGES 7
+#define HI3_NUM_STAGES 6
 
 /*
  * Workspace bytes that hi3_moe_forward and hi3_moe_forward_norm_residual

@@ -23,7 +23,7 @@ HI3_E_SHAPE = -2
 HI3_E_UNSUPPORTED = -3
 HI3_E_WORKSPACE = -4
 HI3_E_HIP = -5
-HI3_NUM_STAGES = 7
+HI3_NUM_STAGES = 6
 
 EXPORTED = (
     "hi3_moe_workspace_size",

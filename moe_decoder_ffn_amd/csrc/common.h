@@ -26,6 +26,8 @@ constexpr int kMaxE = 64;
 constexpr int kRouterTB = 32;
 // The bf16 router splits the hidden dimension over at most this many slices.
 constexpr int kRouterMaxSlices = 16;
+// Tokens per block of the bf16 router's logit kernel.
+constexpr int kRouterMT = 128;
 
 // bf16 grouped GEMM tiles: rows x 256 weight rows x k step, LDS stages.
 // The row-tile list holds tiles of HI3_GEMM_BM rows (the up/gate tile); the
@@ -223,7 +225,7 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) 
 struct RouterArgs {
   const void *x;
   const float *w_router;
-  const uint16_t *wsplit;
+  uint16_t *wsplit;  // bf16 layers: the split weight (written by launch_router)
   const uint8_t *pad;
   int64_t T;
   int H, E, K, Epad;
@@ -308,8 +310,6 @@ struct NormArgs {
 };
 hipError_t launch_rmsnorm(const NormArgs &a, int dtype, hipStream_t s);
 
-hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, int Epad,
-                               int H, hipStream_t s);
 // partial: [slices][E][T] fp32 scratch (one slice for fp32 layers).
 hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStream_t s);
 hipError_t launch_histogram(const int32_t *idx, const uint8_t *pad, int64_t T, int E,

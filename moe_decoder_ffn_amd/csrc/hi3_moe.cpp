@@ -91,32 +91,28 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   const int32_t *gto = static_cast<const int32_t *>(at(p.gto));
   Recorder rec{events, s};
 
-  // 0: router weight split (bf16 layers only)
+  // 0: router + per-block histogram
   rec.at(0);
-  if (dtype == HI3_BF16)
-    HI3_TRY(launch_split_router(w_router, static_cast<uint16_t *>(at(p.wsplit)), E, p.Epad, H, s));
-  // 1: router + per-block histogram
-  rec.at(1);
-  RouterArgs ra{x, w_router, static_cast<const uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
-                p.Epad, idx, wts, blkcnt, blkval};
+  RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K, p.Epad,
+                idx, wts, blkcnt, blkval};
   HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
-  // 2: scans -> expert offsets, real-row list, GEMM row tiles
-  rec.at(2);
+  // 1: scans -> expert offsets, real-row list, GEMM row tiles
+  rec.at(1);
   ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
               static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
               static_cast<int32_t *>(at(p.eoff)), expert_counts,
               static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
               static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
   HI3_TRY(launch_scan(sa, s));
-  // 3: stable slots
-  rec.at(3);
+  // 2: stable slots
+  rec.at(2);
   int32_t *perm = static_cast<int32_t *>(at(p.perm));
   ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm, slotof, vtok, vidx};
   HI3_TRY(launch_scatter(sc, s));
-  // 4: grouped [up; gate] projection + SwiGLU (routed experts and the shared
+  // 3: grouped [up; gate] projection + SwiGLU (routed experts and the shared
   // expert); the routed rows are gathered from x through the slot -> token map
   // by the GEMM's operand copies, so no grouped copy of x is materialised
-  rec.at(4);
+  rec.at(3);
   GemmArgs up{};
   up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
   up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
@@ -124,8 +120,8 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   up.gto = gto;
   up.E = E;
   HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
-  // 5: grouped down projection
-  rec.at(5);
+  // 4: grouped down projection
+  rec.at(4);
   GemmArgs dn{};
   dn.cls[0] = GemmClass{at(p.h), I, nullptr, w_down, int64_t{H} * I, at(p.y), H, H, I};
   dn.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
@@ -133,12 +129,12 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   dn.gto = gto;
   dn.E = E;
   HI3_TRY(launch_gemm_down(dn, p.max_tiles, p.BM, dtype, s));
-  // 6: combine
-  rec.at(6);
+  // 5: combine
+  rec.at(5);
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                  slotof, vidx, wts, pad_mask, T, H, K, out, resid};
   HI3_TRY(launch_combine(ca, dtype, s));
-  rec.at(7);
+  rec.at(6);
   return rec.ok ? HI3_OK : HI3_E_HIP;
 }
 
@@ -170,10 +166,9 @@ int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask,
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
-  if (dtype == HI3_BF16)
-    HI3_TRY(launch_split_router(w_router, static_cast<uint16_t *>(at(p.wsplit)), E, p.Epad, H, s));
-  RouterArgs ra{x, w_router, static_cast<const uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
-                p.Epad, topk_idx, topk_w, static_cast<int32_t *>(at(p.blkcnt)),
+  RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K, p.Epad,
+                topk_idx, topk_w,
+                static_cast<int32_t *>(at(p.blkcnt)),
                 static_cast<int32_t *>(at(p.blkval))};
   HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
   if (expert_counts) {
@@ -282,8 +277,7 @@ int hi3_moe_rmsnorm(const void *x, const void *weight, float eps, const uint8_t 
 
 const char *hi3_moe_stage_name(int stage) {
   static const char *names[HI3_NUM_STAGES] = {
-      "router_weight_split", "router", "scan", "scatter",
-      "gemm_up_gate_swiglu", "gemm_down", "combine"};
+      "router", "scan", "scatter", "gemm_up_gate_swiglu", "gemm_down", "combine"};
   if (stage < 0 || stage >= HI3_NUM_STAGES) return "?";
   return names[stage];
 }

@@ -6,11 +6,12 @@
 // bf16 activations: the fp32 router weight is split once per call into three
 // bf16 terms hi + mid + lo that sum to it exactly (Henry, Tang & Heinecke,
 // "Leveraging the bfloat16 Artificial Intelligence Datatype for
-// Higher-Precision Computations", ARITH 2019). Each product x*term is exact
-// in fp32, so bf16 MFMA with fp32 accumulation gives the fp32 router at
-// matrix-core rate instead of the vector-FMA rate.
+// Higher-Precision Computations", ARITH 2019), stored in MFMA-fragment order
+// so every fragment load is one contiguous 1 KiB per wave. Each product
+// x*term is exact in fp32, so bf16 MFMA with fp32 accumulation gives the fp32
+// router at matrix-core rate instead of the vector-FMA rate.
 //
-// The same kernel also builds the per-block expert histogram that the
+// The selection kernel also builds the per-block expert histogram that the
 // stable counting sort scans (block b covers tokens [32b, 32b + 32)).
 #include <algorithm>
 
@@ -53,13 +54,6 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
   ws[wsplit_index(2, e, h, ns, nchunks)] = f32_to_bf16(r2);  // at most 8 significant bits: exact
 }
 
-hipError_t launch_split_router(const float *w_router, uint16_t *wsplit, int E, int Epad,
-                               int H, hipStream_t s) {
-  const int64_t n = static_cast<int64_t>(Epad) * H;
-  hipLaunchKernelGGL(split_router_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                     dim3(256), 0, s, w_router, wsplit, E, Epad, H);
-  return hipGetLastError();
-}
 
 // --------------------------------------------------------------- selection
 
@@ -83,6 +77,8 @@ struct SelectShared {
   int esel[kRouterTB][kMaxE];
   uint64_t selmask[kRouterTB];
 };
+
+__device__ __forceinline__ float nan_as_neg_inf(float v) { return v != v ? -INFINITY : v; }
 
 // Orders this wave's LDS writes before its following LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -134,8 +130,11 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
       if (lane == 0) sh.selmask[rr] = 0;
       continue;
     }
+    // A NaN logit counts as -infinity: the order (larger first, lower index
+    // on equal values) is then total, the ranks of the E lanes are a
+    // permutation, and exactly K experts are selected whatever the inputs.
     const bool live = lane < E;
-    const float l = live ? sh.logit[rr][lane] : -INFINITY;
+    const float l = live ? nan_as_neg_inf(sh.logit[rr][lane]) : -INFINITY;
     float m = -INFINITY;
     int rank = 0;
 #pragma unroll
@@ -146,8 +145,9 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
       for (int q = 0; q < 4; ++q) {
         const int e = 4 * i + q;
         if (EC == 0 && e >= E) break;
-        m = fmaxf(m, v[q]);
-        rank += (v[q] > l || (v[q] == l && e < lane)) ? 1 : 0;
+        const float vq = nan_as_neg_inf(v[q]);
+        m = fmaxf(m, vq);
+        rank += (vq > l || (vq == l && e < lane)) ? 1 : 0;
       }
     }
     const float ex = live ? expf(l - m) : 0.0f;
@@ -199,61 +199,61 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
 
 // --------------------------------------------------------------- bf16 router
 
-// Partial logits of 32 tokens over one slice of the hidden dimension.
-// Grid: x = blocks of 32 tokens, y = k slices (each a range of 64-wide
-// chunks). 256 threads = 4 waves; wave w accumulates the chunks
-// c = first + w, first + w + 4, ... of all 32 tokens x Epad experts with
-// v_mfma_f32_32x32x16_bf16, the 4 wave partials are summed in a fixed order
-// in LDS and written to partial[slice][e][t]. Splitting the hidden dimension
-// across blocks gives the machine enough waves at a few thousand tokens.
+// Partial logits of kRouterMT tokens over one slice of the hidden
+// dimension. Grid: x = blocks of kRouterMT tokens, y = k slices (ranges of
+// 64-wide chunks). 256 threads = 4 waves; wave w takes the chunks
+// first + w, first + w + 4, ... of the slice for all kRouterMT / 32 token
+// tiles, so each router-weight fragment it loads (and splits) serves every
+// token tile of the block. The 4 waves' sums are added in a fixed order in
+// LDS and written to partial[slice][e][t].
 //
-// MFMA operand layout used here (32x32x16): lane l supplies row (l % 32) of
-// A and column (l % 32) of B, and 8 consecutive k values; lanes 0-31 and
-// 32-63 cover two disjoint k groups. Any k assignment is valid as long as A
-// and B agree, so within a 64-wide chunk lane half g takes k in
-// [32g, 32g + 32) and MFMA q uses its elements [8q, 8q + 8): each lane reads
-// 64 contiguous bytes per operand row. Result element v of lane l is
-// row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+// MFMA operand layout (v_mfma_f32_32x32x16_bf16): lane l supplies row
+// (l % 32) of A and column (l % 32) of B, and 8 consecutive k values; lanes
+// 0-31 and 32-63 cover two disjoint k groups. Any k assignment is valid as
+// long as A and B agree: within a 64-wide chunk lane half g takes k in
+// [32g, 32g + 32) and step q uses its elements [8q, 8q + 8), so each lane
+// reads 64 contiguous bytes of x and 128 of the weight row per chunk.
+// Result element v of lane l is token 8 (v / 4) + 4 (l / 32) + v % 4 of the
+// tile and expert l % 32 of the column tile. The three terms of a weight go
+// into the same accumulator, hi first; the next chunk's operands are loaded
+// while the current chunk is multiplied.
 template <int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void router_partial_kernel(RouterArgs a, float *partial, int chunks_per_slice) {
-  __shared__ float part[4][kRouterTB][NS * 32 + 1];
+__global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a, float *partial,
+                                                            int chunks_per_slice) {
+  constexpr int TT = kRouterMT / 32;  // token tiles per block
+  __shared__ float part[4][kRouterMT][NS * 32 + 1];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r = lane & 31;
   const int g = lane >> 5;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
-  const int64_t t = t0 + r;
-  const bool row_ok = t < a.T && !(a.pad && a.pad[t]);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterMT;
   const uint16_t *x = static_cast<const uint16_t *>(a.x);
-  const uint16_t *xrow = x + (row_ok ? t : 0) * static_cast<int64_t>(a.H);
   const int nchunks = a.H / 64;
 
-  f32x16_t acc_hi[NS], acc_lo[NS];
+  const uint16_t *xrow[TT];
+  bool row_ok[TT];
 #pragma unroll
-  for (int n = 0; n < NS; ++n)
+  for (int tt = 0; tt < TT; ++tt) {
+    const int64_t t = t0 + tt * 32 + r;
+    row_ok[tt] = t < a.T && !(a.pad && a.pad[t]);
+    xrow[tt] = x + (row_ok[tt] ? t : 0) * static_cast<int64_t>(a.H);
+  }
+
+  f32x16_t acc[TT][NS];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      acc_hi[n][v] = 0.0f;
-      acc_lo[n][v] = 0.0f;
-    }
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tt][n][v] = 0.0f;
 
   const int c_first = blockIdx.y * chunks_per_slice;
   const int c_end = min(nchunks, c_first + chunks_per_slice);
-  for (int c = c_first + wave; c < c_end; c += 4) {
-    // every operand of the chunk is requested before the first MFMA, so the
-    // loads are in flight together
+  // operands of one chunk: the split weights' fragments and the token rows
+  u32x4_t wv[NS][3][4];
+  u32x4_t xv[TT][4];
+  auto load = [&](int c) __attribute__((always_inline)) {
     const int k0 = c * 64 + g * 32;
-    u32x4_t av[4];
-    u32x4_t bv[NS][3][4];
-    if (row_ok) {
-      const u32x4_t *p = reinterpret_cast<const u32x4_t *>(xrow + k0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) av[q] = p[q];
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) av[q] = u32x4_t{0u, 0u, 0u, 0u};
-    }
 #pragma unroll
     for (int n = 0; n < NS; ++n)
 #pragma unroll
@@ -262,46 +262,71 @@ void router_partial_kernel(RouterArgs a, float *partial, int chunks_per_slice) {
         const u32x4_t *p = reinterpret_cast<const u32x4_t *>(a.wsplit) +
                            (((static_cast<int64_t>(sp) * NS + n) * nchunks + c) * 4) * 64 + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bv[n][sp][q] = p[q * 64];
+        for (int q = 0; q < 4; ++q) wv[n][sp][q] = p[q * 64];
       }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const u32x4_t *p = reinterpret_cast<const u32x4_t *>(xrow[tt] + k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[tt][q] = row_ok[tt] ? p[q] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  int c = c_first + wave;
+  if (c < c_end) load(c);
+  for (; c < c_end; c += 4) {
+    // keep this chunk's operands, then request the next chunk's before the
+    // MFMAs
+    u32x4_t bw[NS][3][4];
+    u32x4_t av[TT][4];
 #pragma unroll
     for (int n = 0; n < NS; ++n)
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[q]);
-          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bv[n][sp][q]);
-          if (sp == 0)
-            acc_hi[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc_hi[n], 0, 0, 0);
-          else
-            acc_lo[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc_lo[n], 0, 0, 0);
-        }
-    // all of the chunk's loads are issued before its MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x020, 4 + NS * 12, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NS * 12, 0);
+        for (int q = 0; q < 4; ++q) bw[n][sp][q] = wv[n][sp][q];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[tt][q] = xv[tt][q];
+    if (c + 4 < c_end) load(c + 4);
+    // consecutive MFMAs update different accumulators (TT x NS of them)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int n = 0; n < NS; ++n)
+            acc[tt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, av[tt][q]),
+                __builtin_bit_cast(bf16x8_t, bw[n][sp][q]), acc[tt][n], 0, 0, 0);
   }
 #pragma unroll
-  for (int n = 0; n < NS; ++n)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      part[wave][(v >> 2) * 8 + g * 4 + (v & 3)][n * 32 + r] = acc_hi[n][v] + acc_lo[n][v];
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        part[wave][tt * 32 + (v >> 2) * 8 + g * 4 + (v & 3)][n * 32 + r] = acc[tt][n][v];
   __syncthreads();
   float *out = partial + static_cast<int64_t>(blockIdx.y) * a.E * a.T;
-  for (int i = threadIdx.x; i < kRouterTB * a.E; i += blockDim.x) {
-    const int e = i / kRouterTB, rr = i % kRouterTB;
-    const int64_t tt = t0 + rr;
-    if (tt < a.T)
-      out[static_cast<int64_t>(e) * a.T + tt] =
+  for (int i = threadIdx.x; i < kRouterMT * a.E; i += blockDim.x) {
+    const int e = i / kRouterMT, rr = i % kRouterMT;
+    const int64_t t = t0 + rr;
+    if (t < a.T)
+      out[static_cast<int64_t>(e) * a.T + t] =
           ((part[0][rr][e] + part[1][rr][e]) + part[2][rr][e]) + part[3][rr][e];
   }
 }
 
 int router_slices(int64_t T, int H) {
-  const int nb = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
-  // at least one chunk per wave, at most kRouterMaxSlices
+  const int nb = static_cast<int>((T + kRouterMT - 1) / kRouterMT);
+  // one block per CU (the block's LDS allows no second one): at most 256
+  // blocks, so none waits for a second round; at least 4 chunks (one per
+  // wave) per slice
   const int max_slices = std::max(1, std::min(kRouterMaxSlices, H / 256));
-  const int want = (512 + nb - 1) / nb;  // about two waves per SIMD
+  const int want = 256 / nb;
   return std::max(1, std::min(max_slices, want));
 }
 
@@ -334,14 +359,16 @@ hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStre
   if (dtype == kF32) {
     hipLaunchKernelGGL(router_f32_kernel, dim3(nb), dim3(256), 0, s, a, partial);
   } else {
+    const int64_t nw = static_cast<int64_t>(a.Epad) * a.H;
+    hipLaunchKernelGGL(split_router_kernel, dim3(static_cast<unsigned>((nw + 255) / 256)),
+                       dim3(256), 0, s, a.w_router, a.wsplit, a.E, a.Epad, a.H);
     slices = router_slices(a.T, a.H);
     const int cps = (a.H / 64 + slices - 1) / slices;
+    const dim3 grid(static_cast<unsigned>((a.T + kRouterMT - 1) / kRouterMT), slices);
     if (a.Epad <= 32)
-      hipLaunchKernelGGL(router_partial_kernel<1>, dim3(nb, slices), dim3(256), 0, s, a,
-                         partial, cps);
+      hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, s, a, partial, cps);
     else
-      hipLaunchKernelGGL(router_partial_kernel<2>, dim3(nb, slices), dim3(256), 0, s, a,
-                         partial, cps);
+      hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, a, partial, cps);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -31,7 +31,7 @@
  *      made on the fp32 logits, because fp32 p can underflow and make
  *      distinct logits tie. On equal logits the lower expert index is taken
  *      first. Output order: descending logit (so non-increasing weight), ties
- *      by ascending index.
+ *      by ascending index. A NaN logit counts as -infinity in steps 2-4.
  *   4. Renormalise: w[k] = p[idx[k]] / sum_k' p[idx[k']], sum in k order,
  *      in fp32.
  *   5. For each selected expert e: [u; g] = W13[e] x with W13[e] of shape
@@ -137,10 +137,16 @@ static void router_logits_row(const void *x, int dtype, int64_t t, int64_t H,
 
 /* Steps 2-4 for one row: softmax over all experts, top-K, renormalise
  * (fp32). */
-static void softmax_topk_row(const float *logits, int E, int K,
+static void softmax_topk_row(const float *logits_in, int E, int K,
                              float *probs, int32_t *idx, float *w)
 {
-    float m = logits[0];
+    /* A NaN logit (from a NaN weight or input) counts as -infinity: ranked
+     * after every number (equal values by index) and given probability 0,
+     * so exactly K distinct experts are always selected. */
+    float logits[1024];
+    for (int e = 0; e < E; e++)
+        logits[e] = isnan(logits_in[e]) ? -INFINITY : logits_in[e];
+    float m = E > 0 ? logits[0] : -INFINITY;
     for (int e = 1; e < E; e++)
         if (logits[e] > m)
             m = logits[e];

@@ -102,6 +102,28 @@ def test_forward_tile_boundaries(T):
     assert np.all(idx == 0) and np.all(w == 1.0) and cnt[0] == T
 
 
+def test_forward_nan_rows_keep_dispatch_in_bounds():
+    # Real rows whose input is NaN and a NaN router row: routing still picks
+    # exactly K experts per row (a NaN logit counts as -infinity), so the
+    # dispatch sizes hold; the NaN rows give NaN outputs and every other row
+    # matches the oracle.
+    _say("[forward] NaN rows and a NaN router row")
+    shape = wk.LayerShape(H=256, E=16, K=4, I=128, Is=128, dtype=wk.BF16)
+    d = wk.make_inputs(wk.custom(shape, (200,)), 5)
+    d["x"][[3, 111]] = wk.BF16_NAN
+    d["w_router"] = d["w_router"] * np.float32(5.0)
+    d["w_router"][9] = np.nan
+    out, idx, w, cnt = gpu_forward(upload(d), 4)
+    assert int(cnt.sum()) == 200 * 4 and cnt[9] == 0
+    ok = np.setdiff1d(np.arange(200), [3, 111])
+    ref = oracle.route(d["x"], d["w_router"], 4)
+    near, ref_idx, ref_w = check_routes(idx[ok], w[ok], {k: v[ok] for k, v in ref.items()},
+                                        None, 16, 4)
+    exact = oracle.moe(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"], K=4,
+                       rows=ok, idx=ref_idx, w=ref_w)["exact"]
+    check_output(out[ok], exact, wk.BF16)
+
+
 @pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
 def test_forward_k_equals_e(dtype):
     _say(f"[forward] K=E dtype={dtype}")

@@ -106,3 +106,25 @@ def test_route_all_padding():
     pad = np.ones(70, np.uint8)
     idx, w, cnt = run_route(x, wk.make_router_weight(shape, 0), 4, pad)
     assert np.all(idx == -1) and np.all(w == 0) and np.all(cnt == 0)
+
+
+def test_route_nan_logits_select_exactly_k():
+    # A NaN router row (that expert's logit is NaN for every token) and real
+    # rows whose input is NaN (every logit NaN): a NaN logit counts as
+    # -infinity, so every real row still selects exactly K distinct experts
+    # and the counts total T * K; ids match the oracle on every row.
+    _say("[route] NaN logits")
+    shape = wk.LayerShape(H=512, E=64, K=8, I=64, Is=64, dtype=wk.BF16)
+    x, _ = wk.make_x(wk.custom(shape, (300,)), 4)
+    x[[7, 150]] = wk.BF16_NAN
+    wr = wk.make_router_weight(shape, 4)
+    wr[5] = np.nan
+    idx, w, cnt = run_route(x, wr, 8)
+    ref = oracle.route(x, wr, 8)
+    # expert 5 is chosen only by the two all-NaN rows, which tie every expert
+    # at -infinity and take experts 0..7
+    assert int(cnt.sum()) == 300 * 8 and cnt[5] == 2
+    assert np.all(np.sort(idx, 1)[:, 1:] != np.sort(idx, 1)[:, :-1])
+    assert np.array_equal(idx[[7, 150]], ref["idx"][[7, 150]])
+    ok = np.setdiff1d(np.arange(300), [7, 150])
+    check_routes(idx[ok], w[ok], {k: v[ok] for k, v in ref.items()}, None, 64, 8)

@@ -101,6 +101,30 @@ def test_uniform_router():
     assert np.all(r["w"] == 0.25)
 
 
+def test_nan_logits_rank_last():
+    # A NaN logit counts as -infinity: a router row of NaN makes that
+    # expert's logit NaN for every token; it gets probability 0, is never
+    # selected, and the other experts' selection and weights are those of
+    # the router without that expert (closed form: the same top-K over the
+    # remaining logits, renormalised the same way).
+    wl, d = _small(wk.BF16, T=30, E=8, K=3, seed=12)
+    wr = d["w_router"] * np.float32(10.0)
+    bad = wr.copy()
+    bad[2] = np.nan
+    r = oracle.route(d["x"], bad, K=3)
+    assert np.all(r["idx"] != 2) and np.all(r["probs"][:, 2] == 0.0)
+    keep = [e for e in range(8) if e != 2]
+    r7 = oracle.route(d["x"], wr[keep], K=3)
+    assert np.array_equal(r["idx"], np.array(keep)[r7["idx"]])
+    np.testing.assert_allclose(r["w"], r7["w"], rtol=1e-6)
+    # a row whose input is NaN: every logit is NaN, all count as -infinity,
+    # and the tie rule takes experts 0..K-1
+    x = d["x"].copy()
+    x[5] = wk.BF16_NAN
+    r = oracle.route(x, wr, K=3)
+    assert np.array_equal(r["idx"][5], [0, 1, 2])
+
+
 def test_selection_survives_fp32_underflow():
     # One expert's logit is far above the rest, so every other fp32
     # probability underflows to 0 (or a subnormal) and many tie in p. The
