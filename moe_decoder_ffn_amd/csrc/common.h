@@ -148,7 +148,7 @@ struct Plan {
   int BM;         // grouped-GEMM tile rows (per dtype)
   int max_tiles;  // upper bound on grouped-GEMM row tiles
   size_t wsplit;  // [3][Epad][H] bf16: router weight split into 3 bf16 terms
-  size_t rpart;   // [slices][E][T] fp32: router partial logits
+  size_t rpart;   // [slices][T][E] fp32: router partial logits
   size_t idx;     // [T*K] int32 routes when the caller passes none
   size_t wts;     // [T*K] fp32
   size_t blkcnt;  // [NB][E] int32 per-block expert histogram
@@ -310,7 +310,7 @@ struct NormArgs {
 };
 hipError_t launch_rmsnorm(const NormArgs &a, int dtype, hipStream_t s);
 
-// partial: [slices][E][T] fp32 scratch (one slice for fp32 layers).
+// partial: [slices][T][E] fp32 scratch (one slice for fp32 layers).
 hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStream_t s);
 hipError_t launch_histogram(const int32_t *idx, const uint8_t *pad, int64_t T, int E,
                             int K, int32_t *blkcnt, int32_t *blkval, hipStream_t s);

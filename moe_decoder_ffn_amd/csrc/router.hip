@@ -61,18 +61,21 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
 // block: 8 waves, one token per wave at a time, lane = expert; then the
 // block's expert histogram and real-row count.
 // The token's logits are the slice partials summed in slice order. Every
-// lane reads all of the token's logits from LDS (broadcast reads, no
-// cross-lane shuffles) to get the maximum and its own rank in the selection
-// order (larger logit first, lower index first on equal logits; softmax is
+// lane reads all of the token's logits from the other lanes (readlane, in
+// expert order) to get the maximum and its own rank in the selection order
+// (larger logit first, lower index first on equal logits; softmax is
 // strictly increasing, so this is the order of the probabilities, and fp32
 // underflow of small probabilities cannot change it). Z sums exp(l - max) in
 // ascending expert order, the selected p = exp(l - max) / Z are summed in
 // selection order, and each is divided by that sum.
-// partial: [slices][E][T] fp32. EC = 64: E is 64 (no per-expert guards);
+// partial: [slices][T][E] fp32. EC = 64: E is 64 (no per-expert guards);
 // EC = 0: any E <= 64.
+#ifndef HI3_SEL_THREADS
+#define HI3_SEL_THREADS 1024
+#endif
+// threads of the selection kernel (kRouterTB / (threads / 64) tokens per wave)
+constexpr int kSelThreads = HI3_SEL_THREADS;
 struct SelectShared {
-  float logit[kRouterTB][kMaxE + 4];  // 16-byte aligned rows
-  float ex[kRouterTB][kMaxE + 4];
   float psel[kRouterTB][kMaxE];
   int esel[kRouterTB][kMaxE];
   uint64_t selmask[kRouterTB];
@@ -80,15 +83,20 @@ struct SelectShared {
 
 __device__ __forceinline__ float nan_as_neg_inf(float v) { return v != v ? -INFINITY : v; }
 
-// Orders this wave's LDS writes before its following LDS reads.
+// Orders this wave's LDS writes before its following LDS reads: LDS
+// operations of one wave complete in order, so waiting for the wave's own
+// LDS counter is enough (a memory fence would also wait for the wave's
+// global stores).
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int EC>
-__global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const float *partial,
+__global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a,
+                                                                   const float *partial,
                                                             int slices) {
   __shared__ SelectShared sh;
   const int E = EC > 0 ? EC : a.E;
@@ -97,26 +105,35 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
   const int lane = threadIdx.x & 63;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
 
-  // logits of the block's tokens: thread (expert e, token rr) sums the
-  // slices; the slice reads are issued together
-  for (int i = threadIdx.x; i < kRouterTB * E; i += blockDim.x) {
-    const int e = i / kRouterTB, rr = i % kRouterTB;
-    const int64_t tt = t0 + rr;
-    float v[kRouterMaxSlices];
+  // logits of the wave's tokens: lane e sums partial[ks][t][e] over the
+  // slices in slice order (one coalesced 256-byte row per slice); all of the
+  // wave's loads are issued before the first sum
+  constexpr int TPW = kRouterTB / (kSelThreads / 64);  // tokens per wave
+  float lsum[TPW];
+  {
+    float v[TPW][kRouterMaxSlices];
 #pragma unroll
-    for (int ks = 0; ks < kRouterMaxSlices; ++ks)
-      v[ks] = (ks < slices && tt < a.T)
-                  ? partial[(static_cast<int64_t>(ks) * E + e) * a.T + tt]
-                  : 0.0f;
-    float l = 0.0f;
+    for (int j = 0; j < TPW; ++j) {
+      const int64_t t = t0 + wave + (kSelThreads / 64) * j;
+      const int64_t tc = t < a.T ? t : a.T - 1;
+      const int ec = lane < E ? lane : E - 1;
 #pragma unroll
-    for (int ks = 0; ks < kRouterMaxSlices; ++ks)
-      if (ks < slices) l += v[ks];
-    sh.logit[rr][e] = l;
+      for (int ks = 0; ks < kRouterMaxSlices; ++ks)
+        if (ks < slices) v[j][ks] = partial[(static_cast<int64_t>(ks) * a.T + tc) * E + ec];
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      float l = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kRouterMaxSlices; ++ks)
+        if (ks < slices) l += v[j][ks];
+      lsum[j] = l;
+    }
   }
-  __syncthreads();
 
-  for (int rr = wave; rr < kRouterTB; rr += blockDim.x >> 6) {
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int rr = wave + (kSelThreads / 64) * j;
     const int64_t t = t0 + rr;
     if (t >= a.T) {
       if (lane == 0) sh.selmask[rr] = 0;
@@ -133,36 +150,26 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
     // A NaN logit counts as -infinity: the order (larger first, lower index
     // on equal values) is then total, the ranks of the E lanes are a
     // permutation, and exactly K experts are selected whatever the inputs.
+    // Every lane walks the row's logits in expert order (readlane: no
+    // memory round trips) for the maximum, its own rank in the selection
+    // order and the softmax denominator, summed in ascending expert order.
     const bool live = lane < E;
-    const float l = live ? nan_as_neg_inf(sh.logit[rr][lane]) : -INFINITY;
+    const float l = live ? nan_as_neg_inf(lsum[j]) : -INFINITY;
     float m = -INFINITY;
     int rank = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxE / 4; ++i) {
-      if (EC == 0 && 4 * i >= E) break;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&sh.logit[rr][4 * i]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * i + q;
-        if (EC == 0 && e >= E) break;
-        const float vq = nan_as_neg_inf(v[q]);
-        m = fmaxf(m, vq);
-        rank += (vq > l || (vq == l && e < lane)) ? 1 : 0;
-      }
+    for (int e = 0; e < kMaxE; ++e) {
+      if (EC == 0 && e >= E) break;
+      const float ve = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
+      m = fmaxf(m, ve);
+      rank += (ve > l || (ve == l && e < lane)) ? 1 : 0;
     }
     const float ex = live ? expf(l - m) : 0.0f;
-    if (live) sh.ex[rr][lane] = ex;
-    wave_lds_sync();
     float z = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxE / 4; ++i) {
-      if (EC == 0 && 4 * i >= E) break;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&sh.ex[rr][4 * i]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (EC == 0 && 4 * i + q >= E) break;
-        z += v[q];  // ascending expert order
-      }
+    for (int e = 0; e < kMaxE; ++e) {
+      if (EC == 0 && e >= E) break;
+      z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), e));
     }
     const float p = ex / z;
     const bool sel = live && rank < K;
@@ -172,9 +179,10 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
     }
     const uint64_t mask = __ballot(sel);
     wave_lds_sync();
+    // the selected probabilities summed in selection order
+    float ssum = 0.0f;
+    for (int k = 0; k < K; ++k) ssum += sh.psel[rr][k];
     if (lane < K) {
-      float ssum = 0.0f;
-      for (int k = 0; k < K; ++k) ssum += sh.psel[rr][k];  // selection order
       a.idx[t * K + lane] = sh.esel[rr][lane];
       a.wts[t * K + lane] = sh.psel[rr][lane] / ssum;
     }
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(512) void router_select_kernel(RouterArgs a, const 
 // first + w, first + w + 4, ... of the slice for all kRouterMT / 32 token
 // tiles, so each router-weight fragment it loads (and splits) serves every
 // token tile of the block. The 4 waves' sums are added in a fixed order in
-// LDS and written to partial[slice][e][t].
+// LDS and written to partial[slice][t][e].
 //
 // MFMA operand layout (v_mfma_f32_32x32x16_bf16): lane l supplies row
 // (l % 32) of A and column (l % 32) of B, and 8 consecutive k values; lanes
@@ -312,11 +320,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a, float 
   __syncthreads();
   float *out = partial + static_cast<int64_t>(blockIdx.y) * a.E * a.T;
   for (int i = threadIdx.x; i < kRouterMT * a.E; i += blockDim.x) {
-    const int e = i / kRouterMT, rr = i % kRouterMT;
+    const int rr = i / a.E, e = i % a.E;
     const int64_t t = t0 + rr;
     if (t < a.T)
-      out[static_cast<int64_t>(e) * a.T + t] =
-          ((part[0][rr][e] + part[1][rr][e]) + part[2][rr][e]) + part[3][rr][e];
+      out[t * a.E + e] = ((part[0][rr][e] + part[1][rr][e]) + part[2][rr][e]) + part[3][rr][e];
   }
 }
 
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(RouterArgs a, float *pa
       const float *wrow = a.w_router + static_cast<int64_t>(lane) * a.H;
       float acc = 0.0f;
       for (int h = 0; h < a.H; ++h) acc = fmaf(xr[h], wrow[h], acc);
-      partial[static_cast<int64_t>(lane) * a.T + t] = acc;
+      partial[t * a.E + lane] = acc;
     }
   }
 }
@@ -373,10 +380,11 @@ hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.E == kMaxE)
-    hipLaunchKernelGGL(router_select_kernel<kMaxE>, dim3(nb), dim3(512), 0, s, a, partial,
+    hipLaunchKernelGGL(router_select_kernel<kMaxE>, dim3(nb), dim3(kSelThreads), 0, s, a, partial,
                        slices);
   else
-    hipLaunchKernelGGL(router_select_kernel<0>, dim3(nb), dim3(512), 0, s, a, partial, slices);
+    hipLaunchKernelGGL(router_select_kernel<0>, dim3(nb), dim3(kSelThreads), 0, s, a, partial,
+                       slices);
   return hipGetLastError();
 }
 
