@@ -411,6 +411,153 @@ void orc_rmsnorm(const void *x, int dtype, const void *weight, double eps,
     }
 }
 
+/*
+ * Backward pass of the layer (for the pages' fine-tuning: HunyuanImage-3.0
+ * model-coverage page, "Train": LoRA and full fine-tuning of the MoE
+ * decoder). Given dout = dL/dout for the real rows, the gradients of
+ * L = sum_t dout[t] . out[t] with respect to x and every weight, with the
+ * routes held fixed (top-k selection is piecewise constant; its gradient
+ * flows only through the renormalised weights), evaluated at the forward's
+ * stored values: the router's fp32 p and w, the SwiGLU activation h rounded
+ * to the dtype as the forward stores it, the pre-activations u, g and every
+ * product exact (fp64). Per real row t, for each routed k (expert e, weight
+ * w_k) and then the shared expert (weight 1):
+ *   y_k   = W2[e] h_k                      (h_k = dtype(SiLU(g) u))
+ *   dw_k  = dout . y_k,  dy_k = w_k dout
+ *   dW2[e]  += dy_k h_k^T,  dh = W2[e]^T dy_k
+ *   du = dh SiLU(g),  dg = dh u SiLU'(g),  SiLU'(g) = s (1 + g (1 - s)),
+ *        s = 1 / (1 + exp(-g))
+ *   dW13[e] += [du; dg] x^T (up rows first),  dx += W13[e]^T [du; dg]
+ * Router: w_k = p_k / S with S = sum of the selected p, so for a selected j
+ *   dp_j = (dw_j - sum_k w_k dw_k) / S  (0 for the others);
+ *   softmax: dl_e = p_e (dp_e - sum_j p_j dp_j);
+ *   dWr += dl x^T,  dx += Wr^T dl.
+ * idx_in / w_in ([T, K]) replace the router's choice when given (p is still
+ * the router's). Weight gradients are summed over tokens in ascending t
+ * (single-threaded, deterministic); padding rows contribute nothing and
+ * their dx rows are not written. Any output pointer may be NULL.
+ */
+void orc_moe_backward(const void *x, int dtype, const float *w_router, const void *w13,
+                      const void *w2, const void *ws13, const void *ws2, const uint8_t *pad,
+                      const void *dout, int64_t T, int64_t H, int E, int K, int64_t I,
+                      int64_t Is, const int32_t *idx_in, const double *w_in, double *dx,
+                      double *dwr, double *dw13, double *dw2, double *dws13, double *dws2)
+{
+    int64_t Imax = I > Is ? I : Is;
+    double *xr = malloc(sizeof(double) * (size_t)H);
+    double *dv = malloc(sizeof(double) * (size_t)H);
+    double *dxr = malloc(sizeof(double) * (size_t)H);
+    double *dy = malloc(sizeof(double) * (size_t)H);
+    double *u = malloc(sizeof(double) * (size_t)Imax);
+    double *g = malloc(sizeof(double) * (size_t)Imax);
+    double *hb = malloc(sizeof(double) * (size_t)Imax);
+    double *du = malloc(sizeof(double) * (size_t)Imax);
+    double *dg = malloc(sizeof(double) * (size_t)Imax);
+    if (dwr) memset(dwr, 0, sizeof(double) * (size_t)E * (size_t)H);
+    if (dw13) memset(dw13, 0, sizeof(double) * (size_t)E * 2 * (size_t)I * (size_t)H);
+    if (dw2) memset(dw2, 0, sizeof(double) * (size_t)E * (size_t)H * (size_t)I);
+    if (dws13) memset(dws13, 0, sizeof(double) * 2 * (size_t)Is * (size_t)H);
+    if (dws2) memset(dws2, 0, sizeof(double) * (size_t)H * (size_t)Is);
+    for (int64_t t = 0; t < T; t++) {
+        if (pad && pad[t])
+            continue;
+        float lbuf[1024], pbuf[1024], wf[1024];
+        int32_t idx[1024];
+        double w[1024], dw[1024];
+        router_logits_row(x, dtype, t, H, w_router, E, lbuf);
+        softmax_topk_row(lbuf, E, K, pbuf, idx, wf);
+        for (int k = 0; k < K; k++)
+            w[k] = (double)wf[k];
+        if (idx_in) {
+            for (int k = 0; k < K; k++) {
+                idx[k] = idx_in[t * K + k];
+                w[k] = w_in[t * K + k];
+            }
+        }
+        for (int64_t h = 0; h < H; h++) {
+            xr[h] = elem(x, dtype, t * H + h);
+            dv[h] = elem(dout, dtype, t * H + h);
+            dxr[h] = 0.0;
+        }
+        /* routed experts (k >= 0, weight w[k]) and the shared expert (k = K, weight 1) */
+        for (int k = 0; k <= K; k++) {
+            const int shared = k == K;
+            const int e = shared ? 0 : idx[k];
+            const int64_t II = shared ? Is : I;
+            const void *W13 = shared ? ws13 : offset_elems(w13, dtype, (size_t)e * expert_up_gate_elems(H, I));
+            const void *W2 = shared ? ws2 : offset_elems(w2, dtype, (size_t)e * expert_down_elems(H, I));
+            double *gW13 = shared ? dws13 : (dw13 ? dw13 + (size_t)e * 2 * (size_t)I * (size_t)H : NULL);
+            double *gW2 = shared ? dws2 : (dw2 ? dw2 + (size_t)e * (size_t)H * (size_t)I : NULL);
+            const double wk = shared ? 1.0 : w[k];
+            for (int64_t i = 0; i < II; i++) {
+                double uu = 0.0, gg = 0.0;
+                for (int64_t h = 0; h < H; h++) {
+                    uu += xr[h] * elem(W13, dtype, i * H + h);
+                    gg += xr[h] * elem(W13, dtype, (II + i) * H + h);
+                }
+                u[i] = uu;
+                g[i] = gg;
+                hb[i] = round_dtype(gg / (1.0 + exp(-gg)) * uu, dtype);
+            }
+            double dwk = 0.0;
+            for (int64_t j = 0; j < H; j++) {
+                double yj = 0.0;
+                for (int64_t i = 0; i < II; i++)
+                    yj += hb[i] * elem(W2, dtype, j * II + i);
+                dwk += dv[j] * yj;
+                dy[j] = wk * dv[j];
+            }
+            if (!shared)
+                dw[k] = dwk;
+            if (gW2)
+                for (int64_t j = 0; j < H; j++)
+                    for (int64_t i = 0; i < II; i++)
+                        gW2[j * II + i] += dy[j] * hb[i];
+            for (int64_t i = 0; i < II; i++) {
+                double dh = 0.0;
+                for (int64_t j = 0; j < H; j++)
+                    dh += elem(W2, dtype, j * II + i) * dy[j];
+                double sg = 1.0 / (1.0 + exp(-g[i]));
+                du[i] = dh * g[i] * sg;
+                dg[i] = dh * u[i] * sg * (1.0 + g[i] * (1.0 - sg));
+            }
+            for (int64_t i = 0; i < II; i++)
+                for (int64_t h = 0; h < H; h++) {
+                    if (gW13) {
+                        gW13[i * H + h] += du[i] * xr[h];
+                        gW13[(II + i) * H + h] += dg[i] * xr[h];
+                    }
+                    dxr[h] += elem(W13, dtype, i * H + h) * du[i] +
+                              elem(W13, dtype, (II + i) * H + h) * dg[i];
+                }
+        }
+        /* router */
+        double S = 0.0, A = 0.0, B = 0.0;
+        double dp[1024];
+        for (int e = 0; e < E; e++)
+            dp[e] = 0.0;
+        for (int k = 0; k < K; k++) {
+            S += (double)pbuf[idx[k]];
+            A += w[k] * dw[k];
+        }
+        for (int k = 0; k < K; k++)
+            dp[idx[k]] = (dw[k] - A) / S;
+        for (int e = 0; e < E; e++)
+            B += (double)pbuf[e] * dp[e];
+        for (int e = 0; e < E; e++) {
+            double dl = (double)pbuf[e] * (dp[e] - B);
+            for (int64_t h = 0; h < H; h++) {
+                if (dwr) dwr[(int64_t)e * H + h] += dl * xr[h];
+                dxr[h] += (double)w_router[(int64_t)e * H + h] * dl;
+            }
+        }
+        if (dx)
+            for (int64_t h = 0; h < H; h++)
+                dx[t * H + h] = dxr[h];
+    }
+    free(xr); free(dv); free(dxr); free(dy); free(u); free(g); free(hb); free(du); free(dg);
+}
+
 void orc_round_bf16_array(const double *v, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; i++)
