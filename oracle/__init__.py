@@ -39,7 +39,7 @@ def _load():
                                            i64, i64, P, i64, P, P, P]
         lib.orc_moe_dense_rows.restype = None
         lib.orc_moe_backward.argtypes = [P, i32, P, P, P, P, P, P, P, i64, i64, i32, i32, i64,
-                                         i64, P, P, P, P, P, P, P, P]
+                                         i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_moe_backward.restype = None
         lib.orc_rmsnorm.argtypes = [P, i32, P, ctypes.c_double, P, i64, i64, P]
         lib.orc_rmsnorm.restype = None
@@ -221,12 +221,14 @@ def moe_norm_residual(h, norm_weight, w_router, w13, w2, ws13, ws2, K, eps=1e-5,
 
 
 def moe_backward(x, w_router, w13, w2, ws13, ws2, dout, K, pad_mask=None, idx=None, w=None,
-                 want=("dx", "dw_router", "dw13", "dw2", "dws13", "dws2")):
+                 want=("dx", "dw_router", "dw13", "dw2", "dws13", "dws2"), magnitudes=False):
     """Gradients of L = sum over real rows of dout . out (moe_oracle.c,
     orc_moe_backward), with the routes held fixed. dout has x's shape and
     dtype. idx/w ([T,K]) replace the router's choice when given. Returns
     the requested fp64 arrays: dx [T,H] (NaN rows for padding), dw_router
-    [E,H], dw13 [E,2I,H], dw2 [E,H,I], dws13 [2Is,H], dws2 [H,Is]."""
+    [E,H], dw13 [E,2I,H], dw2 [E,H,I], dws13 [2Is,H], dws2 [H,Is]; with
+    magnitudes=True also "m_<name>": per element the sum of the absolute
+    values of the terms summed into it."""
     lib = _load()
     x = np.ascontiguousarray(x)
     dt = _dtype_of(x)
@@ -243,8 +245,12 @@ def moe_backward(x, w_router, w13, w2, ws13, ws2, dout, K, pad_mask=None, idx=No
               "dws13": (2 * Is, H), "dws2": (H, Is)}
     outs = {k: (np.full(v, np.nan) if k == "dx" else np.zeros(v)) if k in want else None
             for k, v in shapes.items()}
+    mags = {k: (np.full(v, np.nan) if k == "dx" else np.zeros(v))
+            if (magnitudes and k in want) else None for k, v in shapes.items()}
+    names = ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2")
     lib.orc_moe_backward(_ptr(x), dt, _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(ws13),
                          _ptr(ws2), _ptr(pad), _ptr(dout), T, H, E, K, I, Is, _ptr(idx),
-                         _ptr(w), _ptr(outs["dx"]), _ptr(outs["dw_router"]), _ptr(outs["dw13"]),
-                         _ptr(outs["dw2"]), _ptr(outs["dws13"]), _ptr(outs["dws2"]))
-    return {k: v for k, v in outs.items() if v is not None}
+                         _ptr(w), *[_ptr(outs[k]) for k in names], *[_ptr(mags[k]) for k in names])
+    res = {k: v for k, v in outs.items() if v is not None}
+    res.update({"m_" + k: v for k, v in mags.items() if v is not None})
+    return res

@@ -436,12 +436,19 @@ void orc_rmsnorm(const void *x, int dtype, const void *weight, double eps,
  * the router's). Weight gradients are summed over tokens in ascending t
  * (single-threaded, deterministic); padding rows contribute nothing and
  * their dx rows are not written. Any output pointer may be NULL.
+ * The m* outputs (each may be NULL) hold, per element of the matching
+ * gradient, the sum of the absolute values of the terms that the gradient
+ * sums (|dy| |h| for dW2, |[du; dg]| |x| for dW13, |W13| |[du; dg]| +
+ * |Wr| |dl| for dx, |dl| |x| for dWr): the scale that the rounding error of
+ * a computation from rounded terms is bounded by.
  */
 void orc_moe_backward(const void *x, int dtype, const float *w_router, const void *w13,
                       const void *w2, const void *ws13, const void *ws2, const uint8_t *pad,
                       const void *dout, int64_t T, int64_t H, int E, int K, int64_t I,
                       int64_t Is, const int32_t *idx_in, const double *w_in, double *dx,
-                      double *dwr, double *dw13, double *dw2, double *dws13, double *dws2)
+                      double *dwr, double *dw13, double *dw2, double *dws13, double *dws2,
+                      double *mdx, double *mdwr, double *mdw13, double *mdw2, double *mdws13,
+                      double *mdws2)
 {
     int64_t Imax = I > Is ? I : Is;
     double *xr = malloc(sizeof(double) * (size_t)H);
@@ -453,11 +460,13 @@ void orc_moe_backward(const void *x, int dtype, const float *w_router, const voi
     double *hb = malloc(sizeof(double) * (size_t)Imax);
     double *du = malloc(sizeof(double) * (size_t)Imax);
     double *dg = malloc(sizeof(double) * (size_t)Imax);
-    if (dwr) memset(dwr, 0, sizeof(double) * (size_t)E * (size_t)H);
-    if (dw13) memset(dw13, 0, sizeof(double) * (size_t)E * 2 * (size_t)I * (size_t)H);
-    if (dw2) memset(dw2, 0, sizeof(double) * (size_t)E * (size_t)H * (size_t)I);
-    if (dws13) memset(dws13, 0, sizeof(double) * 2 * (size_t)Is * (size_t)H);
-    if (dws2) memset(dws2, 0, sizeof(double) * (size_t)H * (size_t)Is);
+    double *mxr = malloc(sizeof(double) * (size_t)H);
+    double *gs[12] = {dwr, dw13, dw2, dws13, dws2, NULL, mdwr, mdw13, mdw2, mdws13, mdws2, NULL};
+    size_t gn[6] = {(size_t)E * (size_t)H, (size_t)E * 2 * (size_t)I * (size_t)H,
+                    (size_t)E * (size_t)H * (size_t)I, 2 * (size_t)Is * (size_t)H,
+                    (size_t)H * (size_t)Is, 0};
+    for (int q = 0; q < 12; q++)
+        if (gs[q]) memset(gs[q], 0, sizeof(double) * gn[q % 6]);
     for (int64_t t = 0; t < T; t++) {
         if (pad && pad[t])
             continue;
@@ -478,6 +487,7 @@ void orc_moe_backward(const void *x, int dtype, const float *w_router, const voi
             xr[h] = elem(x, dtype, t * H + h);
             dv[h] = elem(dout, dtype, t * H + h);
             dxr[h] = 0.0;
+            mxr[h] = 0.0;
         }
         /* routed experts (k >= 0, weight w[k]) and the shared expert (k = K, weight 1) */
         for (int k = 0; k <= K; k++) {
@@ -488,6 +498,8 @@ void orc_moe_backward(const void *x, int dtype, const float *w_router, const voi
             const void *W2 = shared ? ws2 : offset_elems(w2, dtype, (size_t)e * expert_down_elems(H, I));
             double *gW13 = shared ? dws13 : (dw13 ? dw13 + (size_t)e * 2 * (size_t)I * (size_t)H : NULL);
             double *gW2 = shared ? dws2 : (dw2 ? dw2 + (size_t)e * (size_t)H * (size_t)I : NULL);
+            double *mW13 = shared ? mdws13 : (mdw13 ? mdw13 + (size_t)e * 2 * (size_t)I * (size_t)H : NULL);
+            double *mW2 = shared ? mdws2 : (mdw2 ? mdw2 + (size_t)e * (size_t)H * (size_t)I : NULL);
             const double wk = shared ? 1.0 : w[k];
             for (int64_t i = 0; i < II; i++) {
                 double uu = 0.0, gg = 0.0;
@@ -513,6 +525,10 @@ void orc_moe_backward(const void *x, int dtype, const float *w_router, const voi
                 for (int64_t j = 0; j < H; j++)
                     for (int64_t i = 0; i < II; i++)
                         gW2[j * II + i] += dy[j] * hb[i];
+            if (mW2)
+                for (int64_t j = 0; j < H; j++)
+                    for (int64_t i = 0; i < II; i++)
+                        mW2[j * II + i] += fabs(dy[j]) * fabs(hb[i]);
             for (int64_t i = 0; i < II; i++) {
                 double dh = 0.0;
                 for (int64_t j = 0; j < H; j++)
@@ -527,8 +543,14 @@ void orc_moe_backward(const void *x, int dtype, const float *w_router, const voi
                         gW13[i * H + h] += du[i] * xr[h];
                         gW13[(II + i) * H + h] += dg[i] * xr[h];
                     }
+                    if (mW13) {
+                        mW13[i * H + h] += fabs(du[i]) * fabs(xr[h]);
+                        mW13[(II + i) * H + h] += fabs(dg[i]) * fabs(xr[h]);
+                    }
                     dxr[h] += elem(W13, dtype, i * H + h) * du[i] +
                               elem(W13, dtype, (II + i) * H + h) * dg[i];
+                    mxr[h] += fabs(elem(W13, dtype, i * H + h) * du[i]) +
+                              fabs(elem(W13, dtype, (II + i) * H + h) * dg[i]);
                 }
         }
         /* router */
@@ -548,14 +570,18 @@ void orc_moe_backward(const void *x, int dtype, const float *w_router, const voi
             double dl = (double)pbuf[e] * (dp[e] - B);
             for (int64_t h = 0; h < H; h++) {
                 if (dwr) dwr[(int64_t)e * H + h] += dl * xr[h];
+                if (mdwr) mdwr[(int64_t)e * H + h] += fabs(dl * xr[h]);
                 dxr[h] += (double)w_router[(int64_t)e * H + h] * dl;
+                mxr[h] += fabs((double)w_router[(int64_t)e * H + h] * dl);
             }
         }
-        if (dx)
-            for (int64_t h = 0; h < H; h++)
-                dx[t * H + h] = dxr[h];
+        for (int64_t h = 0; h < H; h++) {
+            if (dx) dx[t * H + h] = dxr[h];
+            if (mdx) mdx[t * H + h] = mxr[h];
+        }
     }
     free(xr); free(dv); free(dxr); free(dy); free(u); free(g); free(hb); free(du); free(dg);
+    free(mxr);
 }
 
 void orc_round_bf16_array(const double *v, int64_t n, uint16_t *out)

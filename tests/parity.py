@@ -131,6 +131,43 @@ def check_output(gpu_rows, exact_rows, dtype, what=""):
     return err / rms
 
 
+def check_grad(gpu, exact, mag, dtype, what=""):
+    """Gradient rule (the backward's outputs): fp32 layers as the forward
+    (max |err| <= 1e-5 RMS). bf16 layers, every element:
+        |err| <= ulp(exact) + 2^-8 * mag
+    where mag is the sum of the absolute values of the terms the oracle sums
+    into that element: each term reaches the GPU through at most two bf16
+    roundings of relative size <= 2^-9 (an MFMA operand and its producer)
+    and fp32 sums, and the result is rounded once more (<= 1 ulp of the
+    exact value, allowing for a binade change). Plus, for the whole tensor,
+    RMS error <= 5e-3 RMS: the roundings are unbiased, so a systematic
+    mistake (a missing or doubled row) shows there even where the per-element
+    worst case is wide. Differences below 2^-16 of the tensor's largest
+    magnitude are not resolved: the oracle's router values are fp32, and its
+    evaluation of the softmax chain leaves residues of that order where the
+    exact derivative is zero (the logits of unselected experts).
+    Returns max |err| / RMS."""
+    g = as_f64(gpu)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    if g.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(exact ** 2)))
+    diff = np.abs(g - exact)
+    err = float(diff.max())
+    if dtype == wk.F32:
+        tol = OUT_TOL[dtype] * rms
+        assert err <= tol, f"{what}: max err {err:.4g} > {tol:.4g} (1e-5 * RMS {rms:.4g})"
+    else:
+        bound = bf16_ulp(exact) + 2.0 ** -8 * mag + 2.0 ** -16 * float(np.max(mag))
+        bad = np.argwhere(diff > bound)
+        assert bad.size == 0, (f"{what}: {len(bad)} elements outside ulp + 2^-8 * sum|terms|; "
+                               f"first {bad[:3].tolist()}, worst err / bound "
+                               f"{float((diff / bound).max()):.3f}")
+        erms = float(np.sqrt(np.mean(diff ** 2)))
+        assert erms <= 5e-3 * rms, f"{what}: RMS error {erms / rms:.4g} * RMS"
+    return err / max(rms, 1e-300)
+
+
 def oracle_rows(d, K, rows, idx, w, pad=None):
     """The oracle's layer output at `rows` using the given routes for them."""
     r = oracle.moe(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"], K=K,

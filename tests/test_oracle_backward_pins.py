@@ -159,3 +159,22 @@ def test_backward_unselected_and_padding():
     for k in gc:
         a = g[k][real] if k == "dx" else g[k]
         assert np.array_equal(a, gc[k]), k
+
+
+def test_backward_term_magnitudes():
+    # the magnitudes bound the gradients (triangle inequality); with one
+    # token every expert-weight gradient element is a single term, so the
+    # magnitude equals the gradient's absolute value
+    K = 2
+    d = _case(wk.F32, T=9, seed=11)
+    g = oracle.moe_backward(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
+                            d["dout"], K, magnitudes=True)
+    for k in ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2"):
+        assert np.all(g["m_" + k] >= np.abs(g[k]) * (1 - 1e-12)), k
+        assert np.array_equal(g[k], oracle.moe_backward(
+            d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"], d["dout"], K)[k])
+    d1 = _case(wk.F32, T=1, seed=12)
+    g1 = oracle.moe_backward(d1["x"], d1["w_router"], d1["w13"], d1["w2"], d1["ws13"],
+                             d1["ws2"], d1["dout"], K, magnitudes=True)
+    for k in ("dw13", "dw2", "dws13", "dws2"):
+        assert np.allclose(g1["m_" + k], np.abs(g1[k]), rtol=1e-12, atol=0), k
