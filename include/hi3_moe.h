@@ -75,6 +75,8 @@ extern "C" {
 
 /* Number of timed stages of hi3_moe_forward_instrumented. */
 #define HI3_NUM_STAGES 6
+/* Number of timed stages of hi3_moe_backward_instrumented. */
+#define HI3_NUM_BWD_STAGES 11
 
 /*
  * Workspace bytes that hi3_moe_forward and hi3_moe_forward_norm_residual
@@ -212,6 +214,69 @@ int hi3_moe_forward_norm_residual(const void *h, const void *norm_weight, float 
                                   int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
                                   void *workspace, size_t workspace_bytes,
                                   void *hip_stream);
+
+/*
+ * Backward pass of the layer, for fine-tuning (HunyuanImage-3.0
+ * model-coverage page, "Train": LoRA and full fine-tuning of the MoE
+ * decoder). Given dout = dL/dout for the rows of hi3_moe_forward, computes
+ * the gradients of L = sum over real rows t of dout[t] . out[t] with the
+ * routes held fixed (the top-k choice is piecewise constant; the router gets
+ * its gradient through the renormalised weights), at the values the forward
+ * keeps: fp32 router probabilities and weights, fp32 u and g, h rounded to
+ * dtype. Per real row, with w_k, e_k the k-th weight and expert:
+ *   dy_k = w_k dout, dh_k = W2[e_k]^T dy_k, du = dh SiLU(g),
+ *   dg = dh u SiLU'(g); the shared expert the same with weight 1;
+ *   a_k = dh_k . h_k, dl_k = a_k - w_k sum_j a_j (the logit gradient; zero
+ *   at unselected experts);
+ *   dx = sum_k W13[e_k]^T [du; dg]_k + W13s^T [du; dg]_s + sum_k dl_k W_r[e_k]
+ *   dW2[e] = sum dy h^T, dW13[e] = sum [du; dg] x^T over e's rows,
+ *   dW_r[e] = sum dl x over e's rows; shared weights over all real rows.
+ * The routes and the [up; gate] projection are recomputed inside the call.
+ * Arguments as in hi3_moe_forward, plus:
+ *   dout             [T, H] dtype.
+ *   dx               [T, H] dtype out or NULL; padding rows are not written.
+ *   dw_router        [E, H] fp32 out or NULL.
+ *   dw_up_gate       [E, 2*I, H] dtype out or NULL ([up; gate] rows).
+ *   dw_down          [E, H, I] dtype out or NULL.
+ *   dw_shared_up_gate [2*I_shared, H] dtype out or NULL.
+ *   dw_shared_down   [H, I_shared] dtype out or NULL.
+ *   workspace        at least hi3_moe_backward_workspace_size(...) bytes.
+ * A NULL output is not computed. Weight gradients are overwritten (not
+ * accumulated); those of experts that no row selects are zero; sums are
+ * accumulated in fp32 in a fixed order and rounded once (deterministic).
+ * T = 0 zero-fills the requested weight gradients; x, dout and the weights
+ * are then not read and may be NULL, and no workspace is needed.
+ */
+size_t hi3_moe_backward_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K,
+                                       int32_t I, int32_t I_shared, int32_t dtype);
+
+int hi3_moe_backward(const void *x, const float *w_router, const void *w_up_gate,
+                     const void *w_down, const void *w_shared_up_gate,
+                     const void *w_shared_down, const uint8_t *pad_mask, const void *dout,
+                     int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                     int32_t I_shared, int32_t dtype, void *dx, float *dw_router,
+                     void *dw_up_gate, void *dw_down, void *dw_shared_up_gate,
+                     void *dw_shared_down, void *workspace, size_t workspace_bytes,
+                     void *hip_stream);
+
+/*
+ * hi3_moe_backward with per-stage timing: HI3_NUM_BWD_STAGES + 1 events,
+ * recorded as in hi3_moe_forward_instrumented (names:
+ * hi3_moe_backward_stage_name). stage_events must not be NULL.
+ */
+int hi3_moe_backward_instrumented(const void *x, const float *w_router,
+                                  const void *w_up_gate, const void *w_down,
+                                  const void *w_shared_up_gate, const void *w_shared_down,
+                                  const uint8_t *pad_mask, const void *dout, int64_t T,
+                                  int32_t H, int32_t E, int32_t K, int32_t I,
+                                  int32_t I_shared, int32_t dtype, void *dx,
+                                  float *dw_router, void *dw_up_gate, void *dw_down,
+                                  void *dw_shared_up_gate, void *dw_shared_down,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *hip_stream, void *const *stage_events);
+
+/* Static name of backward stage i (0 <= i < HI3_NUM_BWD_STAGES), else "?". */
+const char *hi3_moe_backward_stage_name(int stage);
 
 /* Static name of timed stage i (0 <= i < HI3_NUM_STAGES), else "?". */
 const char *hi3_moe_stage_name(int stage);

@@ -24,6 +24,7 @@ HI3_E_UNSUPPORTED = -3
 HI3_E_WORKSPACE = -4
 HI3_E_HIP = -5
 HI3_NUM_STAGES = 6
+HI3_NUM_BWD_STAGES = 11
 
 EXPORTED = (
     "hi3_moe_workspace_size",
@@ -33,6 +34,10 @@ EXPORTED = (
     "hi3_moe_forward_instrumented",
     "hi3_moe_rmsnorm",
     "hi3_moe_forward_norm_residual",
+    "hi3_moe_backward_workspace_size",
+    "hi3_moe_backward",
+    "hi3_moe_backward_instrumented",
+    "hi3_moe_backward_stage_name",
     "hi3_moe_stage_name",
     "hi3_moe_status_string",
 )
@@ -67,6 +72,15 @@ def _load():
     lib.hi3_moe_rmsnorm.restype = ctypes.c_int
     lib.hi3_moe_forward_norm_residual.argtypes = [P, P, f32] + fwd[1:]
     lib.hi3_moe_forward_norm_residual.restype = ctypes.c_int
+    lib.hi3_moe_backward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.hi3_moe_backward_workspace_size.restype = sz
+    bwd = [P, P, P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
+    lib.hi3_moe_backward.argtypes = bwd
+    lib.hi3_moe_backward.restype = ctypes.c_int
+    lib.hi3_moe_backward_instrumented.argtypes = bwd + [P]
+    lib.hi3_moe_backward_instrumented.restype = ctypes.c_int
+    lib.hi3_moe_backward_stage_name.argtypes = [ctypes.c_int]
+    lib.hi3_moe_backward_stage_name.restype = ctypes.c_char_p
     lib.hi3_moe_stage_name.argtypes = [ctypes.c_int]
     lib.hi3_moe_stage_name.restype = ctypes.c_char_p
     lib.hi3_moe_status_string.argtypes = [ctypes.c_int]
@@ -184,6 +198,49 @@ def hi3_moe_forward_norm_residual(h, norm_weight, eps, w_router, w_up_gate, w_do
                                              *args[1:]))
 
 
+def hi3_moe_backward_workspace_size(T, H, E, K, I, I_shared, dtype) -> int:
+    return int(lib.hi3_moe_backward_workspace_size(T, H, E, K, I, I_shared, dtype))
+
+
+def _backward_args(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                   dout, K, dx, dw_router, dw_up_gate, dw_down, dw_shared_up_gate,
+                   dw_shared_down, workspace, stream):
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = w_up_gate.shape[1] // 2
+    Is = w_shared_up_gate.shape[0] // 2
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (_ptr(x), _ptr(w_router), _ptr(w_up_gate), _ptr(w_down), _ptr(w_shared_up_gate),
+            _ptr(w_shared_down), _ptr(pad_mask), _ptr(dout), T, H, E, K, I, Is,
+            dtype_code(x.dtype), _ptr(dx), _ptr(dw_router), _ptr(dw_up_gate), _ptr(dw_down),
+            _ptr(dw_shared_up_gate), _ptr(dw_shared_down), _ptr(workspace), ws_bytes,
+            _stream(stream))
+
+
+def hi3_moe_backward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                     pad_mask, dout, K, dx, dw_router, dw_up_gate, dw_down, dw_shared_up_gate,
+                     dw_shared_down, workspace, stream=None):
+    _check(lib.hi3_moe_backward(*_backward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, dout, K, dx,
+        dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down, workspace, stream)))
+
+
+def hi3_moe_backward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_gate,
+                                  w_shared_down, pad_mask, dout, K, dx, dw_router, dw_up_gate,
+                                  dw_down, dw_shared_up_gate, dw_shared_down, workspace,
+                                  stage_events, stream=None):
+    """stage_events: sequence of HI3_NUM_BWD_STAGES + 1 raw hipEvent_t handles."""
+    arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
+    _check(lib.hi3_moe_backward_instrumented(*_backward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, dout, K, dx,
+        dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down, workspace, stream),
+        arr))
+
+
+def hi3_moe_backward_stage_name(i) -> str:
+    return lib.hi3_moe_backward_stage_name(i).decode()
+
+
 def hi3_moe_stage_name(i) -> str:
     return lib.hi3_moe_stage_name(i).decode()
 
@@ -245,3 +302,30 @@ def moe_forward_norm_residual(h, norm_weight, w_router, w_up_gate, w_down, w_sha
     if return_routes:
         return out, idx, w, counts
     return out
+
+
+def moe_backward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, dout, K,
+                 pad_mask=None, workspace=None,
+                 want=("dx", "dw_router", "dw_up_gate", "dw_down", "dw_shared_up_gate",
+                       "dw_shared_down")):
+    """Allocates the requested gradients and the workspace with torch, then
+    calls hi3_moe_backward. Returns a dict of the requested gradients
+    (padding rows of dx are zero)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = w_up_gate.shape[1] // 2
+    Is = w_shared_up_gate.shape[0] // 2
+    dev, dt = x.device, x.dtype
+    shapes = {"dx": ((T, H), dt), "dw_router": ((E, H), torch.float32),
+              "dw_up_gate": ((E, 2 * I, H), dt), "dw_down": ((E, H, I), dt),
+              "dw_shared_up_gate": ((2 * Is, H), dt), "dw_shared_down": ((H, Is), dt)}
+    outs = {k: (torch.zeros(sh, dtype=d, device=dev) if k == "dx" else
+                torch.empty(sh, dtype=d, device=dev)) if k in want else None
+            for k, (sh, d) in shapes.items()}
+    if workspace is None:
+        n = hi3_moe_backward_workspace_size(T, H, E, K, I, Is, dtype_code(dt))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    hi3_moe_backward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                     dout, K, outs["dx"], outs["dw_router"], outs["dw_up_gate"], outs["dw_down"],
+                     outs["dw_shared_up_gate"], outs["dw_shared_down"], workspace)
+    return {k: v for k, v in outs.items() if v is not None}

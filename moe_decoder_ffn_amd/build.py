@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhi3moe.so")
-SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "combine.hip", "norm.hip", "hi3_moe.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "combine.hip", "norm.hip", "backward.hip",
+           "hi3_moe.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

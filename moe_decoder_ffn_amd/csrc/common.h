@@ -169,12 +169,33 @@ struct Plan {
   size_t hs;      // [T, Is] dtype: SwiGLU activations of the shared expert
   size_t y;       // [T*K, H] fp32: routed expert outputs by slot
   size_t ys;      // [T, H] fp32: shared expert outputs by real-row index
+  // backward only (the forward's y / ys hold dx by slot / by real row)
+  size_t ug;      // [T*K, 2I] fp32: u and g of the routed rows
+  size_t ugs;     // [T, 2Is] fp32: u and g of the shared expert
+  size_t xs;      // [T*K, H] dtype: x by slot
+  size_t dys;     // [T*K, H] dtype: w * dout by slot
+  size_t xv;      // [T, H] dtype: x by real-row index (padding only)
+  size_t doutv;   // [T, H] dtype: dout by real-row index (padding only)
+  size_t dd;      // [T*K, 2I] dtype: [du; dg] of the routed rows
+  size_t dds;     // [T, 2Is] dtype: [du; dg] of the shared expert
+  size_t apart;   // [T*K, P] fp32: partial sums of dh * h
+  size_t dls;     // [T*K] fp32: logit gradient by slot
+  size_t wslot;   // [T*K] fp32: routing weight by slot
+  size_t zrow;    // 512 bytes of zeros
+  int P;
   size_t total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) {
+// Partial sums of dh * h per routed row written by the mode-2 GEMM.
+inline int apart_cols(int I, int dtype) {
+  return dtype == kBF16 ? (I + kGemmBN - 1) / kGemmBN * kGemmWN : (I + kGemmF32BN - 1) / kGemmF32BN;
+}
+
+
+inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
+                      bool backward = false) {
   Plan p{};
   p.T = T; p.H = H; p.E = E; p.K = K; p.I = I; p.Is = Is; p.dtype = dtype;
   p.NB = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
@@ -215,6 +236,21 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype) 
     p.hs = take(T * Is * es);
     p.y = take(TK * H * 4);
     p.ys = take(T * H * 4);
+  }
+  if (backward && I > 0) {
+    p.P = apart_cols(I, dtype);
+    p.ug = take(TK * 2 * I * 4);
+    p.ugs = take(T * 2 * Is * 4);
+    p.xs = take(TK * H * es);
+    p.dys = take(TK * H * es);
+    p.xv = take(T * H * es);
+    p.doutv = take(T * H * es);
+    p.dd = take(TK * 2 * I * es);
+    p.dds = take(T * 2 * Is * es);
+    p.apart = take(TK * p.P * 4);
+    p.dls = take(TK * 4);
+    p.wslot = take(TK * 4);
+    p.zrow = take(512);
   }
   p.total = o;
   return p;
@@ -263,17 +299,33 @@ struct ScatterArgs {
 };
 
 // One class of grouped-GEMM problems: the E routed experts (class 0) or the
-// shared expert (class 1).
+// shared expert (class 1). Modes (gemm.hip):
+//   0 [up; gate] + SwiGLU, 1 down projection: A [rows, Kd] and B [N, Kd],
+//     both k-contiguous;
+//   2 gradient through the down projection (dh = W2^T dy, SwiGLU backward in
+//     the epilogue), 3 gradient through [up; gate] (dx = W13^T [du; dg]):
+//     A k-contiguous, B k-major ([Kd, N], row stride ldb);
+//   4 weight gradients C[m, n] = sum_k A[k, m] B[k, n] over the group's rows:
+//     A k-major ([rows, M], row stride lda), B k-major ([rows, N], ldb).
 struct GemmClass {
-  const void *A;        // rows of the left operand, row stride lda elements
+  const void *A;        // left operand, row stride lda elements
   int64_t lda;
-  const int32_t *arow;  // nullable: row map (tile row index -> A row)
-  const void *B;        // [N, Kd] per group, row-major (weights [out, in])
+  const int32_t *arow;  // nullable: row map (tile row index -> A row), modes 0-3
+  const void *B;        // per group: [N, Kd] (modes 0, 1) or [Kd, N] (2, 3), row-major
   int64_t strideB;      // elements between consecutive experts' B
   void *C;              // output rows, row stride ldc elements
   int64_t ldc;
   int N;                // projection outputs (2*I for [up; gate], H for down)
-  int Kd;               // reduction length
+  int Kd;               // reduction length (modes 0-3)
+  int64_t ldb;          // B row stride, k-major B (modes 2-4)
+  int M;                // mode 4: output rows (A columns)
+  int64_t strideC;      // mode 4: elements between consecutive experts' C
+  float *ug;            // mode 0: when set, u and g are also stored here (fp32,
+                        // [rows, N] with u in the first N/2 columns); mode 2: read
+  const void *hsave;    // mode 2: SwiGLU activations [rows, N] (layer dtype)
+  float *apart;         // mode 2 (nullable): per-row partial sums of dh * h
+  int apart_ld;         // partial sums per row
+  const float *rowscale;  // mode 2 (nullable): dh = rowscale[row] * (B^T A row)
 };
 
 struct GemmArgs {
@@ -284,6 +336,14 @@ struct GemmArgs {
   int NTn;    // column tiles of the widest class
   int split;     // blocks per listed row tile; set by the launcher
   int sub_rows;  // rows per block when split > 1 (block p takes rows [p sub_rows, ...))
+  // mode 4: group g < E reduces over rows [goff[g], goff[g] + gcnt[g]) of A
+  // and B; the shared group over rows [0, *nreal). Rows past the group's end
+  // are read from zrow (zeros, at least 512 bytes).
+  const int32_t *goff;
+  const int32_t *gcnt;
+  const int32_t *nreal;
+  const void *zrow;
+  int wg_shared_blocks;  // set by the launcher
 };
 
 struct CombineArgs {
@@ -325,5 +385,52 @@ hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int tile_rows, i
 hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
                             hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+
+hipError_t launch_gemm_dgrad_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
+                                  hipStream_t s);
+hipError_t launch_gemm_dgrad_up_gate(const GemmArgs &a, int max_tiles, int tile_rows,
+                                     int dtype, hipStream_t s);
+hipError_t launch_gemm_wgrad(const GemmArgs &a, int E, int dtype, hipStream_t s);
+
+struct BwdGatherArgs {
+  const void *x;
+  const void *dout;
+  const float *wts;
+  const int32_t *slotof;
+  const int32_t *vidx;
+  const uint8_t *pad;
+  int64_t T;
+  int H, K;
+  void *xs;     // [T*K, H]: x by slot
+  void *dys;    // [T*K, H]: w * dout by slot
+  float *wslot; // [T*K]: w by slot
+  void *xv;     // nullable, [T, H]: x by real-row index
+  void *doutv;  // nullable, [T, H]: dout by real-row index
+};
+hipError_t launch_bwd_gather(const BwdGatherArgs &a, int dtype, hipStream_t s);
+
+struct BwdCombineArgs {
+  const float *dxs;      // [T*K, H] by slot
+  const float *dxsh;     // [T, H] by real-row index
+  const float *apart;    // [T*K, P]
+  int P;
+  const int32_t *slotof;
+  const int32_t *idx;
+  const int32_t *vidx;
+  const float *wts;
+  const float *w_router;  // [E, H]
+  const uint8_t *pad;
+  int64_t T;
+  int H, K;
+  float *dls;            // [T*K] logit gradient by slot
+  void *dx;              // nullable
+};
+hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);
+
+hipError_t launch_dw_router(const float *dls, const void *xs, const int32_t *eoff, int E, int H,
+                            int dtype, float *dwr, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 }  // namespace hi3

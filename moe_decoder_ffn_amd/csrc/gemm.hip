@@ -7,8 +7,21 @@
 //   h is stored in the layer dtype.
 //   down projection: y = W2 h with W2 [H, I] (down_proj), y stored in fp32.
 //
-// Both operands are k-contiguous (activations [rows, k], weights [out, in]),
-// so every MFMA operand fragment is one 16-byte LDS read.
+// Backward (the gradient of sum(dout . out) with the routes held fixed; the
+// pages' fine-tuning, HunyuanImage-3.0 model-coverage page, "Train"):
+//   mode 2: dh = w W2^T dout per routed row (w applied in fp32), and in the epilogue
+//       du = dh SiLU(g), dg = dh u SiLU'(g) from the stored u, g, plus the
+//       partial sums of dh . h that give the router's gradient;
+//   mode 3: dx = W13^T [du; dg] per row, fp32;
+//   mode 4: weight gradients dW2 = sum dy h^T, dW13 = sum [du; dg] x^T over
+//       each expert's rows, in the layer dtype.
+//
+// Forward operands are k-contiguous (activations [rows, k], weights
+// [out, in]): every MFMA operand fragment is one 16-byte LDS read. The
+// backward's weights in modes 2 and 3, and both operands of mode 4, are
+// k-major (row k holds the n or m values): they are copied to LDS as stored
+// and their fragments are read with the transposing LDS read of gfx950, so no
+// transposed copy is ever written to HBM.
 //
 // Work list: the row tiles of all groups (written on the device by the scan
 // kernel, expert-major, the shared expert last) times the column tiles; the
@@ -30,11 +43,13 @@
 namespace hi3 {
 
 struct TileJob {
-  int g;     // group: expert id, or E for the shared expert
-  int row0;  // first row of the tile in the group's row space
-  int rows;  // rows in the tile (<= BM)
-  int nt;    // column tile
-  int cls;   // 0 routed, 1 shared
+  int g;       // group: expert id, or E for the shared expert
+  int row0;    // first row of the tile in the group's row space (mode 4: first output row)
+  int rows;    // rows in the tile (<= BM)
+  int nt;      // column tile
+  int cls;     // 0 routed, 1 shared
+  int kstart;  // mode 4: first row of the group in A and B
+  int kcount;  // mode 4: the group's rows (the reduction length)
 };
 
 // ntile_cols(c): column tiles of class c.
@@ -72,6 +87,41 @@ __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   j.cls = tile.x == a.E ? 1 : 0;
   const GemmClass &c = j.cls ? a.cls[1] : a.cls[0];
   return nt < class_col_tiles<MODE, BN>(c);
+}
+
+// Mode 4: the shared group's output tiles come first (they reduce over every
+// real row, the longest jobs); then the routed experts, placed so that all
+// tiles of expert g run on XCD g % 8 (block b runs on XCD b % 8), where that
+// XCD's L2 serves the expert's rows to all of its tiles.
+template <int BM, int BN>
+__device__ __forceinline__ bool resolve_wgrad(const GemmArgs &a, TileJob &j) {
+  int b = blockIdx.x;
+  int cls, g, tt;
+  if (b < a.wg_shared_blocks) {
+    cls = 1;
+    g = a.E;
+    tt = b;
+  } else {
+    b -= a.wg_shared_blocks;
+    const GemmClass &c0 = a.cls[0];
+    const int tpe = ((c0.M + BM - 1) / BM) * ((c0.N + BN - 1) / BN);
+    const int li = b / 8;
+    cls = 0;
+    g = b % 8 + 8 * (li / tpe);
+    tt = li % tpe;
+    if (g >= a.E) return false;
+  }
+  const GemmClass &c = a.cls[cls];
+  const int NT = (c.N + BN - 1) / BN, MT = (c.M + BM - 1) / BM;
+  if (tt >= MT * NT) return false;
+  j.g = g;
+  j.cls = cls;
+  j.row0 = (tt / NT) * BM;
+  j.rows = min(BM, c.M - j.row0);
+  j.nt = tt % NT;
+  j.kstart = cls ? 0 : a.goff[g];
+  j.kcount = cls ? *a.nreal : a.gcnt[g];
+  return true;
 }
 
 // --------------------------------------------------------------- bf16 MFMA
@@ -120,6 +170,47 @@ struct LdsLayout {
   }
 };
 
+// LDS layout of a k-major operand stage: BK rows of k, W columns (2 W bytes
+// per row). 16-byte chunk c of row k is stored at chunk
+// ((c / 4) ^ (k % 4)) * 4 + c % 4: the same 64-byte column unit of four
+// consecutive k rows lands in the four distinct 64-byte windows of the
+// 256-byte bank cycle, which is what a transposing fragment read touches.
+template <int W>
+struct LdsKM {
+  static constexpr int CPR = W / 8;           // 16-byte chunks per row
+  static constexpr int RPC = 1024 / (W * 2);  // rows per 1 KiB copy instruction
+  static_assert(W == 128 || W == 256, "k-major tile width");
+  __device__ static __forceinline__ int pos(int k, int c) {
+    return k * CPR + (((c >> 2) ^ (k & 3)) << 2) + (c & 3);
+  }
+};
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// One MFMA operand fragment (lane l: k = 16 s + 8 (l / 32) + 0..7 of column
+// cb + l % 32) from a k-major stage, with two ds_read_b64_tr_b16. That read
+// works on groups of 16 lanes: lane i of a group receives element i % 4 of
+// the 8 bytes that lane 4 j + i / 4 addressed, as its element j. So lane q
+// of a group addresses row k0 + q / 4 at columns c0 + 4 (q % 4) .. + 3, and
+// receives rows k0 .. k0 + 3 of column c0 + q.
+template <int W>
+__device__ __forceinline__ bf16x8_t read_frag_km(const u32x4_t *stage, int s, int cb, int lane) {
+  using LK = LdsKM<W>;
+  const int q = lane & 15;
+  const int k0 = 16 * s + 8 * (lane >> 5) + (q >> 2);
+  const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+  const int c = col >> 3;
+  const char *base = reinterpret_cast<const char *>(stage) + (col & 4) * 2;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t *)(const_cast<char *>(base + LK::pos(k0, c) * 16)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t *)(const_cast<char *>(base + LK::pos(k0 + 4, c) * 16)));
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // Workgroup barrier without a memory fence: __syncthreads() would also wait
 // for every copy still in flight (the fence drains vmcnt), which would stop
 // later stages from overlapping. Each wave has already waited for its own
@@ -164,7 +255,9 @@ struct StageRing {
 // weight fragment first): result element v of lane l is token l % 32 and
 // weight column 8 (v / 4) + 4 (l / 32) + v % 4 of the 32 x 32 sub-tile, so
 // every lane holds runs of 4 adjacent output columns and stores them with
-// one 8-byte (bf16) or 16-byte (fp32) write.
+// one 8-byte (bf16) or 16-byte (fp32) write. Mode 4 has the same shape with
+// output rows m in place of tokens and output columns n in place of weight
+// rows.
 // The tile body: BM is the row capacity of this body (the LDS stages may be
 // larger); the stage arrays are the kernel's.
 template <int MODE, int BM, int BK, int NST, int WN>
@@ -173,31 +266,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
                                           u32x4_t *sA2, u32x4_t *sB2, u32x4_t *sA3,
                                           u32x4_t *sB3, u32x4_t *sA4, u32x4_t *sB4) {
   constexpr int BN = kGemmBN;
+  constexpr bool AT = MODE == 4;  // A stage k-major
+  constexpr bool BT = MODE >= 2;  // B stage k-major
   using L = LdsLayout<BK>;
   constexpr int NW = 2 * WN;                // waves: 2 along rows x WN along columns
-  constexpr int A_CP = BM / L::RPC / NW;    // copies per wave per stage
-  constexpr int B_CP = BN / L::RPC / NW;
+  constexpr int A_CP = BM * BK * 2 / 1024 / NW;  // copies per wave per stage
+  constexpr int B_CP = BN * BK * 2 / 1024 / NW;
   constexpr int CPW = A_CP + B_CP;
   constexpr int MI = BM / 64;               // 32-row sub-tiles per wave
   constexpr int NI = BN / WN / 32;          // 32-column sub-tiles per wave
   static_assert(BN == 256 && BM % 64 == 0 && BM <= 256 && (BK == 32 || BK == 64), "tile");
+  static_assert(!AT || (BM == 256 && BK == 64), "k-major A tile");
+  static_assert(!BT || BK == 64, "k-major B tile");
   static_assert(NST >= 2 && NST <= 5, "stages");
-  static_assert(BM % (L::RPC * NW) == 0 && BN % (L::RPC * NW) == 0,
-                "each wave copies a whole number of 1 KiB row groups");
+  static_assert(BM * BK * 2 % (1024 * NW) == 0 && BN * BK * 2 % (1024 * NW) == 0,
+                "each wave copies a whole number of 1 KiB blocks");
   static_assert(A_CP >= 1 && B_CP >= 1 && (NST - 2) * CPW < 64, "copy counts");
   static_assert(WN == 2 || WN == 4, "wave grid");
 
   const bool shared_cls = j.cls != 0;
-  const uint16_t *A = static_cast<const uint16_t *>(shared_cls ? a.cls[1].A : a.cls[0].A);
-  const int64_t lda = shared_cls ? a.cls[1].lda : a.cls[0].lda;
-  const int32_t *arow = shared_cls ? a.cls[1].arow : a.cls[0].arow;
-  const uint16_t *B = static_cast<const uint16_t *>(shared_cls ? a.cls[1].B : a.cls[0].B);
-  const int64_t strideB = shared_cls ? 0 : a.cls[0].strideB;
-  void *Cv = shared_cls ? a.cls[1].C : a.cls[0].C;
-  const int64_t ldc = shared_cls ? a.cls[1].ldc : a.cls[0].ldc;
-  const int N = shared_cls ? a.cls[1].N : a.cls[0].N;
-  const int Kd = shared_cls ? a.cls[1].Kd : a.cls[0].Kd;
-  B += static_cast<int64_t>(shared_cls ? 0 : j.g) * strideB;
+  const GemmClass &cl = shared_cls ? a.cls[1] : a.cls[0];
+  const uint16_t *A = static_cast<const uint16_t *>(cl.A);
+  const int64_t lda = cl.lda;
+  const int32_t *arow = cl.arow;
+  const uint16_t *B = static_cast<const uint16_t *>(cl.B);
+  const int64_t strideB = shared_cls ? 0 : cl.strideB;
+  void *Cv = cl.C;
+  const int64_t ldc = cl.ldc;
+  const int N = cl.N;
+  const int Kd = cl.Kd;
+  const int64_t ldb = cl.ldb;
+  if constexpr (!AT) B += static_cast<int64_t>(shared_cls ? 0 : j.g) * strideB;
 
   const int tid = threadIdx.x;
   const int wave = wave_uniform(tid >> 6);
@@ -205,17 +304,34 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   const int r = lane & 31, g = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
 
-  // Copy q of this wave covers tile rows (wave * CP + q) * RPC + [0, RPC);
-  // lane i takes row (wave * CP + q) * RPC + i / CPR and the logical chunk
-  // that the swizzle stores at position i % CPR.
-  int arow_src[A_CP];
+  // k-contiguous A: copy q of this wave covers tile rows
+  // (wave * CP + q) * RPC + [0, RPC); lane i takes row
+  // (wave * CP + q) * RPC + i / CPR and the logical chunk that the swizzle
+  // stores at position i % CPR.
+  int arow_src[AT ? 1 : A_CP];
+  if constexpr (!AT) {
 #pragma unroll
-  for (int q = 0; q < A_CP; ++q) {
-    const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
-    const int rr = min(row, j.rows - 1);  // tail rows reread a real row
-    const int ri = j.row0 + rr;
-    arow_src[q] = arow ? arow[ri] : ri;
+    for (int q = 0; q < A_CP; ++q) {
+      const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
+      const int rr = min(row, j.rows - 1);  // tail rows reread a real row
+      const int ri = j.row0 + rr;
+      arow_src[q] = arow ? arow[ri] : ri;
+    }
   }
+  // k-major stage of width W: copy ci covers k rows ci * RPC + [0, RPC);
+  // lane i takes row ci * RPC + i / CPR and the logical chunk stored at
+  // position i % CPR. Source row pointer for global k row kg: rowp(kg).
+  auto km_copy = [&](auto Wc, int ci, int col0, int cmax, u32x4_t *stage,
+                     auto rowp) __attribute__((always_inline)) {
+    constexpr int W = decltype(Wc)::value;
+    using LK = LdsKM<W>;
+    const int krow = ci * LK::RPC + lane / LK::CPR;
+    const int p = lane % LK::CPR;
+    const int c = (((p >> 2) ^ (krow & 3)) << 2) | (p & 3);
+    const int col = min(col0 + c * 8, cmax - 8);
+    lds_dma16(rowp(krow, col), stage + ci * 64);
+  };
+  const uint16_t *zrow = static_cast<const uint16_t *>(a.zrow) + 8 * (lane & 31);
   // Copies [q0, q1) of this wave (A copies first, then B) for k step kc.
   auto issue_range = [&](int kc, u32x4_t *la, u32x4_t *lb, auto Q0, auto Q1) __attribute__((always_inline)) {
     constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
@@ -223,26 +339,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 #pragma unroll
     for (int q = 0; q < A_CP; ++q) {
       if (q < q0 || q >= q1) continue;
-      const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
-      const int c = (lane % L::CPR) ^ L::swz(row);
-      lds_dma16(A + static_cast<int64_t>(arow_src[q]) * lda + ko + c * 8,
-                la + (wave * A_CP + q) * 64);
+      if constexpr (AT) {
+        km_copy(std::integral_constant<int, BM>{}, wave * A_CP + q, j.row0, cl.M, la,
+                [&](int krow, int col) {
+                  const int kg = ko + krow;
+                  return kg < j.kcount ? A + static_cast<int64_t>(j.kstart + kg) * lda + col
+                                       : zrow;
+                });
+      } else {
+        const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
+        const int c = (lane % L::CPR) ^ L::swz(row);
+        lds_dma16(A + static_cast<int64_t>(arow_src[q]) * lda + ko + c * 8,
+                  la + (wave * A_CP + q) * 64);
+      }
     }
 #pragma unroll
     for (int q = 0; q < B_CP; ++q) {
       if (A_CP + q < q0 || A_CP + q >= q1) continue;
-      const int row = (wave * B_CP + q) * L::RPC + lane / L::CPR;
-      const int c = (lane % L::CPR) ^ L::swz(row);
-      int brow;
-      if (MODE == 0) {
-        const int Ih = N / 2;
-        const int col = min(j.nt * (BN / 2) + (row & (BN / 2 - 1)), Ih - 1);
-        brow = row < BN / 2 ? col : Ih + col;
+      if constexpr (AT) {
+        km_copy(std::integral_constant<int, BN>{}, wave * B_CP + q, j.nt * BN, N, lb,
+                [&](int krow, int col) {
+                  const int kg = ko + krow;
+                  return kg < j.kcount ? B + static_cast<int64_t>(j.kstart + kg) * ldb + col
+                                       : zrow;
+                });
+      } else if constexpr (BT) {
+        km_copy(std::integral_constant<int, BN>{}, wave * B_CP + q, j.nt * BN, N, lb,
+                [&](int krow, int col) { return B + static_cast<int64_t>(ko + krow) * ldb + col; });
       } else {
-        brow = min(j.nt * BN + row, N - 1);
+        const int row = (wave * B_CP + q) * L::RPC + lane / L::CPR;
+        const int c = (lane % L::CPR) ^ L::swz(row);
+        int brow;
+        if (MODE == 0) {
+          const int Ih = N / 2;
+          const int col = min(j.nt * (BN / 2) + (row & (BN / 2 - 1)), Ih - 1);
+          brow = row < BN / 2 ? col : Ih + col;
+        } else {
+          brow = min(j.nt * BN + row, N - 1);
+        }
+        lds_dma16(B + static_cast<int64_t>(brow) * Kd + ko + c * 8,
+                  lb + (wave * B_CP + q) * 64);
       }
-      lds_dma16(B + static_cast<int64_t>(brow) * Kd + ko + c * 8,
-                lb + (wave * B_CP + q) * 64);
     }
   };
   auto issue = [&](int kc, u32x4_t *la, u32x4_t *lb) __attribute__((always_inline)) {
@@ -292,10 +429,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     // fragment read i (A fragments first, then B) of sub-step s into buffer buf
     auto read = [&](int buf, int s, int i) __attribute__((always_inline)) {
       const int ch = 2 * s + g;
-      if (i < MI)
-        af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
-      else
-        bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
+      if (i < MI) {
+        if constexpr (AT)
+          af[buf][i] = read_frag_km<BM>(la, s, wm * (BM / 2) + i * 32, lane);
+        else
+          af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
+      } else {
+        if constexpr (BT)
+          bf[buf][i - MI] = read_frag_km<BN>(lb, s, nrow[i - MI], lane);
+        else
+          bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
+      }
     };
 #pragma unroll
     for (int i = 0; i < NR; ++i) read(0, 0, i);
@@ -314,11 +458,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 #pragma unroll
           for (int i = i0; i < i1; ++i) read(cur ^ 1, s + 1, i);
           // MFMA, read, MFMA, read, ...
-#pragma unroll
-          for (int t = 0; t < (NI > i1 - i0 ? NI : i1 - i0); ++t) {
-            if (t < NI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (t < i1 - i0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
+          constexpr int NT_ = NI > i1 - i0 ? NI : i1 - i0;
+          static_for<NT_>([&](auto Tv) __attribute__((always_inline)) {
+            constexpr int t = decltype(Tv)::value;
+            if constexpr (t < NI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            // LDS read instructions of fragment read i0 + t (two if k-major)
+            constexpr int nrd = ((i0 + t) < MI ? AT : BT) ? 2 : 1;
+            if constexpr (t < i1 - i0) __builtin_amdgcn_sched_group_barrier(0x100, nrd, 0);
+          });
         }
         __builtin_amdgcn_sched_barrier(0);
         constexpr int q0 = (grp - 1) * PER < CPW ? (grp - 1) * PER : CPW;
@@ -358,7 +505,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     wait_vmem<0>();
   };
 
-  const int nk = Kd / BK;
+  const int nk = AT ? (j.kcount + BK - 1) / BK : Kd / BK;
   // One k step from stage S: start the copy NST - 1 steps ahead into the
   // stage read in the previous step, multiply, then wait for the next
   // step's copy (the copies of the steps after it may stay in flight) and
@@ -386,14 +533,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     if (kc + decltype(S)::value < nk) step(S, kc + decltype(S)::value);
   });
 
-  if (MODE == 0) {
+  if constexpr (MODE == 0) {
     const int Ih = N / 2;
     uint16_t *C = static_cast<uint16_t *>(Cv);
+    float *ug = cl.ug;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int row = wm * (BM / 2) + mi * 32 + r;
       if (row >= j.rows) continue;
-      uint16_t *crow = C + (static_cast<int64_t>(j.row0) + row) * ldc;
+      const int64_t grow = static_cast<int64_t>(j.row0) + row;
+      uint16_t *crow = C + grow * ldc;
 #pragma unroll
       for (int p = 0; p < NI / 2; ++p)
 #pragma unroll
@@ -412,9 +561,90 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
           o[0] = pack_bf16x2(hv[0], hv[1]);
           o[1] = pack_bf16x2(hv[2], hv[3]);
           *reinterpret_cast<u32x2_t *>(crow + col) = o;
+          if (ug) {
+            float *ur = ug + grow * N;
+            *reinterpret_cast<f32x4_t *>(ur + col) =
+                f32x4_t{acc[mi][p][4 * q], acc[mi][p][4 * q + 1], acc[mi][p][4 * q + 2],
+                        acc[mi][p][4 * q + 3]};
+            *reinterpret_cast<f32x4_t *>(ur + Ih + col) =
+                f32x4_t{acc[mi][p + NI / 2][4 * q], acc[mi][p + NI / 2][4 * q + 1],
+                        acc[mi][p + NI / 2][4 * q + 2], acc[mi][p + NI / 2][4 * q + 3]};
+          }
+        }
+    }
+  } else if constexpr (MODE == 2) {
+    // dh = rowscale * acc of (row, column) (the routing weight of the row:
+    // acc = W2^T dout); u and g as the forward computed them, h as it stored
+    // them. du = dh SiLU(g), dg = dh u SiLU'(g) with
+    // SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g)); [du; dg] is
+    // stored in the layer dtype (row stride 2N, du first). The sum of dh h
+    // over the wave's columns of each row goes to apart.
+    uint16_t *D = static_cast<uint16_t *>(Cv);
+    const float *ugp = cl.ug;
+    const uint16_t *hp = static_cast<const uint16_t *>(cl.hsave);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * (BM / 2) + mi * 32 + r;
+      const bool ok = row < j.rows;
+      const int64_t grow = static_cast<int64_t>(j.row0) + (ok ? row : 0);
+      float asum = 0.0f;
+      if (ok) {
+        const float rs = cl.rowscale ? cl.rowscale[grow] : 1.0f;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = j.nt * BN + wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
+            if (col >= N) continue;
+            const f32x4_t u4 = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + col);
+            const f32x4_t g4 = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + N + col);
+            const u32x2_t h2 = *reinterpret_cast<const u32x2_t *>(hp + grow * N + col);
+            float du[4], dg[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float dh = rs * acc[mi][ni][4 * q + e];
+              const float gt = g4[e];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+              du[e] = dh * (gt * sg);
+              dg[e] = dh * u4[e] * (sg * (1.0f + gt * (1.0f - sg)));
+              const uint32_t hw = h2[e >> 1];
+              const float hv = __uint_as_float((e & 1) ? (hw & 0xffff0000u) : (hw << 16));
+              asum += dh * hv;
+            }
+            u32x2_t o;
+            o[0] = pack_bf16x2(du[0], du[1]);
+            o[1] = pack_bf16x2(du[2], du[3]);
+            *reinterpret_cast<u32x2_t *>(D + grow * ldc + col) = o;
+            o[0] = pack_bf16x2(dg[0], dg[1]);
+            o[1] = pack_bf16x2(dg[2], dg[3]);
+            *reinterpret_cast<u32x2_t *>(D + grow * ldc + N + col) = o;
+          }
+      }
+      // lanes l and l ^ 32 hold the same row
+      asum += __shfl_xor(asum, 32, kWave);
+      if (cl.apart && ok && g == 0) cl.apart[grow * cl.apart_ld + j.nt * WN + wn] = asum;
+    }
+  } else if constexpr (MODE == 4) {
+    uint16_t *C = static_cast<uint16_t *>(Cv) + static_cast<int64_t>(j.g < a.E ? j.g : 0) * cl.strideC;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * (BM / 2) + mi * 32 + r;
+      if (row >= j.rows) continue;
+      uint16_t *crow = C + (static_cast<int64_t>(j.row0) + row) * ldc;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = j.nt * BN + wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
+          if (col >= N) continue;
+          u32x2_t o;
+          o[0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
+          o[1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+          *reinterpret_cast<u32x2_t *>(crow + col) = o;
         }
     }
   } else {
+    // modes 1 and 3: fp32 rows
     float *C = static_cast<float *>(Cv);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -440,12 +670,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 // the half-height body (half the MFMAs and A copies, the same B copies), one
 // with at most 3 BM / 4 rows the three-quarter body (when those heights are
 // multiples of 64). The bodies are straight-line code over the same LDS
-// ring.
+// ring. Mode 4 jobs are whole output tiles (one body).
 template <int MODE, int BM, int BK, int NST, int WN>
 __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int BN = kGemmBN;
-  using L = LdsLayout<BK>;
-  constexpr int AE = BM * L::CPR, BE = BN * L::CPR;
+  constexpr int AE = BM * BK / 8, BE = BN * BK / 8;  // 16-byte chunks per stage
   static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
   __shared__ u32x4_t sA0[AE], sB0[BE], sA1[AE], sB1[BE];
   __shared__ u32x4_t sA2[NST > 2 ? AE : 1], sB2[NST > 2 ? BE : 1];
@@ -453,57 +682,76 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ u32x4_t sA4[NST > 4 ? AE : 1], sB4[NST > 4 ? BE : 1];
 
   TileJob j;
-  if (!resolve_job<MODE, BN>(a, j)) return;
-  constexpr int BMS = BM / 2, BM3 = BM / 4 * 3;
-  if constexpr (BMS >= 64 && BMS % 64 == 0) {
-    if (j.rows <= BMS) {
-      gemm_tile<MODE, BMS, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
-      return;
+  if constexpr (MODE == 4) {
+    if (!resolve_wgrad<BM, BN>(a, j)) return;
+    gemm_tile<MODE, BM, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+  } else {
+    if (!resolve_job<MODE, BN>(a, j)) return;
+    constexpr int BMS = BM / 2, BM3 = BM / 4 * 3;
+    if constexpr (BMS >= 64 && BMS % 64 == 0) {
+      if (j.rows <= BMS) {
+        gemm_tile<MODE, BMS, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+        return;
+      }
     }
-  }
-  if constexpr (BM3 > BMS && BM3 % 64 == 0) {
-    if (j.rows <= BM3) {
-      gemm_tile<MODE, BM3, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
-      return;
+    if constexpr (BM3 > BMS && BM3 % 64 == 0) {
+      if (j.rows <= BM3) {
+        gemm_tile<MODE, BM3, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+        return;
+      }
     }
+    gemm_tile<MODE, BM, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
   }
-  gemm_tile<MODE, BM, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
 }
 
 // --------------------------------------------------------------- fp32
 
-// fp32 layers: LDS-tiled FMA, 64 rows x 64 weight rows per block ([up; gate]:
+// fp32 layers: LDS-tiled FMA, 64 rows x 64 columns per block ([up; gate]:
 // 32 up + the matching 32 gate rows), k step 16; thread (ty, tx) owns rows
-// 4ty..4ty+3 and four weight columns.
+// 4ty..4ty+3 and four columns. Operands are staged k-major in LDS whatever
+// their layout in memory.
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BM = kGemmF32BM, BN = kGemmF32BN, BK = 16;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
+  __shared__ float red[BM][17];
   TileJob j;
-  if (!resolve_job<MODE, BN>(a, j)) return;
+  if constexpr (MODE == 4) {
+    if (!resolve_wgrad<BM, BN>(a, j)) return;
+  } else {
+    if (!resolve_job<MODE, BN>(a, j)) return;
+  }
   const bool shared_cls = j.cls != 0;
   const GemmClass &c = shared_cls ? a.cls[1] : a.cls[0];
   const float *A = static_cast<const float *>(c.A);
-  const float *B = static_cast<const float *>(c.B) +
-                   static_cast<int64_t>(shared_cls ? 0 : j.g) * c.strideB;
-  const int N = c.N, Kd = c.Kd;
+  const float *B = static_cast<const float *>(c.B);
+  if (MODE != 4) B += static_cast<int64_t>(shared_cls ? 0 : j.g) * c.strideB;
+  const int N = c.N;
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
 
+  // k-contiguous operands: thread loads 4 consecutive k of row lrow;
+  // k-major operands: 4 consecutive columns (lcol) of k row lkk
   const int lrow = tid >> 2, lk = (tid & 3) * 4;
-  const int arr = min(lrow, j.rows - 1);
-  const int64_t ari = static_cast<int64_t>(j.row0) + arr;
-  const float *aptr = A + (c.arow ? static_cast<int64_t>(c.arow[ari]) : ari) * c.lda + lk;
-  int brow;
-  if (MODE == 0) {
-    const int Ih = N / 2;
-    const int col = min(j.nt * (BN / 2) + (lrow & (BN / 2 - 1)), Ih - 1);
-    brow = lrow < BN / 2 ? col : Ih + col;
-  } else {
-    brow = min(j.nt * BN + lrow, N - 1);
+  const int lkk = tid >> 4, lcol = (tid & 15) * 4;
+  const float *aptr = nullptr, *bptr = nullptr;
+  if (MODE != 4) {
+    const int arr = min(lrow, j.rows - 1);
+    const int64_t ari = static_cast<int64_t>(j.row0) + arr;
+    aptr = A + (c.arow ? static_cast<int64_t>(c.arow[ari]) : ari) * c.lda + lk;
   }
-  const float *bptr = B + static_cast<int64_t>(brow) * Kd + lk;
+  if (MODE <= 1) {
+    int brow;
+    if (MODE == 0) {
+      const int Ih = N / 2;
+      const int col = min(j.nt * (BN / 2) + (lrow & (BN / 2 - 1)), Ih - 1);
+      brow = lrow < BN / 2 ? col : Ih + col;
+    } else {
+      brow = min(j.nt * BN + lrow, N - 1);
+    }
+    bptr = B + static_cast<int64_t>(brow) * c.Kd + lk;
+  }
 
   int bcol[4];
 #pragma unroll
@@ -516,13 +764,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
 
-  for (int k0 = 0; k0 < Kd; k0 += BK) {
-    const f32x4_t av = *reinterpret_cast<const f32x4_t *>(aptr + k0);
-    const f32x4_t bv = *reinterpret_cast<const f32x4_t *>(bptr + k0);
+  const int klen = MODE == 4 ? j.kcount : c.Kd;
+  for (int k0 = 0; k0 < klen; k0 += BK) {
+    if (MODE == 4) {
+      const int kg = k0 + lkk;
+      f32x4_t av = {0.0f, 0.0f, 0.0f, 0.0f}, bv = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (kg < j.kcount) {
+        const int64_t kr = static_cast<int64_t>(j.kstart) + kg;
+        av = *reinterpret_cast<const f32x4_t *>(A + kr * c.lda + j.row0 + lcol);
+        bv = *reinterpret_cast<const f32x4_t *>(B + kr * c.ldb + j.nt * BN + lcol);
+      }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      As[lk + q][lrow] = av[q];
-      Bs[lk + q][lrow] = bv[q];
+      for (int q = 0; q < 4; ++q) {
+        As[lkk][lcol + q] = av[q];
+        Bs[lkk][lcol + q] = bv[q];
+      }
+    } else {
+      const f32x4_t av = *reinterpret_cast<const f32x4_t *>(aptr + k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) As[lk + q][lrow] = av[q];
+      if (MODE <= 1) {
+        const f32x4_t bv = *reinterpret_cast<const f32x4_t *>(bptr + k0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Bs[lk + q][lrow] = bv[q];
+      } else {
+        const f32x4_t bv = *reinterpret_cast<const f32x4_t *>(
+            B + static_cast<int64_t>(k0 + lkk) * c.ldb + j.nt * BN + lcol);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Bs[lkk][lcol + q] = bv[q];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -540,19 +810,65 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     __syncthreads();
   }
 
+  if (MODE == 2) {
+    // as the bf16 mode-2 epilogue, in fp32; the partial sums of dh h are
+    // reduced over the block's 64 columns in a fixed order
+    float *D = static_cast<float *>(c.C);
+    const float *hp = static_cast<const float *>(c.hsave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ty * 4 + i;
+      float ps = 0.0f;
+      if (row < j.rows) {
+        const int64_t grow = static_cast<int64_t>(j.row0) + row;
+        const float rs = c.rowscale ? c.rowscale[grow] : 1.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = j.nt * BN + tx * 4 + q;
+          const float dh = rs * acc[i][q];
+          const float u = c.ug[grow * 2 * N + col], gt = c.ug[grow * 2 * N + N + col];
+          const float sg = 1.0f / (1.0f + expf(-gt));
+          D[grow * c.ldc + col] = dh * (gt * sg);
+          D[grow * c.ldc + N + col] = dh * u * (sg * (1.0f + gt * (1.0f - sg)));
+          ps += dh * hp[grow * N + col];
+        }
+      }
+      red[row][tx] = ps;
+    }
+    __syncthreads();
+    if (c.apart && tx == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = ty * 4 + i;
+        if (row >= j.rows) continue;
+        float t = 0.0f;
+        for (int x = 0; x < 16; ++x) t += red[row][x];
+        c.apart[(static_cast<int64_t>(j.row0) + row) * c.apart_ld + j.nt] = t;
+      }
+    }
+    return;
+  }
   float *C = static_cast<float *>(c.C);
+  if (MODE == 4) C += static_cast<int64_t>(j.g < a.E ? j.g : 0) * c.strideC;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = ty * 4 + i;
     if (row >= j.rows) continue;
-    float *crow = C + (static_cast<int64_t>(j.row0) + row) * c.ldc;
+    const int64_t grow = static_cast<int64_t>(j.row0) + row;
+    float *crow = C + grow * c.ldc;
     if (MODE == 0) {
       const int Ih = N / 2;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int col = j.nt * (BN / 2) + tx * 2 + q;
         const float u = acc[i][q], gt = acc[i][2 + q];
-        if (col < Ih) crow[col] = gt / (1.0f + expf(-gt)) * u;
+        if (col < Ih) {
+          crow[col] = gt / (1.0f + expf(-gt)) * u;
+          if (c.ug) {
+            c.ug[grow * N + col] = u;
+            c.ug[grow * N + Ih + col] = gt;
+          }
+        }
       }
     } else {
 #pragma unroll
@@ -570,49 +886,92 @@ static int col_tiles_host(int N, int BN, bool upgate) {
   return upgate ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
 }
 
-static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtype,
-                              bool upgate, hipStream_t s) {
+// mode 0 ([up; gate]) and mode 3 run the default tile; modes 1 and 2 (the
+// down projection's shapes: fewer k steps) split each listed row tile.
+static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtype, int mode,
+                              hipStream_t s) {
   const int BN = dtype == kBF16 ? kGemmBN : kGemmF32BN;
   const bool stream = dtype == kBF16 && tile_rows == kGemmStreamBM;
+  const bool upgate = mode == 0;
+  const bool down_like = mode == 1 || mode == 2;
   a.NTn = std::max(col_tiles_host(a.cls[0].N, BN, upgate), col_tiles_host(a.cls[1].N, BN, upgate));
-  a.split = dtype == kBF16 && !upgate && !stream ? kGemmDownSplit : 1;
+  a.split = dtype == kBF16 && down_like && !stream ? kGemmDownSplit : 1;
   a.sub_rows = a.split > 1 ? kGemmBM / a.split : 1 << 30;
   const int64_t work = static_cast<int64_t>(max_tiles) * a.split * a.NTn;
   const unsigned grid = static_cast<unsigned>((work + 7) / 8 * 8);
   if (grid == 0) return hipSuccess;
   const dim3 block(128 * kGemmWN);
-  if (stream) {
-    if (upgate)
-      hipLaunchKernelGGL((gemm_bf16_kernel<0, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages, kGemmWN>),
-                         dim3(grid), block, 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<1, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages, kGemmWN>),
-                         dim3(grid), block, 0, s, a);
-  } else if (dtype == kBF16) {
-    if (upgate)
-      hipLaunchKernelGGL((gemm_bf16_kernel<0, kGemmBM, kGemmBK, kGemmStages, kGemmWN>),
-                         dim3(grid), block, 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<1, kGemmBM / kGemmDownSplit, kGemmBK, kGemmDownStages,
-                                           kGemmWN>),
-                         dim3(grid), block, 0, s, a);
+#define HI3_LAUNCH(M, BMv, BKv, NSTv)                                                      \
+  hipLaunchKernelGGL((gemm_bf16_kernel<M, BMv, BKv, NSTv, kGemmWN>), dim3(grid), block, 0, s, a)
+  if (dtype == kBF16) {
+    constexpr int DBM = kGemmBM / kGemmDownSplit;
+    switch (mode) {
+      case 0:
+        if (stream) HI3_LAUNCH(0, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages);
+        else HI3_LAUNCH(0, kGemmBM, kGemmBK, kGemmStages);
+        break;
+      case 1:
+        if (stream) HI3_LAUNCH(1, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages);
+        else HI3_LAUNCH(1, DBM, kGemmBK, kGemmDownStages);
+        break;
+      case 2:
+        if (stream) HI3_LAUNCH(2, kGemmStreamBM, 64, kGemmStreamStages);
+        else HI3_LAUNCH(2, DBM, 64, kGemmDownStages);
+        break;
+      default:
+        if (stream) HI3_LAUNCH(3, kGemmStreamBM, 64, kGemmStreamStages);
+        else HI3_LAUNCH(3, kGemmBM, 64, kGemmStages);
+        break;
+    }
   } else {
-    if (upgate)
-      hipLaunchKernelGGL(gemm_f32_kernel<0>, dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+    switch (mode) {
+      case 0: hipLaunchKernelGGL(gemm_f32_kernel<0>, dim3(grid), dim3(256), 0, s, a); break;
+      case 1: hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(grid), dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL(gemm_f32_kernel<2>, dim3(grid), dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL(gemm_f32_kernel<3>, dim3(grid), dim3(256), 0, s, a); break;
+    }
   }
+#undef HI3_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
                               hipStream_t s) {
-  return launch_gemm(a, max_tiles, tile_rows, dtype, true, s);
+  return launch_gemm(a, max_tiles, tile_rows, dtype, 0, s);
 }
 
 hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
                             hipStream_t s) {
-  return launch_gemm(a, max_tiles, tile_rows, dtype, false, s);
+  return launch_gemm(a, max_tiles, tile_rows, dtype, 1, s);
+}
+
+hipError_t launch_gemm_dgrad_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
+                                  hipStream_t s) {
+  return launch_gemm(a, max_tiles, tile_rows, dtype, 2, s);
+}
+
+hipError_t launch_gemm_dgrad_up_gate(const GemmArgs &a, int max_tiles, int tile_rows,
+                                     int dtype, hipStream_t s) {
+  return launch_gemm(a, max_tiles, tile_rows, dtype, 3, s);
+}
+
+// Mode 4: a class whose C is null is skipped.
+hipError_t launch_gemm_wgrad(const GemmArgs &a0, int E, int dtype, hipStream_t s) {
+  GemmArgs a = a0;
+  const int T = dtype == kBF16 ? kGemmBN : kGemmF32BN;  // square output tiles
+  auto tiles_of = [&](const GemmClass &c) {
+    return static_cast<int64_t>((c.M + T - 1) / T) * ((c.N + T - 1) / T);
+  };
+  a.wg_shared_blocks = a.cls[1].C ? static_cast<int>((tiles_of(a.cls[1]) + 7) / 8 * 8) : 0;
+  const int64_t routed = a.cls[0].C ? 8 * tiles_of(a.cls[0]) * ((E + 7) / 8) : 0;
+  const int64_t grid = a.wg_shared_blocks + routed;
+  if (grid == 0) return hipSuccess;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, kGemmBN, 64, 2, kGemmWN>), dim3(static_cast<unsigned>(grid)),
+                       dim3(128 * kGemmWN), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemm_f32_kernel<4>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace hi3

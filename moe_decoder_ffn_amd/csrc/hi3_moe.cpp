@@ -138,6 +138,180 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   return rec.ok ? HI3_OK : HI3_E_HIP;
 }
 
+// Gradient of sum over real rows of dout . out with the routes held fixed:
+// the routes and the [up; gate] projection are recomputed (u and g kept in
+// fp32), then the gradients flow through the down projection (mode 2, with
+// the SwiGLU backward in its epilogue), the [up; gate] projection (mode 3),
+// the router, and into the weight gradients (mode 4).
+int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
+                  const void *w_down, const void *w_shared_up_gate, const void *w_shared_down,
+                  const uint8_t *pad_mask, const void *dout, int64_t T, int32_t H, int32_t E,
+                  int32_t K, int32_t I, int32_t Is, int32_t dtype, void *dx, float *dw_router,
+                  void *dw_up_gate, void *dw_down, void *dw_shared_up_gate,
+                  void *dw_shared_down, void *workspace, size_t workspace_bytes,
+                  void *hip_stream, void *const *events) {
+  int st = check_sizes(T, H, E, K, I, Is, dtype, true);
+  if (st != HI3_OK) return st;
+  // with no rows the inputs are not read (they may be NULL)
+  if (T > 0 &&
+      (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !dout))
+    return HI3_E_NULL;
+  st = all_aligned({x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                    dout, dx, dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down,
+                    workspace});
+  if (st != HI3_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const size_t es = dtype == HI3_BF16 ? 2 : 4;
+  if (T == 0) {
+    // no rows: every requested weight gradient is zero
+    HI3_TRY(launch_zero(dw_router, dw_router ? size_t(E) * H * 4 : 0, s));
+    HI3_TRY(launch_zero(dw_up_gate, dw_up_gate ? size_t(E) * 2 * I * H * es : 0, s));
+    HI3_TRY(launch_zero(dw_down, dw_down ? size_t(E) * H * I * es : 0, s));
+    HI3_TRY(launch_zero(dw_shared_up_gate, dw_shared_up_gate ? size_t(2) * Is * H * es : 0, s));
+    HI3_TRY(launch_zero(dw_shared_down, dw_shared_down ? size_t(H) * Is * es : 0, s));
+    return HI3_OK;
+  }
+  if (!workspace) return HI3_E_NULL;
+  const Plan p = make_plan(T, H, E, K, I, Is, dtype, true);
+  if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
+
+  char *ws = static_cast<char *>(workspace);
+  auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  int32_t *idx = static_cast<int32_t *>(at(p.idx));
+  float *wts = static_cast<float *>(at(p.wts));
+  int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
+  int32_t *blkval = static_cast<int32_t *>(at(p.blkval));
+  int32_t *slotof = static_cast<int32_t *>(at(p.slotof));
+  int32_t *perm = static_cast<int32_t *>(at(p.perm));
+  int32_t *vtok = static_cast<int32_t *>(at(p.vtok));
+  int32_t *vidx = static_cast<int32_t *>(at(p.vidx));
+  const int4 *tiles = static_cast<const int4 *>(at(p.tiles));
+  const int32_t *gto = static_cast<const int32_t *>(at(p.gto));
+  const int32_t *eoff = static_cast<const int32_t *>(at(p.eoff));
+  const int32_t *counts = static_cast<const int32_t *>(at(p.counts));
+  const int32_t *misc = static_cast<const int32_t *>(at(p.misc));
+  Recorder rec{events, s};
+
+  // 0-2: routes, offsets, slots (as in the forward)
+  rec.at(0);
+  RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K, p.Epad,
+                idx, wts, blkcnt, blkval};
+  HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
+  rec.at(1);
+  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
+              static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
+              static_cast<int32_t *>(at(p.eoff)), nullptr,
+              static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
+              static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
+  HI3_TRY(launch_scan(sa, s));
+  rec.at(2);
+  ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm, slotof, vtok, vidx};
+  HI3_TRY(launch_scatter(sc, s));
+  // 3: [up; gate] projection again: h as the forward stores it, u and g in fp32
+  rec.at(3);
+  GemmArgs up{};
+  up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
+  up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
+  up.cls[0].ug = static_cast<float *>(at(p.ug));
+  up.cls[1].ug = static_cast<float *>(at(p.ugs));
+  up.tiles = tiles;
+  up.gto = gto;
+  up.E = E;
+  HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
+  // 4: x and w dout by slot; x and dout by real row when there is padding
+  rec.at(4);
+  const bool compact = pad_mask != nullptr;
+  BwdGatherArgs ga{x, dout, wts, slotof, vidx, pad_mask, T, H, K, at(p.xs), at(p.dys),
+                   static_cast<float *>(at(p.wslot)), compact ? at(p.xv) : nullptr,
+                   compact ? at(p.doutv) : nullptr};
+  HI3_TRY(launch_bwd_gather(ga, dtype, s));
+  // 5: dh = w W2^T dout (dout rows gathered through the slot -> token map, w
+  // applied in fp32) and the SwiGLU backward: [du; dg], partial sums of dh h
+  rec.at(5);
+  GemmArgs d2{};
+  d2.cls[0] = GemmClass{dout, H, perm, w_down, int64_t{H} * I, at(p.dd), 2 * I, I, H};
+  d2.cls[0].rowscale = static_cast<const float *>(at(p.wslot));
+  d2.cls[0].ldb = I;
+  d2.cls[0].ug = static_cast<float *>(at(p.ug));
+  d2.cls[0].hsave = at(p.h);
+  d2.cls[0].apart = static_cast<float *>(at(p.apart));
+  d2.cls[0].apart_ld = p.P;
+  d2.cls[1] = GemmClass{dout, H, vtok, w_shared_down, 0, at(p.dds), 2 * Is, Is, H};
+  d2.cls[1].ldb = Is;
+  d2.cls[1].ug = static_cast<float *>(at(p.ugs));
+  d2.cls[1].hsave = at(p.hs);
+  d2.tiles = tiles;
+  d2.gto = gto;
+  d2.E = E;
+  HI3_TRY(launch_gemm_dgrad_down(d2, p.max_tiles, p.BM, dtype, s));
+  // 6: dx by slot / by real row = W13^T [du; dg]
+  rec.at(6);
+  if (dx) {
+    GemmArgs d3{};
+    d3.cls[0] = GemmClass{at(p.dd), 2 * I, nullptr, w_up_gate, int64_t{2} * I * H, at(p.y), H,
+                          H, 2 * I};
+    d3.cls[0].ldb = H;
+    d3.cls[1] = GemmClass{at(p.dds), 2 * Is, nullptr, w_shared_up_gate, 0, at(p.ys), H, H,
+                          2 * Is};
+    d3.cls[1].ldb = H;
+    d3.tiles = tiles;
+    d3.gto = gto;
+    d3.E = E;
+    HI3_TRY(launch_gemm_dgrad_up_gate(d3, p.max_tiles, p.BM, dtype, s));
+  }
+  // 7: logit gradient and dx
+  rec.at(7);
+  float *dls = static_cast<float *>(at(p.dls));
+  BwdCombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
+                    static_cast<const float *>(at(p.apart)), p.P, slotof, idx, vidx, wts,
+                    w_router, pad_mask, T, H, K, dls, dx};
+  HI3_TRY(launch_bwd_combine(ca, dtype, s));
+  // 8: router weight gradient
+  rec.at(8);
+  if (dw_router) HI3_TRY(launch_dw_router(dls, at(p.xs), eoff, E, H, dtype, dw_router, s));
+  // 9, 10: expert weight gradients
+  HI3_TRY(launch_zero(at(p.zrow), 512, s));
+  rec.at(9);
+  GemmArgs w2{};
+  w2.goff = eoff;
+  w2.gcnt = counts;
+  w2.nreal = misc;
+  w2.zrow = at(p.zrow);
+  w2.E = E;
+  if (dw_down) {
+    w2.cls[0].A = at(p.dys); w2.cls[0].lda = H;
+    w2.cls[0].B = at(p.h); w2.cls[0].ldb = I;
+    w2.cls[0].C = dw_down; w2.cls[0].ldc = I; w2.cls[0].strideC = int64_t{H} * I;
+    w2.cls[0].M = H; w2.cls[0].N = I;
+  }
+  if (dw_shared_down) {
+    w2.cls[1].A = compact ? at(p.doutv) : dout; w2.cls[1].lda = H;
+    w2.cls[1].B = at(p.hs); w2.cls[1].ldb = Is;
+    w2.cls[1].C = dw_shared_down; w2.cls[1].ldc = Is;
+    w2.cls[1].M = H; w2.cls[1].N = Is;
+  }
+  HI3_TRY(launch_gemm_wgrad(w2, E, dtype, s));
+  rec.at(10);
+  GemmArgs w13 = w2;
+  w13.cls[0] = GemmClass{};
+  w13.cls[1] = GemmClass{};
+  if (dw_up_gate) {
+    w13.cls[0].A = at(p.dd); w13.cls[0].lda = 2 * I;
+    w13.cls[0].B = at(p.xs); w13.cls[0].ldb = H;
+    w13.cls[0].C = dw_up_gate; w13.cls[0].ldc = H; w13.cls[0].strideC = int64_t{2} * I * H;
+    w13.cls[0].M = 2 * I; w13.cls[0].N = H;
+  }
+  if (dw_shared_up_gate) {
+    w13.cls[1].A = at(p.dds); w13.cls[1].lda = 2 * Is;
+    w13.cls[1].B = compact ? at(p.xv) : x; w13.cls[1].ldb = H;
+    w13.cls[1].C = dw_shared_up_gate; w13.cls[1].ldc = H;
+    w13.cls[1].M = 2 * Is; w13.cls[1].N = H;
+  }
+  HI3_TRY(launch_gemm_wgrad(w13, E, dtype, s));
+  rec.at(11);
+  return rec.ok ? HI3_OK : HI3_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,6 +447,51 @@ int hi3_moe_rmsnorm(const void *x, const void *weight, float eps, const uint8_t 
   NormArgs na{x, weight, pad_mask, T, H, eps, xn};
   HI3_TRY(launch_rmsnorm(na, dtype, static_cast<hipStream_t>(hip_stream)));
   return HI3_OK;
+}
+
+size_t hi3_moe_backward_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                                       int32_t I_shared, int32_t dtype) {
+  if (check_sizes(T, H, E, K, I, I_shared, dtype, true) != HI3_OK) return 0;
+  if (T == 0) return 0;
+  return make_plan(T, H, E, K, I, I_shared, dtype, true).total;
+}
+
+int hi3_moe_backward(const void *x, const float *w_router, const void *w_up_gate,
+                     const void *w_down, const void *w_shared_up_gate,
+                     const void *w_shared_down, const uint8_t *pad_mask, const void *dout,
+                     int64_t T, int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                     int32_t dtype, void *dx, float *dw_router, void *dw_up_gate,
+                     void *dw_down, void *dw_shared_up_gate, void *dw_shared_down,
+                     void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return backward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                       dout, T, H, E, K, I, I_shared, dtype, dx, dw_router, dw_up_gate, dw_down,
+                       dw_shared_up_gate, dw_shared_down, workspace, workspace_bytes, hip_stream,
+                       nullptr);
+}
+
+int hi3_moe_backward_instrumented(const void *x, const float *w_router, const void *w_up_gate,
+                                  const void *w_down, const void *w_shared_up_gate,
+                                  const void *w_shared_down, const uint8_t *pad_mask,
+                                  const void *dout, int64_t T, int32_t H, int32_t E, int32_t K,
+                                  int32_t I, int32_t I_shared, int32_t dtype, void *dx,
+                                  float *dw_router, void *dw_up_gate, void *dw_down,
+                                  void *dw_shared_up_gate, void *dw_shared_down,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream,
+                                  void *const *stage_events) {
+  if (!stage_events) return HI3_E_NULL;
+  return backward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                       dout, T, H, E, K, I, I_shared, dtype, dx, dw_router, dw_up_gate, dw_down,
+                       dw_shared_up_gate, dw_shared_down, workspace, workspace_bytes, hip_stream,
+                       stage_events);
+}
+
+const char *hi3_moe_backward_stage_name(int stage) {
+  static const char *names[HI3_NUM_BWD_STAGES] = {
+      "router", "scan", "scatter", "gemm_up_gate_recompute", "gather_bwd", "gemm_dgrad_down",
+      "gemm_dgrad_up_gate", "combine_bwd", "dw_router", "gemm_wgrad_down",
+      "gemm_wgrad_up_gate"};
+  if (stage < 0 || stage >= HI3_NUM_BWD_STAGES) return "?";
+  return names[stage];
 }
 
 const char *hi3_moe_stage_name(int stage) {

@@ -193,3 +193,65 @@ def _fwd_nr(**kw):
 ])
 def test_forward_norm_residual_validation(kw, status):
     assert _fwd_nr(**kw) == status
+
+
+def _bwd(**kw):
+    a = dict(x=P, wr=P, w13=P, w2=P, ws13=P, ws2=P, pad=None, dout=P, T=64, H=256, E=8, K=2,
+             I=128, Is=128, dt=m.HI3_BF16, dx=P, dwr=P, dw13=P, dw2=P, dws13=P, dws2=P, ws=P,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return m.lib.hi3_moe_backward(
+        a["x"], a["wr"], a["w13"], a["w2"], a["ws13"], a["ws2"], a["pad"], a["dout"], a["T"],
+        a["H"], a["E"], a["K"], a["I"], a["Is"], a["dt"], a["dx"], a["dwr"], a["dw13"],
+        a["dw2"], a["dws13"], a["dws2"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), m.HI3_E_NULL),
+    (dict(wr=None), m.HI3_E_NULL),
+    (dict(w13=None), m.HI3_E_NULL),
+    (dict(w2=None), m.HI3_E_NULL),
+    (dict(ws13=None), m.HI3_E_NULL),
+    (dict(ws2=None), m.HI3_E_NULL),
+    (dict(dout=None), m.HI3_E_NULL),
+    (dict(ws=None), m.HI3_E_NULL),
+    (dict(T=-1), m.HI3_E_SHAPE),
+    (dict(K=9), m.HI3_E_SHAPE),
+    (dict(I=0), m.HI3_E_SHAPE),
+    (dict(dt=2), m.HI3_E_UNSUPPORTED),
+    (dict(E=65, K=8), m.HI3_E_UNSUPPORTED),
+    (dict(H=250), m.HI3_E_UNSUPPORTED),
+    (dict(Is=96), m.HI3_E_UNSUPPORTED),
+    (dict(dout=UNALIGNED), m.HI3_E_UNSUPPORTED),
+    (dict(dx=UNALIGNED), m.HI3_E_UNSUPPORTED),
+    (dict(dw13=UNALIGNED), m.HI3_E_UNSUPPORTED),
+    (dict(wsb=1000), m.HI3_E_WORKSPACE),
+    # no rows and no weight gradient requested: nothing to enqueue
+    (dict(T=0, ws=None, dwr=None, dw13=None, dw2=None, dws13=None, dws2=None), m.HI3_OK),
+    (dict(T=0, x=None, dout=None, ws=None, dwr=None, dw13=None, dw2=None, dws13=None,
+          dws2=None), m.HI3_OK),
+])
+def test_backward_validation(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_backward_workspace_size_and_stage_names():
+    bws = m.hi3_moe_backward_workspace_size
+    need = bws(64, 256, 8, 2, 128, 128, m.HI3_BF16)
+    assert need > m.hi3_moe_workspace_size(64, 256, 8, 2, 128, 128, m.HI3_BF16)
+    assert _bwd(wsb=need - 1) == m.HI3_E_WORKSPACE
+    assert bws(0, 256, 8, 2, 128, 128, 1) == 0
+    assert bws(64, 256, 8, 2, 0, 128, 1) == 0
+    # dominant buffers at full size: fp32 u, g and dx by slot, then the
+    # bf16 slot copies of x, w dout and [du; dg]
+    T, TK = 4131, 4131 * 8
+    big = TK * 6144 * 4 + TK * 4096 * 4 + TK * 4096 * 2 * 2 + TK * 6144 * 2 + TK * 3072 * 2
+    full = bws(T, 4096, 64, 8, 3072, 3072, m.HI3_BF16)
+    assert big <= full <= big + 512 * 2 ** 20
+    names = [m.hi3_moe_backward_stage_name(i) for i in range(m.HI3_NUM_BWD_STAGES)]
+    assert len(set(names)) == m.HI3_NUM_BWD_STAGES and "?" not in names
+    assert m.hi3_moe_backward_stage_name(m.HI3_NUM_BWD_STAGES) == "?"
+    f = m.lib.hi3_moe_backward_instrumented
+    args = [P, P, P, P, P, P, None, P, 64, 256, 8, 2, 128, 128, 1, P, P, P, P, P, P, P,
+            1 << 40, None]
+    assert f(*args, None) == m.HI3_E_NULL

@@ -1,0 +1,189 @@
+"""GPU parity of the layer's backward pass (hi3_moe_backward) against the CPU
+oracle's backward (oracle.moe_backward): small cases compared on every
+element of every gradient (several GEMM tiles, ragged tails, padding, the
+small-batch tile configuration), the full-size workload on sampled rows of
+dx, plus invariants and determinism.
+
+Routes: the backward recomputes them; the GPU's routes (hi3_moe_route, the
+same kernel) are checked against the oracle's by the forward rules, and the
+oracle's backward then runs on the GPU's ids where the K-th and (K+1)-th
+logits are within the tie tolerance (both selections are correct there).
+
+Tolerance (parity.check_grad): fp32 layers max |err| <= 1e-5 RMS; bf16
+layers per element |err| <= ulp + 2^-8 * (sum of |terms| summed into the
+element, from the oracle), and RMS error <= 5e-3 RMS over each tensor.
+The forward's 2e-2 RMS max-error bar does not fit gradients: they are sums
+over few rows of heavy-tailed products, whose largest elements sit far
+above the tensor's RMS and whose cancelling elements far below their terms.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wk
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+from parity import check_grad, check_routes, to_dev, to_host, upload  # noqa: E402
+
+NAMES = {"dx": "dx", "dw_router": "dw_router", "dw_up_gate": "dw13", "dw_down": "dw2",
+         "dw_shared_up_gate": "dws13", "dw_shared_down": "dws2"}
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_backward(d, K, pad=None):
+    import moe_decoder_ffn_amd as m
+    dd = upload(d)
+    padd = to_dev(pad) if pad is not None else None
+    g = m.moe_backward(dd["x"], dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"],
+                       dd["dout"], K, pad_mask=padd)
+    _, idx, w, _ = m.moe_forward(dd["x"], dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
+                                 dd["ws2"], K, pad_mask=padd, return_routes=True)
+    torch.cuda.synchronize()
+    return {k: to_host(v) for k, v in g.items()}, to_host(idx), to_host(w)
+
+
+def make_case(dtype, H, E, K, I, Is, seq, plen, seed=7, rscale=5.0):
+    shape = wk.LayerShape(H=H, E=E, K=K, I=I, Is=Is, dtype=dtype)
+    wl = wk.custom(shape, seq, plen)
+    d = wk.make_inputs(wl, seed)
+    d["w_router"] = d["w_router"] * np.float32(rscale)
+    d["dout"] = wk.make_dout(wl, seed)
+    pad = d.pop("pad_mask")
+    return d, (pad if pad.any() else None)
+
+
+def check_all(d, K, pad, dtype):
+    E = d["w_router"].shape[0]
+    g, idx, w = gpu_backward(d, K, pad)
+    ref = oracle.route(d["x"], d["w_router"], K, pad_mask=pad)
+    near, ref_idx, ref_w = check_routes(idx, w, ref, pad, E, K)
+    exp = oracle.moe_backward(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
+                              d["dout"], K, pad_mask=pad, idx=ref_idx, w=ref_w,
+                              magnitudes=True)
+    valid = np.ones(d["x"].shape[0], bool) if pad is None else pad == 0
+    errs = {}
+    for k, ok in NAMES.items():
+        if k == "dx":
+            errs[k] = check_grad(g[k][valid], exp[ok][valid], exp["m_" + ok][valid], dtype, k)
+            if pad is not None:
+                assert np.all(g[k][~valid] == 0), "padding rows of dx were written"
+        else:
+            errs[k] = check_grad(g[k], exp[ok], exp["m_" + ok], dtype, k)
+    return g, errs, near
+
+
+SMALL = [
+    # name, dtype, H, E, K, I, Is, seq_lens, padded_len
+    ("tiny_f32", wk.F32, 256, 8, 2, 128, 128, (64,), None),
+    ("f32_ragged_pad", wk.F32, 192, 8, 3, 192, 64, (150, 37), 160),
+    ("bf16_tiles", wk.BF16, 512, 8, 2, 256, 192, (700,), None),
+    ("bf16_e16_pad", wk.BF16, 256, 16, 4, 320, 128, (300, 129, 7), 300),
+    ("bf16_e64_k8_stream", wk.BF16, 512, 64, 8, 128, 256, (600,), None),
+    ("bf16_one_token", wk.BF16, 256, 8, 2, 128, 128, (1,), None),
+]
+
+
+@pytest.mark.parametrize("name,dtype,H,E,K,I,Is,seq,plen", SMALL)
+def test_backward_small_all_elements(name, dtype, H, E, K, I, Is, seq, plen):
+    _say(f"[backward] {name}")
+    d, pad = make_case(dtype, H, E, K, I, Is, seq, plen)
+    g, errs, near = check_all(d, K, pad, dtype)
+    _say(f"  max err / RMS: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+def test_backward_unused_experts_zero_and_deterministic():
+    # 3 tokens over 16 experts with K = 2: at least 10 experts get no row;
+    # their weight gradients (and router rows) must be exactly zero; two
+    # runs are bit-identical
+    _say("[backward] unused experts")
+    d, pad = make_case(wk.BF16, 256, 16, 2, 128, 128, (3,), None)
+    g1, idx, _ = gpu_backward(d, 2)
+    g2, _, _ = gpu_backward(d, 2)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+    used = set(np.unique(idx).tolist())
+    assert len(used) <= 6
+    for e in range(16):
+        if e not in used:
+            assert np.all(g1["dw_up_gate"][e] == 0) and np.all(g1["dw_down"][e] == 0)
+            assert np.all(g1["dw_router"][e] == 0)
+
+
+def test_backward_zero_dout_gives_zero():
+    _say("[backward] zero dout")
+    d, pad = make_case(wk.BF16, 256, 8, 2, 128, 128, (100,), None)
+    d["dout"] = np.zeros_like(d["dout"])
+    g, _, _ = gpu_backward(d, 2)
+    for k, v in g.items():
+        assert np.all(v.astype(np.float64) == 0) if v.dtype != np.uint16 else np.all(
+            (v & 0x7FFF) == 0), k
+
+
+def test_backward_outputs_optional():
+    # any subset of outputs: the computed ones are bit-identical to a full run
+    import moe_decoder_ffn_amd as m
+    _say("[backward] optional outputs")
+    d, pad = make_case(wk.BF16, 256, 8, 2, 128, 128, (200,), None)
+    dd = upload(d)
+    full = m.moe_backward(dd["x"], dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"],
+                          dd["dout"], 2)
+    for want in (("dx",), ("dw_router",), ("dw_down", "dw_shared_up_gate")):
+        part = m.moe_backward(dd["x"], dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
+                              dd["ws2"], dd["dout"], 2, want=want)
+        assert set(part) == set(want)
+        for k in want:
+            assert torch.equal(part[k], full[k]), (want, k)
+
+
+def test_backward_no_rows_zero_weight_gradients():
+    import moe_decoder_ffn_amd as m
+    _say("[backward] T = 0")
+    # a zero-row view of a real allocation: inputs must not be NULL
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda")[:0]
+    wr = torch.ones((8, 256), dtype=torch.float32, device="cuda")
+    w13 = torch.ones((8, 256, 256), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.ones((8, 256, 128), dtype=torch.bfloat16, device="cuda")
+    ws13 = torch.ones((256, 256), dtype=torch.bfloat16, device="cuda")
+    ws2 = torch.ones((256, 128), dtype=torch.bfloat16, device="cuda")
+    g = m.moe_backward(x, wr, w13, w2, ws13, ws2, x, 2)
+    torch.cuda.synchronize()
+    for k, v in g.items():
+        if k != "dx":
+            assert v.numel() > 0 and bool((v == 0).all()), k
+
+
+@pytest.mark.parametrize("name", ["image_1024"])
+def test_backward_full_size_sampled_rows(name):
+    # full size, the launch configuration the benchmark times: dx of sampled
+    # rows against the oracle (dx of a row depends on that row alone); every
+    # gradient finite; deterministic
+    _say(f"[backward] full size {name}")
+    wl = wk.workload(name)
+    d = wk.make_inputs(wl, 0)
+    d["dout"] = wk.make_dout(wl, 0)
+    pad = d.pop("pad_mask")
+    pad = pad if pad.any() else None
+    K, E = wl.shape.K, wl.shape.E
+    g, idx, w = gpu_backward(d, K, pad)
+    ref = oracle.route(d["x"], d["w_router"], K, pad_mask=pad)
+    near, ref_idx, ref_w = check_routes(idx, w, ref, pad, E, K)
+    for k, v in g.items():
+        f = v.astype(np.float64) if v.dtype != np.uint16 else wk.bf16_bits_to_f32(v)
+        assert np.isfinite(f).all(), k
+    T = d["x"].shape[0]
+    rows = np.array([0, 1, T // 2, T - 1])
+    sub = {k: d[k][rows] for k in ("x", "dout")}
+    exp = oracle.moe_backward(sub["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
+                              sub["dout"], K, idx=ref_idx[rows], w=ref_w[rows], want=("dx",),
+                              magnitudes=True)
+    check_grad(g["dx"][rows], exp["dx"], exp["m_dx"], wl.shape.dtype, "dx")
+    g2, _, _ = gpu_backward(d, K, pad)
+    for k in g:
+        assert np.array_equal(g[k], g2[k]), k

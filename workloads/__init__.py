@@ -151,7 +151,7 @@ def custom(shape: LayerShape, seq_lens, padded_len=None, skew=False,
 # ---------------------------------------------------------------- helpers
 
 def _streams(seed: int) -> dict:
-    names = ("x", "w_router", "w13", "w2", "ws13", "ws2", "lengths", "spare")
+    names = ("x", "w_router", "w13", "w2", "ws13", "ws2", "lengths", "spare", "dout")
     kids = np.random.SeedSequence(int(seed)).spawn(len(names))
     return dict(zip(names, kids))
 
@@ -269,6 +269,18 @@ def make_x(wl: Workload, seed: int = 0) -> tuple:
     if pad.any():
         x[pad.astype(bool)] = BF16_NAN if wl.shape.dtype == BF16 else np.nan
     return x, pad
+
+
+def make_dout(wl: Workload, seed: int = 0) -> np.ndarray:
+    """Output gradient [T,H] ~ N(0,1) in the layer dtype (the backward's
+    input), padding rows NaN like x's."""
+    s = _streams(seed)
+    H, T = wl.shape.H, wl.T
+    g = _normal_fill(s["dout"], T * H, 1.0, _X_ROWS_PER_CHUNK * H, wl.shape.dtype).reshape(T, H)
+    pad = wl.pad_mask()
+    if pad.any():
+        g[pad.astype(bool)] = BF16_NAN if wl.shape.dtype == BF16 else np.nan
+    return g
 
 
 def make_inputs(wl: Workload, seed: int = 0) -> dict:
