@@ -235,6 +235,129 @@ def norm_residual_bench(args, m, wl, d, dd, pad, ws, stream):
     print(json.dumps(line), flush=True)
 
 
+def backward_gemm_flops(wl):
+    """Algorithmic FLOP of the backward's GEMM stages (routed + shared)."""
+    sh = wl.shape
+    Tv = wl.T_valid
+    up = Tv * (sh.K * 2 * sh.H * 2 * sh.I + 2 * sh.H * 2 * sh.Is)
+    down = Tv * (sh.K * 2 * sh.I * sh.H + 2 * sh.Is * sh.H)
+    return {"gemm_up_gate_recompute": up, "gemm_dgrad_down": down, "gemm_dgrad_up_gate": up,
+            "gemm_wgrad_down": down, "gemm_wgrad_up_gate": up}
+
+
+def cpu_baseline_backward(wl, d, dout, K, target_s):
+    """The CPU oracle's backward as it stands, on a bounded sample of real
+    tokens (every gradient's contribution of those tokens)."""
+    import oracle
+    pad = d["pad_mask"]
+    valid = np.nonzero(pad == 0)[0]
+    args = (d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"])
+    n, total_t = 0, 0.0
+    while total_t < target_s and n < valid.size:
+        rows = valid[n:n + 1]
+        t0 = time.perf_counter()
+        oracle.moe_backward(d["x"][rows], *args, dout[rows], K)
+        total_t += time.perf_counter() - t0
+        n += 1
+    return {"value": n / total_t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} real tokens of {wl.name} (all gradients, fp64 C, one thread), "
+                      f"{total_t:.1f} s"}
+
+
+def backward_bench(args, m, wl, d, dd, pad, stream):
+    """Times hi3_moe_backward per step (all six gradients), with per-stage
+    HIP events; the roofline entry is the slowest GEMM stage."""
+    import torch
+    sh = wl.shape
+    dout_h = wk.make_dout(wl, args.seed)
+    dout = torch.from_numpy(dout_h.view(np.int16)).cuda().view(torch.bfloat16) \
+        if sh.dtype == wk.BF16 else torch.from_numpy(dout_h).cuda()
+    x = dd["x"]
+    dt = x.dtype
+    dx = torch.zeros_like(x)
+    dwr = torch.empty((sh.E, sh.H), dtype=torch.float32, device="cuda")
+    dw13 = torch.empty((sh.E, 2 * sh.I, sh.H), dtype=dt, device="cuda")
+    dw2 = torch.empty((sh.E, sh.H, sh.I), dtype=dt, device="cuda")
+    dws13 = torch.empty((2 * sh.Is, sh.H), dtype=dt, device="cuda")
+    dws2 = torch.empty((sh.H, sh.Is), dtype=dt, device="cuda")
+    n = m.hi3_moe_backward_workspace_size(wl.T, sh.H, sh.E, sh.K, sh.I, sh.Is,
+                                          m.dtype_code(dt))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    log(f"[bench] backward workspace {n / 2**20:.0f} MiB")
+
+    def step(events=None):
+        a = (x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"], pad, dout, sh.K,
+             dx, dwr, dw13, dw2, dws13, dws2, ws)
+        if events is None:
+            m.hi3_moe_backward(*a, stream)
+        else:
+            m.hi3_moe_backward_instrumented(*a, events, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+    hip = HipEvents()
+    ns = m.HI3_NUM_BWD_STAGES
+    evsets = [hip.create(ns + 1) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evsets[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] {args.steps} timed steps done")
+    stage_ms = np.zeros(ns)
+    for evs in evsets:
+        for k in range(ns):
+            stage_ms[k] += hip.elapsed_ms(evs[k], evs[k + 1])
+    stage_ms /= args.steps
+    for evs in evsets:
+        hip.destroy(evs)
+    names = [m.hi3_moe_backward_stage_name(k) for k in range(ns)]
+    ms_per_step = elapsed * 1e3 / args.steps
+    gf = backward_gemm_flops(wl)
+    stages = {}
+    for k, name in enumerate(names):
+        e = {"us": round(stage_ms[k] * 1e3, 2)}
+        if name in gf and stage_ms[k] > 0:
+            e["tflops"] = round(gf[name] / (stage_ms[k] * 1e-3) / 1e12, 1)
+            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        stages[name] = e
+    for name, e in stages.items():
+        log(f"  {name:24s} {e}")
+    dom = max(gf, key=lambda k: stage_ms[names.index(k)])
+    dom_ms = stage_ms[names.index(dom)]
+    achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
+    mode = {"gemm_up_gate_recompute": 0, "gemm_dgrad_down": 2, "gemm_dgrad_up_gate": 3,
+            "gemm_wgrad_down": 4, "gemm_wgrad_up_gate": 4}[dom]
+    roofline = {"kernel": f"gemm_bf16_kernel<{mode}> ({dom})", "bound": "mfma",
+                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    # algorithmic FLOP of the backward proper (twice the forward's GEMMs),
+    # without the recomputed [up; gate] projection
+    flops = sum(v for k, v in gf.items() if k != "gemm_up_gate_recompute")
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle's backward on a sample")
+        cpu = cpu_baseline_backward(wl, d, dout_h, sh.K, args.cpu_seconds)
+    line = {
+        "metric": "MoE-layer backward tokens/s (all gradients), 64e top-8, H=4096, 1 GPU",
+        "value": round(wl.T_valid / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if sh.dtype == wk.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "entry": "backward", "T": wl.T, "T_valid": wl.T_valid,
+                   "H": sh.H, "E": sh.E, "K": sh.K, "I": sh.I, "I_shared": sh.Is,
+                   "seed": args.seed},
+        "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,10 +369,12 @@ def main():
                     help="wall-time budget of the CPU oracle sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
-    ap.add_argument("--entry", default="forward", choices=("forward", "norm_residual"),
+    ap.add_argument("--entry", default="forward",
+                    choices=("forward", "norm_residual", "backward"),
                     help="forward: the layer (hi3_moe_forward); norm_residual: the layer "
                          "inside its block, h + layer(RMSNorm(h)) "
-                         "(hi3_moe_forward_norm_residual)")
+                         "(hi3_moe_forward_norm_residual); backward: all gradients of the "
+                         "layer (hi3_moe_backward)")
     args = ap.parse_args()
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy)
@@ -297,6 +422,10 @@ def main():
 
     if args.entry == "norm_residual":
         norm_residual_bench(args, m, wl, d, dd, pad, ws, stream)
+        return
+    if args.entry == "backward":
+        del ws
+        backward_bench(args, m, wl, d, dd, pad, stream)
         return
 
     for _ in range(args.warmup):

@@ -75,6 +75,33 @@ constexpr int kGemmDownSplit = HI3_GEMM_DOWN_SPLIT;
 constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
 static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
 constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
+// Backward GEMMs: the gradient through the down projection (mode 2) runs each
+// listed row tile as HI3_DGRAD_DOWN_SPLIT blocks; the weight gradients
+// (mode 4) use k steps of HI3_WGRAD_BK rows and HI3_WGRAD_STAGES stages.
+#ifndef HI3_DGRAD_DOWN_SPLIT
+#define HI3_DGRAD_DOWN_SPLIT 2
+#endif
+#ifndef HI3_DGRAD_DOWN_STAGES
+#define HI3_DGRAD_DOWN_STAGES 3
+#endif
+#ifndef HI3_WGRAD_BK
+#define HI3_WGRAD_BK 32
+#endif
+#ifndef HI3_WGRAD_STAGES
+#define HI3_WGRAD_STAGES 3
+#endif
+// Modes 1, 3 and 4 write their tile through the LDS ring (1) or directly
+// from the accumulators (0).
+#ifndef HI3_GEMM_STAGED_STORE
+#define HI3_GEMM_STAGED_STORE 1
+#endif
+constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
+constexpr int kDgradDownSplit = HI3_DGRAD_DOWN_SPLIT;
+constexpr int kDgradDownStages = HI3_DGRAD_DOWN_STAGES;
+constexpr int kWgradBK = HI3_WGRAD_BK;
+constexpr int kWgradStages = HI3_WGRAD_STAGES;
+static_assert(kGemmBM % kDgradDownSplit == 0 && (kGemmBM / kDgradDownSplit) % 64 == 0,
+              "dgrad tile rows");
 // fp32 grouped GEMM tile.
 constexpr int kGemmF32BM = 64;
 constexpr int kGemmF32BN = 64;
@@ -190,7 +217,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Partial sums of dh * h per routed row written by the mode-2 GEMM.
 inline int apart_cols(int I, int dtype) {
-  return dtype == kBF16 ? (I + kGemmBN - 1) / kGemmBN * kGemmWN : (I + kGemmF32BN - 1) / kGemmF32BN;
+  return dtype == kBF16 ? (I + kGemmBN - 1) / kGemmBN : (I + kGemmF32BN - 1) / kGemmF32BN;
 }
 
 

@@ -276,8 +276,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   constexpr int MI = BM / 64;               // 32-row sub-tiles per wave
   constexpr int NI = BN / WN / 32;          // 32-column sub-tiles per wave
   static_assert(BN == 256 && BM % 64 == 0 && BM <= 256 && (BK == 32 || BK == 64), "tile");
-  static_assert(!AT || (BM == 256 && BK == 64), "k-major A tile");
-  static_assert(!BT || BK == 64, "k-major B tile");
+  static_assert(!AT || BM == 256, "k-major A tile");
+  static_assert(!(AT || BT) || BK == 32 || BK == 64, "k-major k step");
   static_assert(NST >= 2 && NST <= 5, "stages");
   static_assert(BM * BK * 2 % (1024 * NW) == 0 && BN * BK * 2 % (1024 * NW) == 0,
                 "each wave copies a whole number of 1 KiB blocks");
@@ -577,52 +577,145 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     // acc = W2^T dout); u and g as the forward computed them, h as it stored
     // them. du = dh SiLU(g), dg = dh u SiLU'(g) with
     // SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g)); [du; dg] is
-    // stored in the layer dtype (row stride 2N, du first). The sum of dh h
-    // over the wave's columns of each row goes to apart.
+    // stored in the layer dtype (row stride 2N, du first); the sum of dh h
+    // over the tile's columns of each row goes to apart[row, column tile].
+    // The accumulators hold one row per lane, which would make every global
+    // access of this epilogue touch 64 rows; so the tile of acc is staged in
+    // the (now idle) LDS ring and each wave then walks whole rows: lane l
+    // takes columns 4 l .. 4 l + 3, and the u, g, h reads and the du, dg
+    // writes are contiguous row segments.
+    constexpr int SLD = BN + 4;  // staged row stride in floats (16 B pad: bank spread)
+    static_assert(BM <= 128 && NST * (BM + BN) * BK * 2 >= BM * SLD * 4,
+                  "the dh tile fits in the LDS ring");
+    float *stg = reinterpret_cast<float *>(sA0);
+    // every wave's last LDS reads have completed (the MFMAs consumed them)
+    // and the last step ended with a workgroup barrier: the ring is free
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * (BM / 2) + mi * 32 + r;
+          const int c = wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
+          *reinterpret_cast<f32x4_t *>(stg + row * SLD + c) =
+              f32x4_t{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                      acc[mi][ni][4 * q + 3]};
+        }
+    __syncthreads();
     uint16_t *D = static_cast<uint16_t *>(Cv);
     const float *ugp = cl.ug;
     const uint16_t *hp = static_cast<const uint16_t *>(cl.hsave);
+    const int col = j.nt * BN + 4 * lane;
+    const bool cok = col < N;
+    constexpr int UR = 4;  // rows per wave in flight
+#pragma unroll 1
+    for (int r0 = wave; r0 < j.rows; r0 += NW * UR) {
+      f32x4_t u4[UR], g4[UR];
+      u32x2_t h2[UR];
+      float rs[UR];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int row = wm * (BM / 2) + mi * 32 + r;
-      const bool ok = row < j.rows;
-      const int64_t grow = static_cast<int64_t>(j.row0) + (ok ? row : 0);
-      float asum = 0.0f;
-      if (ok) {
-        const float rs = cl.rowscale ? cl.rowscale[grow] : 1.0f;
+      for (int u = 0; u < UR; ++u) {
+        const int row = r0 + NW * u;
+        const int64_t grow = static_cast<int64_t>(j.row0) + row;
+        u4[u] = g4[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        h2[u] = u32x2_t{0u, 0u};
+        rs[u] = 1.0f;
+        if (row < j.rows) {
+          if (cl.rowscale) rs[u] = cl.rowscale[grow];
+          if (cok) {
+            u4[u] = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + col);
+            g4[u] = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + N + col);
+            h2[u] = *reinterpret_cast<const u32x2_t *>(hp + grow * N + col);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const int row = r0 + NW * u;
+        if (row >= j.rows) break;  // wave-uniform
+        const int64_t grow = static_cast<int64_t>(j.row0) + row;
+        const f32x4_t acc4 = *reinterpret_cast<const f32x4_t *>(stg + row * SLD + 4 * lane);
+        float du[4], dg[4], asum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dh = rs[u] * acc4[e];
+          const float gt = g4[u][e];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+          du[e] = dh * (gt * sg);
+          dg[e] = dh * u4[u][e] * (sg * (1.0f + gt * (1.0f - sg)));
+          const uint32_t hw = h2[u][e >> 1];
+          asum += dh * __uint_as_float((e & 1) ? (hw & 0xffff0000u) : (hw << 16));
+        }
+        if (cok) {
+          u32x2_t o;
+          o[0] = pack_bf16x2(du[0], du[1]);
+          o[1] = pack_bf16x2(du[2], du[3]);
+          *reinterpret_cast<u32x2_t *>(D + grow * ldc + col) = o;
+          o[0] = pack_bf16x2(dg[0], dg[1]);
+          o[1] = pack_bf16x2(dg[2], dg[3]);
+          *reinterpret_cast<u32x2_t *>(D + grow * ldc + N + col) = o;
+        } else {
+          asum = 0.0f;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) asum += __shfl_xor(asum, o, kWave);
+        if (cl.apart && lane == 0) cl.apart[grow * cl.apart_ld + j.nt] = asum;
+      }
+    }
+  } else if constexpr (kGemmStagedStore) {
+    // modes 1, 3 (fp32 rows) and 4 (weight gradient, layer dtype): the tile
+    // goes through the idle LDS ring (as in mode 2) in chunks of CH rows that
+    // fit there; each wave then writes whole row segments (lane l: columns
+    // 4 l .. 4 l + 3), instead of one row per lane.
+    using OT = std::conditional_t<MODE == 4, uint16_t, float>;
+    constexpr int OB = sizeof(OT);
+    constexpr int LD = BN + 16 / OB;  // staged row stride in elements (16 B pad)
+    constexpr int RING = NST * (BM + BN) * BK * 2;
+    constexpr int CH = BM * LD * OB <= RING ? BM : (BM / 2) * LD * OB <= RING ? BM / 2 : BM / 4;
+    static_assert(CH * LD * OB <= RING && CH % 32 == 0 && BM % CH == 0, "staged chunk fits");
+    OT *stg = reinterpret_cast<OT *>(sA0);
+    OT *C = static_cast<OT *>(Cv);
+    if constexpr (MODE == 4) C += static_cast<int64_t>(j.g < a.E ? j.g : 0) * cl.strideC;
+    const int col = j.nt * BN + 4 * lane;
+    const bool cok = col < N;
+#pragma unroll 1
+    for (int ch = 0; ch < BM / CH && ch * CH < j.rows; ++ch) {
+      static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
+        constexpr int mi = decltype(Mv)::value;
+        const int rb = wm * (BM / 2) + mi * 32;
+        if (rb / CH != ch) return;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = j.nt * BN + wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
-            if (col >= N) continue;
-            const f32x4_t u4 = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + col);
-            const f32x4_t g4 = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + N + col);
-            const u32x2_t h2 = *reinterpret_cast<const u32x2_t *>(hp + grow * N + col);
-            float du[4], dg[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float dh = rs * acc[mi][ni][4 * q + e];
-              const float gt = g4[e];
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
-              du[e] = dh * (gt * sg);
-              dg[e] = dh * u4[e] * (sg * (1.0f + gt * (1.0f - sg)));
-              const uint32_t hw = h2[e >> 1];
-              const float hv = __uint_as_float((e & 1) ? (hw & 0xffff0000u) : (hw << 16));
-              asum += dh * hv;
+            OT *p = stg + (rb - ch * CH + r) * LD + wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
+            if constexpr (MODE == 4) {
+              u32x2_t o;
+              o[0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
+              o[1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+              *reinterpret_cast<u32x2_t *>(p) = o;
+            } else {
+              *reinterpret_cast<f32x4_t *>(p) =
+                  f32x4_t{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                          acc[mi][ni][4 * q + 3]};
             }
-            u32x2_t o;
-            o[0] = pack_bf16x2(du[0], du[1]);
-            o[1] = pack_bf16x2(du[2], du[3]);
-            *reinterpret_cast<u32x2_t *>(D + grow * ldc + col) = o;
-            o[0] = pack_bf16x2(dg[0], dg[1]);
-            o[1] = pack_bf16x2(dg[2], dg[3]);
-            *reinterpret_cast<u32x2_t *>(D + grow * ldc + N + col) = o;
           }
+      });
+      __syncthreads();
+      const int nr = min(CH, j.rows - ch * CH);
+#pragma unroll 4
+      for (int rl = wave; rl < nr; rl += NW) {
+        OT *dst = C + (static_cast<int64_t>(j.row0) + ch * CH + rl) * ldc + col;
+        const OT *src = stg + rl * LD + 4 * lane;
+        if (cok) {
+          if constexpr (MODE == 4)
+            *reinterpret_cast<u32x2_t *>(dst) = *reinterpret_cast<const u32x2_t *>(src);
+          else
+            *reinterpret_cast<f32x4_t *>(dst) = *reinterpret_cast<const f32x4_t *>(src);
+        }
       }
-      // lanes l and l ^ 32 hold the same row
-      asum += __shfl_xor(asum, 32, kWave);
-      if (cl.apart && ok && g == 0) cl.apart[grow * cl.apart_ld + j.nt * WN + wn] = asum;
+      __syncthreads();
     }
   } else if constexpr (MODE == 4) {
     uint16_t *C = static_cast<uint16_t *>(Cv) + static_cast<int64_t>(j.g < a.E ? j.g : 0) * cl.strideC;
@@ -676,10 +769,14 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int BN = kGemmBN;
   constexpr int AE = BM * BK / 8, BE = BN * BK / 8;  // 16-byte chunks per stage
   static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
-  __shared__ u32x4_t sA0[AE], sB0[BE], sA1[AE], sB1[BE];
-  __shared__ u32x4_t sA2[NST > 2 ? AE : 1], sB2[NST > 2 ? BE : 1];
-  __shared__ u32x4_t sA3[NST > 3 ? AE : 1], sB3[NST > 3 ? BE : 1];
-  __shared__ u32x4_t sA4[NST > 4 ? AE : 1], sB4[NST > 4 ? BE : 1];
+  // one array: stage s holds A at (AE + BE) s and B right after it; the
+  // whole ring is reused by the epilogues that stage their tile in LDS
+  __shared__ u32x4_t smem[NST * (AE + BE)];
+  u32x4_t *sA0 = smem, *sB0 = smem + AE;
+  u32x4_t *sA1 = smem + (AE + BE), *sB1 = sA1 + AE;
+  u32x4_t *sA2 = NST > 2 ? smem + 2 * (AE + BE) : smem, *sB2 = NST > 2 ? sA2 + AE : smem;
+  u32x4_t *sA3 = NST > 3 ? smem + 3 * (AE + BE) : smem, *sB3 = NST > 3 ? sA3 + AE : smem;
+  u32x4_t *sA4 = NST > 4 ? smem + 4 * (AE + BE) : smem, *sB4 = NST > 4 ? sA4 + AE : smem;
 
   TileJob j;
   if constexpr (MODE == 4) {
@@ -887,15 +984,14 @@ static int col_tiles_host(int N, int BN, bool upgate) {
 }
 
 // mode 0 ([up; gate]) and mode 3 run the default tile; modes 1 and 2 (the
-// down projection's shapes: fewer k steps) split each listed row tile.
+// down projection's shapes) split each listed row tile.
 static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtype, int mode,
                               hipStream_t s) {
   const int BN = dtype == kBF16 ? kGemmBN : kGemmF32BN;
   const bool stream = dtype == kBF16 && tile_rows == kGemmStreamBM;
   const bool upgate = mode == 0;
-  const bool down_like = mode == 1 || mode == 2;
   a.NTn = std::max(col_tiles_host(a.cls[0].N, BN, upgate), col_tiles_host(a.cls[1].N, BN, upgate));
-  a.split = dtype == kBF16 && down_like && !stream ? kGemmDownSplit : 1;
+  a.split = dtype != kBF16 || stream ? 1 : mode == 1 ? kGemmDownSplit : mode == 2 ? kDgradDownSplit : 1;
   a.sub_rows = a.split > 1 ? kGemmBM / a.split : 1 << 30;
   const int64_t work = static_cast<int64_t>(max_tiles) * a.split * a.NTn;
   const unsigned grid = static_cast<unsigned>((work + 7) / 8 * 8);
@@ -916,7 +1012,7 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
         break;
       case 2:
         if (stream) HI3_LAUNCH(2, kGemmStreamBM, 64, kGemmStreamStages);
-        else HI3_LAUNCH(2, DBM, 64, kGemmDownStages);
+        else HI3_LAUNCH(2, kGemmBM / kDgradDownSplit, 64, kDgradDownStages);
         break;
       default:
         if (stream) HI3_LAUNCH(3, kGemmStreamBM, 64, kGemmStreamStages);
@@ -967,8 +1063,8 @@ hipError_t launch_gemm_wgrad(const GemmArgs &a0, int E, int dtype, hipStream_t s
   const int64_t grid = a.wg_shared_blocks + routed;
   if (grid == 0) return hipSuccess;
   if (dtype == kBF16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<4, kGemmBN, 64, 2, kGemmWN>), dim3(static_cast<unsigned>(grid)),
-                       dim3(128 * kGemmWN), 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, kGemmBN, kWgradBK, kWgradStages, kGemmWN>),
+                       dim3(static_cast<unsigned>(grid)), dim3(128 * kGemmWN), 0, s, a);
   else
     hipLaunchKernelGGL(gemm_f32_kernel<4>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
   return hipGetLastError();
