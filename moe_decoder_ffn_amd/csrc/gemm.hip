@@ -533,7 +533,91 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     if (kc + decltype(S)::value < nk) step(S, kc + decltype(S)::value);
   });
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 && kGemmStagedStore) {
+    // h = SiLU(g) u (the layer dtype), and with ug also u and g (fp32),
+    // written through the idle LDS ring (see mode 2): first the BM x BN/2 h
+    // tile, then u and g in chunks of UGR rows; each wave writes whole row
+    // segments.
+    const int Ih = N / 2;
+    constexpr int HC = BN / 2;         // columns of the h tile
+    constexpr int HLD = HC + 8;        // staged h row stride (bf16, 16 B pad)
+    constexpr int ULD = HC + 4;        // staged u / g row stride (fp32, 16 B pad)
+    constexpr int RING = NST * (BM + BN) * BK * 2;
+    constexpr int UGR = 2 * 64 * ULD * 4 <= RING ? 64 : 32;
+    static_assert(BM * HLD * 2 <= RING && 2 * UGR * ULD * 4 <= RING && NI == 2 * (NI / 2),
+                  "staged h / ug tiles fit in the LDS ring");
+    uint16_t *C = static_cast<uint16_t *>(Cv);
+    float *ug = cl.ug;
+    uint16_t *sh = reinterpret_cast<uint16_t *>(sA0);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int p = 0; p < NI / 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float hv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float u = acc[mi][p][4 * q + e];
+            const float gt = acc[mi][p + NI / 2][4 * q + e];
+            // SiLU(g) * u = g * u / (1 + exp(-g))
+            hv[e] = gt * u * __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+          }
+          u32x2_t o;
+          o[0] = pack_bf16x2(hv[0], hv[1]);
+          o[1] = pack_bf16x2(hv[2], hv[3]);
+          const int row = wm * (BM / 2) + mi * 32 + r;
+          const int c = wn * (HC / WN) + p * 32 + 8 * q + 4 * g;
+          *reinterpret_cast<u32x2_t *>(sh + row * HLD + c) = o;
+        }
+    __syncthreads();
+    // two rows per wave instruction: lanes 0-31 one row, 32-63 the next;
+    // lane l takes columns 4 (l % 32) .. + 3
+    const int hcol = j.nt * HC + 4 * (lane & 31);
+    const bool hok = hcol < Ih;
+#pragma unroll 4
+    for (int rl = 2 * wave + (lane >> 5); rl < j.rows; rl += 2 * NW) {
+      if (hok)
+        *reinterpret_cast<u32x2_t *>(C + (static_cast<int64_t>(j.row0) + rl) * ldc + hcol) =
+            *reinterpret_cast<const u32x2_t *>(sh + rl * HLD + 4 * (lane & 31));
+    }
+    if (ug) {
+      float *su = reinterpret_cast<float *>(sA0);
+      float *sgt = su + UGR * ULD;
+#pragma unroll 1
+      for (int ch = 0; ch < BM / UGR && ch * UGR < j.rows; ++ch) {
+        __syncthreads();
+        static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
+          constexpr int mi = decltype(Mv)::value;
+          const int rb = wm * (BM / 2) + mi * 32;
+          if (rb / UGR != ch) return;
+#pragma unroll
+          for (int p = 0; p < NI / 2; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int o = (rb - ch * UGR + r) * ULD + wn * (HC / WN) + p * 32 + 8 * q + 4 * g;
+              *reinterpret_cast<f32x4_t *>(su + o) =
+                  f32x4_t{acc[mi][p][4 * q], acc[mi][p][4 * q + 1], acc[mi][p][4 * q + 2],
+                          acc[mi][p][4 * q + 3]};
+              *reinterpret_cast<f32x4_t *>(sgt + o) =
+                  f32x4_t{acc[mi][p + NI / 2][4 * q], acc[mi][p + NI / 2][4 * q + 1],
+                          acc[mi][p + NI / 2][4 * q + 2], acc[mi][p + NI / 2][4 * q + 3]};
+            }
+        });
+        __syncthreads();
+        const int nr = min(UGR, j.rows - ch * UGR);
+#pragma unroll 2
+        for (int rl = 2 * wave + (lane >> 5); rl < nr; rl += 2 * NW) {
+          if (!hok) continue;
+          float *ur = ug + (static_cast<int64_t>(j.row0) + ch * UGR + rl) * N;
+          *reinterpret_cast<f32x4_t *>(ur + hcol) =
+              *reinterpret_cast<const f32x4_t *>(su + rl * ULD + 4 * (lane & 31));
+          *reinterpret_cast<f32x4_t *>(ur + Ih + hcol) =
+              *reinterpret_cast<const f32x4_t *>(sgt + rl * ULD + 4 * (lane & 31));
+        }
+      }
+    }
+  } else if constexpr (MODE == 0) {
     const int Ih = N / 2;
     uint16_t *C = static_cast<uint16_t *>(Cv);
     float *ug = cl.ug;
