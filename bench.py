@@ -264,6 +264,83 @@ def cpu_baseline_backward(wl, d, dout, K, target_s):
                       f"{total_t:.1f} s"}
 
 
+def train_bench(args, m, wl, d, dd, pad, stream):
+    """Times a training step of the layer: hi3_moe_forward_train (forward,
+    keeping the routes, u, g, h) then hi3_moe_backward_after_forward (all six
+    gradients without recomputing the forward)."""
+    import torch
+    sh = wl.shape
+    dout_h = wk.make_dout(wl, args.seed)
+    dout = torch.from_numpy(dout_h.view(np.int16)).cuda().view(torch.bfloat16) \
+        if sh.dtype == wk.BF16 else torch.from_numpy(dout_h).cuda()
+    x = dd["x"]
+    dt = x.dtype
+    out = torch.zeros_like(x)
+    idx = torch.empty((wl.T, sh.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((wl.T, sh.K), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((sh.E,), dtype=torch.int32, device="cuda")
+    dx = torch.zeros_like(x)
+    dwr = torch.empty((sh.E, sh.H), dtype=torch.float32, device="cuda")
+    dw13 = torch.empty((sh.E, 2 * sh.I, sh.H), dtype=dt, device="cuda")
+    dw2 = torch.empty((sh.E, sh.H, sh.I), dtype=dt, device="cuda")
+    dws13 = torch.empty((2 * sh.Is, sh.H), dtype=dt, device="cuda")
+    dws2 = torch.empty((sh.H, sh.Is), dtype=dt, device="cuda")
+    n = m.hi3_moe_backward_workspace_size(wl.T, sh.H, sh.E, sh.K, sh.I, sh.Is,
+                                          m.dtype_code(dt))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    w = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
+
+    def step():
+        m.hi3_moe_forward_train(x, *w, pad, sh.K, out, idx, wts, cnt, ws, stream)
+        m.hi3_moe_backward_after_forward(x, *w, pad, dout, sh.K, dx, dwr, dw13, dw2, dws13, dws2,
+                                         ws, stream)
+
+    hip = HipEvents()
+    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    ev = hip.create(3)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+    fwd_ms = bwd_ms = 0.0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        hip.hip.hipEventRecord(ev[0], ctypes.c_void_p(stream.cuda_stream))
+        m.hi3_moe_forward_train(x, *w, pad, sh.K, out, idx, wts, cnt, ws, stream)
+        hip.hip.hipEventRecord(ev[1], ctypes.c_void_p(stream.cuda_stream))
+        m.hi3_moe_backward_after_forward(x, *w, pad, dout, sh.K, dx, dwr, dw13, dw2, dws13, dws2,
+                                         ws, stream)
+        hip.hip.hipEventRecord(ev[2], ctypes.c_void_p(stream.cuda_stream))
+        fwd_ms += hip.elapsed_ms(ev[0], ev[1])
+        bwd_ms += hip.elapsed_ms(ev[1], ev[2])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    hip.destroy(ev)
+    log(f"[bench] {args.steps} timed steps done")
+    ms_per_step = elapsed * 1e3 / args.steps
+    gf = backward_gemm_flops(wl)
+    # algorithmic FLOP of a training step: the forward's GEMMs and twice them
+    flops = 3 * (gf["gemm_up_gate_recompute"] + gf["gemm_dgrad_down"])
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": "MoE-layer training-step tokens/s (forward + all gradients), 64e top-8, "
+                  "H=4096, 1 GPU",
+        "value": round(wl.T_valid / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if sh.dtype == wk.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "entry": "train", "T": wl.T, "T_valid": wl.T_valid,
+                   "H": sh.H, "E": sh.E, "K": sh.K, "I": sh.I, "I_shared": sh.Is,
+                   "seed": args.seed},
+        "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages": {"forward_train": {"us": round(fwd_ms / args.steps * 1e3, 1)},
+                   "backward_after_forward": {"us": round(bwd_ms / args.steps * 1e3, 1)}},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def backward_bench(args, m, wl, d, dd, pad, stream):
     """Times hi3_moe_backward per step (all six gradients), with per-stage
     HIP events; the roofline entry is the slowest GEMM stage."""
@@ -370,11 +447,12 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--entry", default="forward",
-                    choices=("forward", "norm_residual", "backward"),
+                    choices=("forward", "norm_residual", "backward", "train"),
                     help="forward: the layer (hi3_moe_forward); norm_residual: the layer "
                          "inside its block, h + layer(RMSNorm(h)) "
                          "(hi3_moe_forward_norm_residual); backward: all gradients of the "
-                         "layer (hi3_moe_backward)")
+                         "layer (hi3_moe_backward); train: hi3_moe_forward_train + "
+                         "hi3_moe_backward_after_forward")
     args = ap.parse_args()
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy)
@@ -423,9 +501,10 @@ def main():
     if args.entry == "norm_residual":
         norm_residual_bench(args, m, wl, d, dd, pad, ws, stream)
         return
-    if args.entry == "backward":
+    if args.entry in ("backward", "train"):
         del ws
-        backward_bench(args, m, wl, d, dd, pad, stream)
+        (backward_bench if args.entry == "backward" else train_bench)(args, m, wl, d, dd, pad,
+                                                                     stream)
         return
 
     for _ in range(args.warmup):

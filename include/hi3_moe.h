@@ -275,6 +275,38 @@ int hi3_moe_backward_instrumented(const void *x, const float *w_router,
                                   void *workspace, size_t workspace_bytes,
                                   void *hip_stream, void *const *stage_events);
 
+/*
+ * A training step's pair (the pages' fine-tuning, model-coverage page,
+ * "Train"): hi3_moe_forward_train is hi3_moe_forward (same arguments, same
+ * out, routes and counts) that also leaves in its workspace the routes, the
+ * dispatch maps, u and g (fp32) and h; hi3_moe_backward_after_forward is
+ * hi3_moe_backward that takes them from there instead of recomputing the
+ * router, the dispatch and the [up; gate] projection. The workspace must be
+ * at least hi3_moe_backward_workspace_size(...) bytes for both calls; the
+ * second call must get the same workspace, the same x, weights, pad_mask and
+ * sizes, with nothing written to any of them in between (the library cannot
+ * check this: it keeps no state). Results are bit-identical to
+ * hi3_moe_forward and hi3_moe_backward on the same inputs.
+ */
+int hi3_moe_forward_train(const void *x, const float *w_router, const void *w_up_gate,
+                          const void *w_down, const void *w_shared_up_gate,
+                          const void *w_shared_down, const uint8_t *pad_mask, int64_t T,
+                          int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                          int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                          void *hip_stream);
+
+int hi3_moe_backward_after_forward(const void *x, const float *w_router,
+                                   const void *w_up_gate, const void *w_down,
+                                   const void *w_shared_up_gate, const void *w_shared_down,
+                                   const uint8_t *pad_mask, const void *dout, int64_t T,
+                                   int32_t H, int32_t E, int32_t K, int32_t I,
+                                   int32_t I_shared, int32_t dtype, void *dx,
+                                   float *dw_router, void *dw_up_gate, void *dw_down,
+                                   void *dw_shared_up_gate, void *dw_shared_down,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *hip_stream);
+
 /* Static name of backward stage i (0 <= i < HI3_NUM_BWD_STAGES), else "?". */
 const char *hi3_moe_backward_stage_name(int stage);
 

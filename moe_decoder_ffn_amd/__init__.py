@@ -38,6 +38,8 @@ EXPORTED = (
     "hi3_moe_backward",
     "hi3_moe_backward_instrumented",
     "hi3_moe_backward_stage_name",
+    "hi3_moe_forward_train",
+    "hi3_moe_backward_after_forward",
     "hi3_moe_stage_name",
     "hi3_moe_status_string",
 )
@@ -79,6 +81,10 @@ def _load():
     lib.hi3_moe_backward.restype = ctypes.c_int
     lib.hi3_moe_backward_instrumented.argtypes = bwd + [P]
     lib.hi3_moe_backward_instrumented.restype = ctypes.c_int
+    lib.hi3_moe_forward_train.argtypes = fwd
+    lib.hi3_moe_forward_train.restype = ctypes.c_int
+    lib.hi3_moe_backward_after_forward.argtypes = bwd
+    lib.hi3_moe_backward_after_forward.restype = ctypes.c_int
     lib.hi3_moe_backward_stage_name.argtypes = [ctypes.c_int]
     lib.hi3_moe_backward_stage_name.restype = ctypes.c_char_p
     lib.hi3_moe_stage_name.argtypes = [ctypes.c_int]
@@ -235,6 +241,23 @@ def hi3_moe_backward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_ga
         x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, dout, K, dx,
         dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down, workspace, stream),
         arr))
+
+
+def hi3_moe_forward_train(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                          pad_mask, K, out, topk_idx=None, topk_w=None, expert_counts=None,
+                          workspace=None, stream=None):
+    _check(lib.hi3_moe_forward_train(*_forward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
+        topk_idx, topk_w, expert_counts, workspace, stream)))
+
+
+def hi3_moe_backward_after_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate,
+                                   w_shared_down, pad_mask, dout, K, dx, dw_router, dw_up_gate,
+                                   dw_down, dw_shared_up_gate, dw_shared_down, workspace,
+                                   stream=None):
+    _check(lib.hi3_moe_backward_after_forward(*_backward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, dout, K, dx,
+        dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down, workspace, stream)))
 
 
 def hi3_moe_backward_stage_name(i) -> str:

@@ -56,7 +56,8 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
                  const void *w_shared_down, const uint8_t *pad_mask, int64_t T, int32_t H,
                  int32_t E, int32_t K, int32_t I, int32_t Is, int32_t dtype, void *out,
                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts, void *workspace,
-                 size_t workspace_bytes, void *hip_stream, void *const *events) {
+                 size_t workspace_bytes, void *hip_stream, void *const *events,
+                 bool save = false) {
   if (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !out)
     return HI3_E_NULL;
   int st = check_sizes(T, H, E, K, I, Is, dtype, true);
@@ -67,7 +68,9 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   st = all_aligned({x, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate,
                     w_shared_down, pad_mask, out, topk_idx, topk_w, expert_counts, workspace});
   if (st != HI3_OK) return st;
-  const Plan p = make_plan(T, H, E, K, I, Is, dtype);
+  // save: the backward's layout, so that hi3_moe_backward_after_forward finds
+  // the routes, slot maps, u, g and h where it reads them
+  const Plan p = make_plan(T, H, E, K, I, Is, dtype, save);
   if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -80,8 +83,8 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     resid = x;
     x = at(p.xn);
   }
-  int32_t *idx = topk_idx ? topk_idx : static_cast<int32_t *>(at(p.idx));
-  float *wts = topk_w ? topk_w : static_cast<float *>(at(p.wts));
+  int32_t *idx = topk_idx && !save ? topk_idx : static_cast<int32_t *>(at(p.idx));
+  float *wts = topk_w && !save ? topk_w : static_cast<float *>(at(p.wts));
   int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
   int32_t *blkval = static_cast<int32_t *>(at(p.blkval));
   int32_t *slotof = static_cast<int32_t *>(at(p.slotof));
@@ -116,6 +119,10 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   GemmArgs up{};
   up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
   up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
+  if (save) {
+    up.cls[0].ug = static_cast<float *>(at(p.ug));
+    up.cls[1].ug = static_cast<float *>(at(p.ugs));
+  }
   up.tiles = tiles;
   up.gto = gto;
   up.E = E;
@@ -134,6 +141,10 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                  slotof, vidx, wts, pad_mask, T, H, K, out, resid};
   HI3_TRY(launch_combine(ca, dtype, s));
+  if (save && topk_idx)
+    HI3_TRY(hipMemcpyAsync(topk_idx, idx, size_t(T) * K * 4, hipMemcpyDeviceToDevice, s));
+  if (save && topk_w)
+    HI3_TRY(hipMemcpyAsync(topk_w, wts, size_t(T) * K * 4, hipMemcpyDeviceToDevice, s));
   rec.at(6);
   return rec.ok ? HI3_OK : HI3_E_HIP;
 }
@@ -149,7 +160,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
                   int32_t K, int32_t I, int32_t Is, int32_t dtype, void *dx, float *dw_router,
                   void *dw_up_gate, void *dw_down, void *dw_shared_up_gate,
                   void *dw_shared_down, void *workspace, size_t workspace_bytes,
-                  void *hip_stream, void *const *events) {
+                  void *hip_stream, void *const *events, bool reuse = false) {
   int st = check_sizes(T, H, E, K, I, Is, dtype, true);
   if (st != HI3_OK) return st;
   // with no rows the inputs are not read (they may be NULL)
@@ -192,32 +203,42 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   const int32_t *misc = static_cast<const int32_t *>(at(p.misc));
   Recorder rec{events, s};
 
-  // 0-2: routes, offsets, slots (as in the forward)
+  // 0-2: routes, offsets, slots (as in the forward); 3: the [up; gate]
+  // projection again: h as the forward stores it, u and g in fp32. After
+  // hi3_moe_forward_train all of this is already in the workspace.
   rec.at(0);
-  RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K, p.Epad,
-                idx, wts, blkcnt, blkval};
-  HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
+  if (!reuse) {
+    RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
+                  p.Epad, idx, wts, blkcnt, blkval};
+    HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
+  }
   rec.at(1);
-  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
-              static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
-              static_cast<int32_t *>(at(p.eoff)), nullptr,
-              static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
-              static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
-  HI3_TRY(launch_scan(sa, s));
+  if (!reuse) {
+    ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
+                static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
+                static_cast<int32_t *>(at(p.eoff)), nullptr,
+                static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
+                static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
+    HI3_TRY(launch_scan(sa, s));
+  }
   rec.at(2);
-  ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm, slotof, vtok, vidx};
-  HI3_TRY(launch_scatter(sc, s));
-  // 3: [up; gate] projection again: h as the forward stores it, u and g in fp32
+  if (!reuse) {
+    ScatterArgs sc{idx, pad_mask, static_cast<int32_t *>(at(p.blkoff)),
+                   static_cast<int32_t *>(at(p.blkvoff)), T, E, K, perm, slotof, vtok, vidx};
+    HI3_TRY(launch_scatter(sc, s));
+  }
   rec.at(3);
-  GemmArgs up{};
-  up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
-  up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
-  up.cls[0].ug = static_cast<float *>(at(p.ug));
-  up.cls[1].ug = static_cast<float *>(at(p.ugs));
-  up.tiles = tiles;
-  up.gto = gto;
-  up.E = E;
-  HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
+  if (!reuse) {
+    GemmArgs up{};
+    up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
+    up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
+    up.cls[0].ug = static_cast<float *>(at(p.ug));
+    up.cls[1].ug = static_cast<float *>(at(p.ugs));
+    up.tiles = tiles;
+    up.gto = gto;
+    up.E = E;
+    HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
+  }
   // 4: x and w dout by slot; x and dout by real row when there is padding
   rec.at(4);
   const bool compact = pad_mask != nullptr;
@@ -483,6 +504,33 @@ int hi3_moe_backward_instrumented(const void *x, const float *w_router, const vo
                        dout, T, H, E, K, I, I_shared, dtype, dx, dw_router, dw_up_gate, dw_down,
                        dw_shared_up_gate, dw_shared_down, workspace, workspace_bytes, hip_stream,
                        stage_events);
+}
+
+int hi3_moe_forward_train(const void *x, const float *w_router, const void *w_up_gate,
+                          const void *w_down, const void *w_shared_up_gate,
+                          const void *w_shared_down, const uint8_t *pad_mask, int64_t T,
+                          int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                          int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                          void *hip_stream) {
+  return forward_impl(x, nullptr, 0.0f, w_router, w_up_gate, w_down, w_shared_up_gate,
+                      w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
+                      topk_w, expert_counts, workspace, workspace_bytes, hip_stream, nullptr,
+                      true);
+}
+
+int hi3_moe_backward_after_forward(const void *x, const float *w_router, const void *w_up_gate,
+                                   const void *w_down, const void *w_shared_up_gate,
+                                   const void *w_shared_down, const uint8_t *pad_mask,
+                                   const void *dout, int64_t T, int32_t H, int32_t E, int32_t K,
+                                   int32_t I, int32_t I_shared, int32_t dtype, void *dx,
+                                   float *dw_router, void *dw_up_gate, void *dw_down,
+                                   void *dw_shared_up_gate, void *dw_shared_down,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return backward_impl(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                       dout, T, H, E, K, I, I_shared, dtype, dx, dw_router, dw_up_gate, dw_down,
+                       dw_shared_up_gate, dw_shared_down, workspace, workspace_bytes, hip_stream,
+                       nullptr, true);
 }
 
 const char *hi3_moe_backward_stage_name(int stage) {

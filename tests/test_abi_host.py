@@ -255,3 +255,23 @@ def test_backward_workspace_size_and_stage_names():
     args = [P, P, P, P, P, P, None, P, 64, 256, 8, 2, 128, 128, 1, P, P, P, P, P, P, P,
             1 << 40, None]
     assert f(*args, None) == m.HI3_E_NULL
+
+
+def test_training_pair_validation():
+    need_b = m.hi3_moe_backward_workspace_size(64, 256, 8, 2, 128, 128, m.HI3_BF16)
+    need_f = m.hi3_moe_workspace_size(64, 256, 8, 2, 128, 128, m.HI3_BF16)
+    assert need_f < need_b
+    f = m.lib.hi3_moe_forward_train
+    args = [P, P, P, P, P, P, None, 64, 256, 8, 2, 128, 128, 1, P, None, None, None, P]
+    # the forward's own workspace is too small: the backward's layout is needed
+    assert f(*args, need_f, None) == m.HI3_E_WORKSPACE
+    assert f(*args, need_b - 1, None) == m.HI3_E_WORKSPACE
+    bad = list(args)
+    bad[0] = None
+    assert f(*bad, need_b, None) == m.HI3_E_NULL
+    g = m.lib.hi3_moe_backward_after_forward
+    bargs = [P, P, P, P, P, P, None, P, 64, 256, 8, 2, 128, 128, 1, P, P, P, P, P, P, P]
+    assert g(*bargs, need_b - 1, None) == m.HI3_E_WORKSPACE
+    bad = list(bargs)
+    bad[7] = None
+    assert g(*bad, need_b, None) == m.HI3_E_NULL

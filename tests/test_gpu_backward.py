@@ -87,6 +87,10 @@ SMALL = [
     ("bf16_e16_pad", wk.BF16, 256, 16, 4, 320, 128, (300, 129, 7), 300),
     ("bf16_e64_k8_stream", wk.BF16, 512, 64, 8, 128, 256, (600,), None),
     ("bf16_one_token", wk.BF16, 256, 8, 2, 128, 128, (1,), None),
+    # 64 experts, top-8, 256 rows per expert: the full-size tile
+    # configuration (256-row tiles, split dh tiles, several output tiles per
+    # weight gradient)
+    ("bf16_e64_k8_default_tiles", wk.BF16, 512, 64, 8, 256, 256, (2048,), None),
 ]
 
 
@@ -157,6 +161,40 @@ def test_backward_no_rows_zero_weight_gradients():
     for k, v in g.items():
         if k != "dx":
             assert v.numel() > 0 and bool((v == 0).all()), k
+
+
+@pytest.mark.parametrize("dtype,seq,plen", [(wk.BF16, (300, 129, 7), 300),
+                                             (wk.F32, (150, 37), 160)])
+def test_training_pair_bit_identical(dtype, seq, plen):
+    # hi3_moe_forward_train + hi3_moe_backward_after_forward give exactly what
+    # hi3_moe_forward and hi3_moe_backward give on the same inputs
+    import moe_decoder_ffn_amd as m
+    _say(f"[backward] training pair {dtype}")
+    d, pad = make_case(dtype, 256, 16, 4, 192, 128, seq, plen)
+    dd = upload(d)
+    padd = to_dev(pad)
+    x = dd["x"]
+    T, H = x.shape
+    E, K, I, Is = 16, 4, 192, 128
+    w = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
+    out1, idx1, w1, c1 = m.moe_forward(x, *w, K, pad_mask=padd, return_routes=True)
+    g1 = m.moe_backward(x, *w, dd["dout"], K, pad_mask=padd)
+    nws = m.hi3_moe_backward_workspace_size(T, H, E, K, I, Is, m.dtype_code(x.dtype))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    out2 = torch.zeros_like(x)
+    idx2 = torch.empty_like(idx1)
+    w2 = torch.empty_like(w1)
+    c2 = torch.empty_like(c1)
+    m.hi3_moe_forward_train(x, *w, padd, K, out2, idx2, w2, c2, ws)
+    g2 = {k: torch.zeros_like(v) if k == "dx" else torch.empty_like(v) for k, v in g1.items()}
+    m.hi3_moe_backward_after_forward(x, *w, padd, dd["dout"], K, g2["dx"], g2["dw_router"],
+                                     g2["dw_up_gate"], g2["dw_down"], g2["dw_shared_up_gate"],
+                                     g2["dw_shared_down"], ws)
+    torch.cuda.synchronize()
+    for a, b in ((out1, out2), (idx1, idx2), (w1, w2), (c1, c2)):
+        assert torch.equal(a, b)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
 
 
 @pytest.mark.parametrize("name", ["image_1024"])
