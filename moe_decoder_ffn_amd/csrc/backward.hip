@@ -154,19 +154,23 @@ hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s)
 }
 
 // dWr[e, h] = sum over expert e's slots s (ascending) of dl[s] x_s[h], in
-// fp32. Block (e, column block): each thread owns two adjacent columns; the
-// slot loop is unrolled so several rows are in flight.
+// fp32, in two fixed-order steps so that an expert with many rows does not
+// serialise: (1) one block per (row tile of the grouped GEMMs' list, 512
+// columns) sums its tile's slots into part[tile]; (2) one block per
+// (expert, 512 columns) sums its tiles' parts in list order. Each thread
+// owns two adjacent columns; the slot loop is unrolled so several rows are
+// in flight.
 template <int DT>
-__global__ __launch_bounds__(256) void dw_router_kernel(const float *__restrict__ dls,
-                                                        const void *__restrict__ xs,
-                                                        const int32_t *__restrict__ eoff, int H,
-                                                        float *__restrict__ dwr) {
-  const int e = blockIdx.x;
+__global__ __launch_bounds__(256) void dw_router_part_kernel(
+    const float *__restrict__ dls, const void *__restrict__ xs, const int4 *__restrict__ tiles,
+    const int32_t *__restrict__ gto, int E, int H, float *__restrict__ part) {
+  const int tj = blockIdx.x;
+  if (tj >= gto[E]) return;  // only the routed experts' tiles
   const int h = (blockIdx.y * 256 + threadIdx.x) * 2;
   if (h >= H) return;
-  const int s0 = eoff[e], s1 = eoff[e + 1];
+  const int4 tile = tiles[tj];
+  const int s0 = tile.y, s1 = tile.y + tile.z;
   float a0 = 0.0f, a1 = 0.0f;
-  int s = s0;
   auto load = [&](int r, float &v0, float &v1) {
     if (DT == kBF16) {
       const uint32_t w = *reinterpret_cast<const uint32_t *>(
@@ -179,6 +183,7 @@ __global__ __launch_bounds__(256) void dw_router_kernel(const float *__restrict_
       v1 = p[1];
     }
   };
+  int s = s0;
   for (; s + 8 <= s1; s += 8) {
     float v0[8], v1[8], d[8];
 #pragma unroll
@@ -198,17 +203,36 @@ __global__ __launch_bounds__(256) void dw_router_kernel(const float *__restrict_
     a0 = fmaf(dls[s], v0, a0);
     a1 = fmaf(dls[s], v1, a1);
   }
-  dwr[static_cast<int64_t>(e) * H + h] = a0;
-  dwr[static_cast<int64_t>(e) * H + h + 1] = a1;
+  *reinterpret_cast<float2 *>(part + static_cast<int64_t>(tj) * H + h) = make_float2(a0, a1);
 }
 
-hipError_t launch_dw_router(const float *dls, const void *xs, const int32_t *eoff, int E, int H,
-                            int dtype, float *dwr, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(E), static_cast<unsigned>((H / 2 + 255) / 256));
+__global__ __launch_bounds__(256) void dw_router_sum_kernel(const float *__restrict__ part,
+                                                            const int32_t *__restrict__ gto,
+                                                            int H, float *__restrict__ dwr) {
+  const int e = blockIdx.x;
+  const int h = (blockIdx.y * 256 + threadIdx.x) * 2;
+  if (h >= H) return;
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int tj = gto[e]; tj < gto[e + 1]; ++tj) {
+    const float2 v = *reinterpret_cast<const float2 *>(part + static_cast<int64_t>(tj) * H + h);
+    a0 += v.x;
+    a1 += v.y;
+  }
+  *reinterpret_cast<float2 *>(dwr + static_cast<int64_t>(e) * H + h) = make_float2(a0, a1);
+}
+
+hipError_t launch_dw_router(const float *dls, const void *xs, const int4 *tiles,
+                            const int32_t *gto, int max_tiles, int E, int H, int dtype,
+                            float *part, float *dwr, hipStream_t s) {
+  const unsigned cb = static_cast<unsigned>((H / 2 + 255) / 256);
+  const dim3 g1(static_cast<unsigned>(max_tiles), cb), g2(static_cast<unsigned>(E), cb);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(dw_router_kernel<kBF16>, grid, dim3(256), 0, s, dls, xs, eoff, H, dwr);
+    hipLaunchKernelGGL(dw_router_part_kernel<kBF16>, g1, dim3(256), 0, s, dls, xs, tiles, gto, E,
+                       H, part);
   else
-    hipLaunchKernelGGL(dw_router_kernel<kF32>, grid, dim3(256), 0, s, dls, xs, eoff, H, dwr);
+    hipLaunchKernelGGL(dw_router_part_kernel<kF32>, g1, dim3(256), 0, s, dls, xs, tiles, gto, E,
+                       H, part);
+  hipLaunchKernelGGL(dw_router_sum_kernel, g2, dim3(256), 0, s, part, gto, H, dwr);
   return hipGetLastError();
 }
 

@@ -208,6 +208,7 @@ struct Plan {
   size_t apart;   // [T*K, P] fp32: partial sums of dh * h
   size_t dls;     // [T*K] fp32: logit gradient by slot
   size_t wslot;   // [T*K] fp32: routing weight by slot
+  size_t dwrpart; // [max_tiles, H] fp32: router weight gradient per row tile
   size_t zrow;    // 512 bytes of zeros
   int P;
   size_t total;
@@ -277,6 +278,7 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
     p.apart = take(TK * p.P * 4);
     p.dls = take(TK * 4);
     p.wslot = take(TK * 4);
+    p.dwrpart = take(static_cast<size_t>(p.max_tiles) * H * 4);
     p.zrow = take(512);
   }
   p.total = o;
@@ -456,8 +458,10 @@ struct BwdCombineArgs {
 };
 hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);
 
-hipError_t launch_dw_router(const float *dls, const void *xs, const int32_t *eoff, int E, int H,
-                            int dtype, float *dwr, hipStream_t s);
+// part: [max_tiles, H] fp32 scratch (per row tile of the grouped GEMMs' list).
+hipError_t launch_dw_router(const float *dls, const void *xs, const int4 *tiles,
+                            const int32_t *gto, int max_tiles, int E, int H, int dtype,
+                            float *part, float *dwr, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 }  // namespace hi3

@@ -289,7 +289,9 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   HI3_TRY(launch_bwd_combine(ca, dtype, s));
   // 8: router weight gradient
   rec.at(8);
-  if (dw_router) HI3_TRY(launch_dw_router(dls, at(p.xs), eoff, E, H, dtype, dw_router, s));
+  if (dw_router)
+    HI3_TRY(launch_dw_router(dls, at(p.xs), tiles, gto, p.max_tiles, E, H, dtype,
+                             static_cast<float *>(at(p.dwrpart)), dw_router, s));
   // 9, 10: expert weight gradients
   HI3_TRY(launch_zero(at(p.zrow), 512, s));
   rec.at(9);

@@ -49,9 +49,9 @@ def gpu_backward(d, K, pad=None):
     return {k: to_host(v) for k, v in g.items()}, to_host(idx), to_host(w)
 
 
-def make_case(dtype, H, E, K, I, Is, seq, plen, seed=7, rscale=5.0):
+def make_case(dtype, H, E, K, I, Is, seq, plen, seed=7, rscale=5.0, skew=False):
     shape = wk.LayerShape(H=H, E=E, K=K, I=I, Is=Is, dtype=dtype)
-    wl = wk.custom(shape, seq, plen)
+    wl = wk.custom(shape, seq, plen, skew=skew)
     d = wk.make_inputs(wl, seed)
     d["w_router"] = d["w_router"] * np.float32(rscale)
     d["dout"] = wk.make_dout(wl, seed)
@@ -100,6 +100,16 @@ def test_backward_small_all_elements(name, dtype, H, E, K, I, Is, seq, plen):
     d, pad = make_case(dtype, H, E, K, I, Is, seq, plen)
     g, errs, near = check_all(d, K, pad, dtype)
     _say(f"  max err / RMS: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+def test_backward_skewed_router():
+    # the skewed router of the skew_16k workload at a small size: four
+    # experts take about half of all routes (reductions several tiles deep),
+    # four get almost none
+    _say("[backward] skewed router")
+    d, pad = make_case(wk.BF16, 512, 16, 4, 256, 256, (1500,), None, rscale=1.0, skew=True)
+    g, errs, near = check_all(d, 4, pad, wk.BF16)
+    _say("  max err / RMS: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
 
 
 def test_backward_unused_experts_zero_and_deterministic():
