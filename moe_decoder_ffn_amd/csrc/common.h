@@ -76,13 +76,20 @@ constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
 static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
 constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
 // Backward GEMMs: the gradient through the down projection (mode 2) runs each
-// listed row tile as HI3_DGRAD_DOWN_SPLIT blocks; the weight gradients
-// (mode 4) use k steps of HI3_WGRAD_BK rows and HI3_WGRAD_STAGES stages.
+// listed row tile as HI3_DGRAD_DOWN_SPLIT blocks; the gradient through
+// [up; gate] (mode 3) and the weight gradients (mode 4) use the given k step
+// and stage counts.
 #ifndef HI3_DGRAD_DOWN_SPLIT
 #define HI3_DGRAD_DOWN_SPLIT 2
 #endif
 #ifndef HI3_DGRAD_DOWN_STAGES
 #define HI3_DGRAD_DOWN_STAGES 3
+#endif
+#ifndef HI3_DGRAD_UP_BK
+#define HI3_DGRAD_UP_BK 64
+#endif
+#ifndef HI3_DGRAD_UP_STAGES
+#define HI3_DGRAD_UP_STAGES 2
 #endif
 #ifndef HI3_WGRAD_BK
 #define HI3_WGRAD_BK 32
@@ -98,9 +105,18 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
 constexpr int kDgradDownSplit = HI3_DGRAD_DOWN_SPLIT;
 constexpr int kDgradDownStages = HI3_DGRAD_DOWN_STAGES;
+// Rows per wave in flight in the mode-2 epilogue (its u, g, h reads).
+#ifndef HI3_DGRAD_EPI_ROWS
+#define HI3_DGRAD_EPI_ROWS 4
+#endif
+constexpr int kDgradEpilogueRows = HI3_DGRAD_EPI_ROWS;
+constexpr int kDgradUpBK = HI3_DGRAD_UP_BK;
+constexpr int kDgradUpStages = HI3_DGRAD_UP_STAGES;
 constexpr int kWgradBK = HI3_WGRAD_BK;
 constexpr int kWgradStages = HI3_WGRAD_STAGES;
-static_assert(kGemmBM % kDgradDownSplit == 0 && (kGemmBM / kDgradDownSplit) % 64 == 0,
+// (the dh epilogue stages its whole tile in LDS: at most 128 rows)
+static_assert(kGemmBM % kDgradDownSplit == 0 && (kGemmBM / kDgradDownSplit) % 64 == 0 &&
+                  kGemmBM / kDgradDownSplit <= 128,
               "dgrad tile rows");
 // fp32 grouped GEMM tile.
 constexpr int kGemmF32BM = 64;

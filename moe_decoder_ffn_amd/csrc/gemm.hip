@@ -244,9 +244,10 @@ struct StageRing {
 // 256 weight rows (down: 256 output columns; [up; gate]: 128 up rows + the
 // matching 128 gate rows); k step BK; NST-stage ring of LDS buffers filled by
 // direct global -> LDS copies: while stage k is multiplied, the copies of
-// the next NST - 1 stages are in flight. Each stage lives in its own LDS
-// arrays. With WN = 4 (512 threads) two waves share each SIMD, so one
-// wave's LDS waits overlap the other's MFMAs.
+// the next NST - 1 stages are in flight. The stages are slices of one LDS
+// array, which the epilogues reuse once the ring is idle. With WN = 4 (512
+// threads) two waves share each SIMD, so one wave's LDS waits overlap the
+// other's MFMAs.
 // Wave (wm, wn) owns rows [BM/2 wm, BM/2 (wm + 1)) and NI 32-row weight
 // sub-tiles; with [up; gate] the first NI/2 are up rows and the last NI/2
 // the gate rows of the same columns, so each lane holds u and g of the same
@@ -692,7 +693,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     const uint16_t *hp = static_cast<const uint16_t *>(cl.hsave);
     const int col = j.nt * BN + 4 * lane;
     const bool cok = col < N;
-    constexpr int UR = 4;  // rows per wave in flight
+    constexpr int UR = kDgradEpilogueRows;  // rows per wave in flight
 #pragma unroll 1
     for (int r0 = wave; r0 < j.rows; r0 += NW * UR) {
       f32x4_t u4[UR], g4[UR];
@@ -869,13 +870,16 @@ __global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
   } else {
     if (!resolve_job<MODE, BN>(a, j)) return;
     constexpr int BMS = BM / 2, BM3 = BM / 4 * 3;
-    if constexpr (BMS >= 64 && BMS % 64 == 0) {
+    // a body exists where its A stage splits into whole 1 KiB copies per wave
+    constexpr bool whole = [] (int bm) constexpr { return bm * BK * 2 % (1024 * 2 * WN) == 0; }(BM3);
+    constexpr bool whole_s = [] (int bm) constexpr { return bm * BK * 2 % (1024 * 2 * WN) == 0; }(BMS);
+    if constexpr (BMS >= 64 && BMS % 64 == 0 && whole_s) {
       if (j.rows <= BMS) {
         gemm_tile<MODE, BMS, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
         return;
       }
     }
-    if constexpr (BM3 > BMS && BM3 % 64 == 0) {
+    if constexpr (BM3 > BMS && BM3 % 64 == 0 && whole) {
       if (j.rows <= BM3) {
         gemm_tile<MODE, BM3, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
         return;
@@ -1100,7 +1104,7 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
         break;
       default:
         if (stream) HI3_LAUNCH(3, kGemmStreamBM, 64, kGemmStreamStages);
-        else HI3_LAUNCH(3, kGemmBM, 64, kGemmStages);
+        else HI3_LAUNCH(3, kGemmBM, kDgradUpBK, kDgradUpStages);
         break;
     }
   } else {
