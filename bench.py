@@ -385,9 +385,11 @@ def backward_bench(args, m, wl, d, dd, pad, stream):
     elapsed = time.perf_counter() - t0
     log(f"[bench] {args.steps} timed steps done")
     stage_ms = np.zeros(ns)
+    step_ms = []
     for evs in evsets:
         for k in range(ns):
             stage_ms[k] += hip.elapsed_ms(evs[k], evs[k + 1])
+        step_ms.append(hip.elapsed_ms(evs[0], evs[ns]))
     stage_ms /= args.steps
     for evs in evsets:
         hip.destroy(evs)
@@ -430,6 +432,8 @@ def backward_bench(args, m, wl, d, dd, pad, stream):
                    "H": sh.H, "E": sh.E, "K": sh.K, "I": sh.I, "I_shared": sh.Is,
                    "seed": args.seed},
         "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "call_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "min": round(float(np.min(step_ms)), 4)},
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -524,9 +528,11 @@ def main():
     log(f"[bench] {args.steps} timed steps done")
 
     stage_ms = np.zeros(ns)
+    step_ms = []
     for evs in evsets:
         for s in range(ns):
             stage_ms[s] += hip.elapsed_ms(evs[s], evs[s + 1])
+        step_ms.append(hip.elapsed_ms(evs[0], evs[ns]))
     stage_ms /= args.steps
     for evs in evsets:
         hip.destroy(evs)
@@ -582,6 +588,9 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "T_valid": wl.T_valid, "H": sh.H,
                    "E": sh.E, "K": sh.K, "I": sh.I, "I_shared": sh.Is, "seed": args.seed},
         "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        # per call, first to last kernel on the stream (HIP events)
+        "call_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "min": round(float(np.min(step_ms)), 4)},
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
