@@ -235,3 +235,18 @@ def test_backward_full_size_sampled_rows(name):
     g2, _, _ = gpu_backward(d, K, pad)
     for k in g:
         assert np.array_equal(g[k], g2[k]), k
+    # linear in dout, exactly: doubling dout doubles every product and sum,
+    # and rounding commutes with a power-of-two scaling, so every gradient
+    # doubles bit for bit (a read of stale or uninitialised memory would not)
+    d2 = dict(d)
+    d2["dout"] = wk.f32_to_bf16_bits(wk.bf16_bits_to_f32(d["dout"]) * np.float32(2.0))
+    g3, _, _ = gpu_backward(d2, K, pad)
+    for k in g:
+        a = g[k].astype(np.float64) if g[k].dtype != np.uint16 else wk.bf16_bits_to_f32(g[k])
+        b = g3[k].astype(np.float64) if g3[k].dtype != np.uint16 else wk.bf16_bits_to_f32(g3[k])
+        assert np.array_equal(2 * a, b), k
+    # the logit gradient of each token sums to zero (renormalised weights do
+    # not change when every selected logit moves together), so the rows of
+    # the router's weight gradient cancel up to rounding
+    dwr = g["dw_router"].astype(np.float64)
+    assert np.abs(dwr.sum(axis=0)).max() <= 1e-3 * np.abs(dwr).sum(axis=0).max()
