@@ -112,6 +112,14 @@ constexpr int kDgradDownStages = HI3_DGRAD_DOWN_STAGES;
 constexpr int kDgradEpilogueRows = HI3_DGRAD_EPI_ROWS;
 constexpr int kDgradUpBK = HI3_DGRAD_UP_BK;
 constexpr int kDgradUpStages = HI3_DGRAD_UP_STAGES;
+// Weight-gradient output tile rows: 256 (8 waves, one block per CU) or 128
+// (4 waves, two blocks per CU, so one block's prologue and epilogue overlap
+// the other's main loop).
+#ifndef HI3_WGRAD_BM
+#define HI3_WGRAD_BM 128
+#endif
+constexpr int kWgradBM = HI3_WGRAD_BM;
+constexpr int kWgradWN = kWgradBM == 256 ? kGemmWN : 2;
 constexpr int kWgradBK = HI3_WGRAD_BK;
 constexpr int kWgradStages = HI3_WGRAD_STAGES;
 // (the dh epilogue stages its whole tile in LDS: at most 128 rows)

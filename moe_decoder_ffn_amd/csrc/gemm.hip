@@ -277,7 +277,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   constexpr int MI = BM / 64;               // 32-row sub-tiles per wave
   constexpr int NI = BN / WN / 32;          // 32-column sub-tiles per wave
   static_assert(BN == 256 && BM % 64 == 0 && BM <= 256 && (BK == 32 || BK == 64), "tile");
-  static_assert(!AT || BM == 256, "k-major A tile");
+  static_assert(!AT || BM == 128 || BM == 256, "k-major A tile");
   static_assert(!(AT || BT) || BK == 32 || BK == 64, "k-major k step");
   static_assert(NST >= 2 && NST <= 5, "stages");
   static_assert(BM * BK * 2 % (1024 * NW) == 0 && BN * BK * 2 % (1024 * NW) == 0,
@@ -849,8 +849,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 // with at most 3 BM / 4 rows the three-quarter body (when those heights are
 // multiples of 64). The bodies are straight-line code over the same LDS
 // ring. Mode 4 jobs are whole output tiles (one body).
-template <int MODE, int BM, int BK, int NST, int WN>
-__global__ __launch_bounds__(128 * WN) void gemm_bf16_kernel(GemmArgs a) {
+// OCC: blocks per CU the register allocation must allow (the 128-row
+// weight-gradient tile runs two per CU).
+template <int MODE, int BM, int BK, int NST, int WN, int OCC = 1>
+__global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int BN = kGemmBN;
   constexpr int AE = BM * BK / 8, BE = BN * BK / 8;  // 16-byte chunks per stage
   static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
@@ -1142,17 +1144,19 @@ hipError_t launch_gemm_dgrad_up_gate(const GemmArgs &a, int max_tiles, int tile_
 // Mode 4: a class whose C is null is skipped.
 hipError_t launch_gemm_wgrad(const GemmArgs &a0, int E, int dtype, hipStream_t s) {
   GemmArgs a = a0;
-  const int T = dtype == kBF16 ? kGemmBN : kGemmF32BN;  // square output tiles
+  const int TM = dtype == kBF16 ? kWgradBM : kGemmF32BM;  // output tile rows
+  const int TN = dtype == kBF16 ? kGemmBN : kGemmF32BN;   // output tile columns
   auto tiles_of = [&](const GemmClass &c) {
-    return static_cast<int64_t>((c.M + T - 1) / T) * ((c.N + T - 1) / T);
+    return static_cast<int64_t>((c.M + TM - 1) / TM) * ((c.N + TN - 1) / TN);
   };
   a.wg_shared_blocks = a.cls[1].C ? static_cast<int>((tiles_of(a.cls[1]) + 7) / 8 * 8) : 0;
   const int64_t routed = a.cls[0].C ? 8 * tiles_of(a.cls[0]) * ((E + 7) / 8) : 0;
   const int64_t grid = a.wg_shared_blocks + routed;
   if (grid == 0) return hipSuccess;
   if (dtype == kBF16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<4, kGemmBN, kWgradBK, kWgradStages, kGemmWN>),
-                       dim3(static_cast<unsigned>(grid)), dim3(128 * kGemmWN), 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, kWgradBM, kWgradBK, kWgradStages, kWgradWN,
+                                         kWgradBM == 128 ? 2 : 1>),
+                       dim3(static_cast<unsigned>(grid)), dim3(128 * kWgradWN), 0, s, a);
   else
     hipLaunchKernelGGL(gemm_f32_kernel<4>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
   return hipGetLastError();
