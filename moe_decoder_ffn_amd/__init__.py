@@ -352,3 +352,51 @@ def moe_backward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down
                      dout, K, outs["dx"], outs["dw_router"], outs["dw_up_gate"], outs["dw_down"],
                      outs["dw_shared_up_gate"], outs["dw_shared_down"], workspace)
     return {k: v for k, v in outs.items() if v is not None}
+
+
+class MoEFunction(torch.autograd.Function):
+    """The layer as an autograd function: forward runs hi3_moe_forward_train,
+    backward runs hi3_moe_backward_after_forward on the workspace the forward
+    filled (kept on the context between the two). Gradients: x, the router
+    weight (fp32), and the four expert weights; pad_mask and K get none.
+    Inputs must not change between forward and backward (as for any saved
+    tensor)."""
+
+    @staticmethod
+    def forward(ctx, x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, K,
+                pad_mask=None):
+        T, H = x.shape
+        E = w_router.shape[0]
+        I = w_up_gate.shape[1] // 2
+        Is = w_shared_up_gate.shape[0] // 2
+        n = hi3_moe_backward_workspace_size(T, H, E, K, I, Is, dtype_code(x.dtype))
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+        out = torch.zeros_like(x)
+        hi3_moe_forward_train(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                              pad_mask, K, out, workspace=ws)
+        ctx.save_for_backward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                              pad_mask)
+        ctx.ws, ctx.K = ws, K
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask = \
+            ctx.saved_tensors
+        dout = dout.contiguous()
+        need = ctx.needs_input_grad
+        g = [torch.zeros_like(x) if need[0] else None]
+        for i, wt in ((1, w_router), (2, w_up_gate), (3, w_down), (4, w_shared_up_gate),
+                      (5, w_shared_down)):
+            g.append(torch.empty_like(wt) if need[i] else None)
+        hi3_moe_backward_after_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate,
+                                       w_shared_down, pad_mask, dout, ctx.K, *g, ctx.ws)
+        ctx.ws = None
+        return (*g, None, None)
+
+
+def moe_layer(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, K,
+              pad_mask=None):
+    """Differentiable layer output (MoEFunction.apply)."""
+    return MoEFunction.apply(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                             K, pad_mask)

@@ -207,6 +207,34 @@ def test_training_pair_bit_identical(dtype, seq, plen):
         assert torch.equal(g1[k], g2[k]), k
 
 
+def test_autograd_function_matches_entry_points():
+    # MoEFunction: out equals hi3_moe_forward's, and the gradients from
+    # torch.autograd equal hi3_moe_backward's, bit for bit; unrequested
+    # gradients are not computed
+    import moe_decoder_ffn_amd as m
+    _say("[backward] autograd function")
+    d, pad = make_case(wk.BF16, 256, 16, 4, 192, 128, (300, 129, 7), 300)
+    dd = upload(d)
+    padd = to_dev(pad)
+    names = ("x", "w_router", "w13", "w2", "ws13", "ws2")
+    leaves = {k: dd[k].clone().requires_grad_(True) for k in names}
+    out = m.moe_layer(*(leaves[k] for k in names), 4, padd)
+    out.backward(dd["dout"])
+    ref_out = m.moe_forward(*(dd[k] for k in names), 4, pad_mask=padd)
+    ref = m.moe_backward(*(dd[k] for k in names), dd["dout"], 4, pad_mask=padd)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    keys = {"x": "dx", "w_router": "dw_router", "w13": "dw_up_gate", "w2": "dw_down",
+            "ws13": "dw_shared_up_gate", "ws2": "dw_shared_down"}
+    for k, r in keys.items():
+        assert torch.equal(leaves[k].grad, ref[r]), k
+    # only x requires a gradient
+    x = dd["x"].clone().requires_grad_(True)
+    (gx,) = torch.autograd.grad(m.moe_layer(x, *(dd[k] for k in names[1:]), 4, padd),
+                                x, dd["dout"])
+    assert torch.equal(gx, ref["dx"])
+
+
 @pytest.mark.parametrize("name", ["image_1024"])
 def test_backward_full_size_sampled_rows(name):
     # full size, the launch configuration the benchmark times: dx of sampled
