@@ -87,6 +87,8 @@ SMALL = [
     ("bf16_e16_pad", wk.BF16, 256, 16, 4, 320, 128, (300, 129, 7), 300),
     ("bf16_e64_k8_stream", wk.BF16, 512, 64, 8, 128, 256, (600,), None),
     ("bf16_one_token", wk.BF16, 256, 8, 2, 128, 128, (1,), None),
+    # H and I not multiples of 256: partial column tiles everywhere
+    ("bf16_h320_i192", wk.BF16, 320, 8, 3, 192, 320, (400,), None),
     # 64 experts, top-8, 256 rows per expert: the full-size tile
     # configuration (256-row tiles, split dh tiles, several output tiles per
     # weight gradient)
