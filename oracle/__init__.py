@@ -43,6 +43,9 @@ def _load():
         lib.orc_moe_backward.restype = None
         lib.orc_rmsnorm.argtypes = [P, i32, P, ctypes.c_double, P, i64, i64, P]
         lib.orc_rmsnorm.restype = None
+        lib.orc_rmsnorm_backward.argtypes = [P, i32, P, ctypes.c_double, P, i64, i64, P, P, P,
+                                             P, P, P]
+        lib.orc_rmsnorm_backward.restype = None
         lib.orc_round_bf16_array.argtypes = [P, i64, P]
         lib.orc_round_bf16_array.restype = None
         _lib = lib
@@ -254,3 +257,54 @@ def moe_backward(x, w_router, w13, w2, ws13, ws2, dout, K, pad_mask=None, idx=No
     res = {k: v for k, v in outs.items() if v is not None}
     res.update({"m_" + k: v for k, v in mags.items() if v is not None})
     return res
+
+
+def rmsnorm_backward(x, weight, g, eps=1e-5, pad_mask=None, mg=None):
+    """Backward of rmsnorm (moe_oracle.c, orc_rmsnorm_backward): g = dL/dxn
+    (fp64 [T,H]). Returns dict(dx [T,H] fp64 (NaN rows for padding), dw [H]),
+    and with mg (magnitudes of g) also m_dx and m_dw."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    weight = np.ascontiguousarray(weight)
+    T, H = x.shape
+    assert weight.shape == (H,) and weight.dtype == x.dtype
+    g = np.ascontiguousarray(np.nan_to_num(np.asarray(g, np.float64)))
+    assert g.shape == (T, H)
+    pad = None if pad_mask is None else np.ascontiguousarray(pad_mask, np.uint8)
+    mgc = None if mg is None else np.ascontiguousarray(np.nan_to_num(np.asarray(mg, np.float64)))
+    dx = np.full((T, H), np.nan)
+    dw = np.zeros(H)
+    mdx = np.full((T, H), np.nan) if mg is not None else None
+    mdw = np.zeros(H) if mg is not None else None
+    lib.orc_rmsnorm_backward(_ptr(x), dt, _ptr(weight), float(eps), _ptr(pad), T, H, _ptr(g),
+                             _ptr(mgc), _ptr(dx), _ptr(dw), _ptr(mdx), _ptr(mdw))
+    res = {"dx": dx, "dw": dw}
+    if mg is not None:
+        res.update({"m_dx": mdx, "m_dw": mdw})
+    return res
+
+
+def moe_norm_residual_backward(h, norm_weight, w_router, w13, w2, ws13, ws2, dout, K,
+                               eps=1e-5, pad_mask=None, idx=None, w=None, magnitudes=False):
+    """Gradients of L = sum over real rows of dout . out for the block's
+    out = h + layer(RMSNorm(h)) (routes held fixed): the layer's backward at
+    the normalised rows, then RMSNorm's, plus dout through the residual.
+    Returns dh [T,H] (NaN rows for padding), dnorm_weight [H], and the layer's
+    weight gradients (dw_router, dw13, dw2, dws13, dws2); with magnitudes=True
+    also m_<name> for each (m_dh is that of the RMSNorm term: dout is
+    exact)."""
+    h = np.ascontiguousarray(h)
+    xn = rmsnorm(h, norm_weight, eps, pad_mask)
+    lb = moe_backward(xn, w_router, w13, w2, ws13, ws2, dout, K, pad_mask=pad_mask, idx=idx,
+                      w=w, magnitudes=magnitudes)
+    nb = rmsnorm_backward(h, norm_weight, lb["dx"], eps, pad_mask,
+                          mg=lb["m_dx"] if magnitudes else None)
+    res = {k: v for k, v in lb.items() if k not in ("dx", "m_dx")}
+    res["dh"] = _as_f64(np.ascontiguousarray(dout)) + nb["dx"]
+    res["dnorm_weight"] = nb["dw"]
+    if magnitudes:
+        res["m_dh"] = nb["m_dx"]
+        res["m_dnorm_weight"] = nb["m_dw"]
+    return res
+

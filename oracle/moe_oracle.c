@@ -412,6 +412,60 @@ void orc_rmsnorm(const void *x, int dtype, const void *weight, double eps,
 }
 
 /*
+ * Backward of the block's RMSNorm (fine-tuning the decoder block:
+ * model-coverage page, "Train"; the forward is orc_rmsnorm). Given
+ * g = dL/dxn (fp64 [T,H]) on the real rows: the derivative of
+ * xn = weight * x * r(x), r = (mean over h of x^2 + eps)^(-1/2), taken at the
+ * forward's fp32 r, with the roundings of n and xn passed straight through:
+ *   dweight[h] += g[t,h] * n[t,h]  (n = the forward's dtype(x r); rows in
+ *                                   ascending order)
+ *   v_h = weight[h] g[t,h],  s = sum over h of x_h v_h
+ *   dx[t,h] = r v_h - r^3 x_h s / H
+ * (d r / d x_h = -r^3 x_h / H). With mg (the magnitudes of g, nullable), mdx
+ * and mdw (nullable) receive the matching magnitudes:
+ *   mdx = r |w_h| mg_h + r^3 |x_h| (sum over h of |x_h w_h| mg_h) / H,
+ *   mdw += mg_h |n_h|.
+ * Padding rows are neither read nor written. Single-threaded.
+ */
+void orc_rmsnorm_backward(const void *x, int dtype, const void *weight, double eps,
+                          const uint8_t *pad, int64_t T, int64_t H, const double *g,
+                          const double *mg, double *dx, double *dw, double *mdx, double *mdw)
+{
+    if (dw) memset(dw, 0, sizeof(double) * (size_t)H);
+    if (mdw) memset(mdw, 0, sizeof(double) * (size_t)H);
+    for (int64_t t = 0; t < T; t++) {
+        if (pad && pad[t])
+            continue;
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            double v = elem(x, dtype, t * H + h);
+            ss += v * v;
+        }
+        float m = (float)(ss / (double)H);
+        float d = m + (float)eps;
+        double r = (double)(float)(1.0 / sqrt((double)d));
+        double s = 0.0, ms = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            double xv = elem(x, dtype, t * H + h);
+            double wv = elem(weight, dtype, h);
+            double n = round_dtype((double)(float)(xv * r), dtype);
+            double gv = g[t * H + h];
+            if (dw) dw[h] += gv * n;
+            if (mdw && mg) mdw[h] += mg[t * H + h] * fabs(n);
+            s += xv * (wv * gv);
+            if (mg) ms += fabs(xv * wv) * mg[t * H + h];
+        }
+        for (int64_t h = 0; h < H; h++) {
+            double xv = elem(x, dtype, t * H + h);
+            double wv = elem(weight, dtype, h);
+            if (dx) dx[t * H + h] = r * (wv * g[t * H + h]) - r * r * r * xv * s / (double)H;
+            if (mdx && mg)
+                mdx[t * H + h] = r * fabs(wv) * mg[t * H + h] + r * r * r * fabs(xv) * ms / (double)H;
+        }
+    }
+}
+
+/*
  * Backward pass of the layer (for the pages' fine-tuning: HunyuanImage-3.0
  * model-coverage page, "Train": LoRA and full fine-tuning of the MoE
  * decoder). Given dout = dL/dout for the real rows, the gradients of
