@@ -276,6 +276,36 @@ int hi3_moe_backward_instrumented(const void *x, const float *w_router,
                                   void *hip_stream, void *const *stage_events);
 
 /*
+ * Backward of the block entry point hi3_moe_forward_norm_residual
+ * (out = h + layer(RMSNorm(h)); model API page, HunyuanImage3Block, a
+ * pre-norm layer; the pages' fine-tuning, model-coverage page, "Train"):
+ * the layer's gradients at the normalised rows as in hi3_moe_backward, then
+ * RMSNorm's, at the forward's fp32 r with the roundings of n and xn passed
+ * straight through, plus the residual:
+ *   g = dL/dxn (the layer's dx, kept in fp32), dx_norm = r w g - r^3 h s / H
+ *   with s = sum over the row of h w g, dh = dout + dx_norm (rounded once),
+ *   dnorm_weight = sum over real rows of g * dtype(h r).
+ * Arguments as in hi3_moe_backward, plus:
+ *   h             [T, H] dtype: the block input (takes the place of x).
+ *   norm_weight   [H] dtype, must not be NULL (unless T = 0).
+ *   eps           finite, >= 0.
+ *   dh            [T, H] dtype out or NULL (takes the place of dx); padding
+ *                 rows are not written.
+ *   dnorm_weight  [H] dtype out or NULL.
+ * Workspace: hi3_moe_backward_workspace_size(...) bytes.
+ */
+int hi3_moe_backward_norm_residual(const void *h, const void *norm_weight, float eps,
+                                   const float *w_router, const void *w_up_gate,
+                                   const void *w_down, const void *w_shared_up_gate,
+                                   const void *w_shared_down, const uint8_t *pad_mask,
+                                   const void *dout, int64_t T, int32_t H, int32_t E,
+                                   int32_t K, int32_t I, int32_t I_shared, int32_t dtype,
+                                   void *dh, void *dnorm_weight, float *dw_router,
+                                   void *dw_up_gate, void *dw_down, void *dw_shared_up_gate,
+                                   void *dw_shared_down, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+
+/*
  * A training step's pair (the pages' fine-tuning, model-coverage page,
  * "Train"): hi3_moe_forward_train is hi3_moe_forward (same arguments, same
  * out, routes and counts) that also leaves in its workspace the routes, the

@@ -40,6 +40,7 @@ EXPORTED = (
     "hi3_moe_backward_stage_name",
     "hi3_moe_forward_train",
     "hi3_moe_backward_after_forward",
+    "hi3_moe_backward_norm_residual",
     "hi3_moe_stage_name",
     "hi3_moe_status_string",
 )
@@ -81,6 +82,8 @@ def _load():
     lib.hi3_moe_backward.restype = ctypes.c_int
     lib.hi3_moe_backward_instrumented.argtypes = bwd + [P]
     lib.hi3_moe_backward_instrumented.restype = ctypes.c_int
+    lib.hi3_moe_backward_norm_residual.argtypes = [P, P, f32] + bwd[1:15] + [P, P] + bwd[16:]
+    lib.hi3_moe_backward_norm_residual.restype = ctypes.c_int
     lib.hi3_moe_forward_train.argtypes = fwd
     lib.hi3_moe_forward_train.restype = ctypes.c_int
     lib.hi3_moe_backward_after_forward.argtypes = bwd
@@ -260,6 +263,19 @@ def hi3_moe_backward_after_forward(x, w_router, w_up_gate, w_down, w_shared_up_g
         dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down, workspace, stream)))
 
 
+def hi3_moe_backward_norm_residual(h, norm_weight, eps, w_router, w_up_gate, w_down,
+                                   w_shared_up_gate, w_shared_down, pad_mask, dout, K, dh,
+                                   dnorm_weight, dw_router, dw_up_gate, dw_down,
+                                   dw_shared_up_gate, dw_shared_down, workspace, stream=None):
+    a = _backward_args(h, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                       dout, K, dh, dw_router, dw_up_gate, dw_down, dw_shared_up_gate,
+                       dw_shared_down, workspace, stream)
+    # a: (x, w_router, ..., dtype, dx, dw_router, ...): insert the norm weight
+    # and eps after h, and dnorm_weight after dh
+    _check(lib.hi3_moe_backward_norm_residual(a[0], _ptr(norm_weight), float(eps), *a[1:16],
+                                              _ptr(dnorm_weight), *a[16:]))
+
+
 def hi3_moe_backward_stage_name(i) -> str:
     return lib.hi3_moe_backward_stage_name(i).decode()
 
@@ -325,6 +341,32 @@ def moe_forward_norm_residual(h, norm_weight, w_router, w_up_gate, w_down, w_sha
     if return_routes:
         return out, idx, w, counts
     return out
+
+
+def moe_backward_norm_residual(h, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate,
+                               w_shared_down, dout, K, eps=1e-5, pad_mask=None, workspace=None):
+    """All gradients of the block entry point with torch-allocated outputs:
+    dict(dh, dnorm_weight, dw_router, dw_up_gate, dw_down, dw_shared_up_gate,
+    dw_shared_down); padding rows of dh are zero."""
+    T, H = h.shape
+    E = w_router.shape[0]
+    I = w_up_gate.shape[1] // 2
+    Is = w_shared_up_gate.shape[0] // 2
+    dev, dt = h.device, h.dtype
+    g = {"dh": torch.zeros_like(h), "dnorm_weight": torch.empty_like(norm_weight),
+         "dw_router": torch.empty((E, H), dtype=torch.float32, device=dev),
+         "dw_up_gate": torch.empty_like(w_up_gate), "dw_down": torch.empty_like(w_down),
+         "dw_shared_up_gate": torch.empty_like(w_shared_up_gate),
+         "dw_shared_down": torch.empty_like(w_shared_down)}
+    if workspace is None:
+        n = hi3_moe_backward_workspace_size(T, H, E, K, I, Is, dtype_code(dt))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    hi3_moe_backward_norm_residual(h, norm_weight, eps, w_router, w_up_gate, w_down,
+                                   w_shared_up_gate, w_shared_down, pad_mask, dout, K, g["dh"],
+                                   g["dnorm_weight"], g["dw_router"], g["dw_up_gate"],
+                                   g["dw_down"], g["dw_shared_up_gate"], g["dw_shared_down"],
+                                   workspace)
+    return g
 
 
 def moe_backward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, dout, K,

@@ -78,7 +78,8 @@ hipError_t launch_bwd_gather(const BwdGatherArgs &a, int dtype, hipStream_t s) {
 // One block per token: a_k from the partials (in column-block order),
 // dl_k = a_k - w_k sum_j a_j (stored by slot for the router's weight
 // gradient), then dx = sum_k dxs[slot_k] + dxsh + sum_k dl_k Wr[e_k], summed
-// in fp32 in that order and rounded once to the layer dtype.
+// in fp32 in that order and rounded once to the layer dtype (or kept in fp32
+// when the block's RMSNorm backward follows).
 template <int DT>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
   __shared__ float ak[kMaxE], dl[kMaxE];
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
     }
   }
   __syncthreads();
-  if (!a.dx) return;
+  if (!a.dx && !a.dx_f32) return;
   const int nq = a.H / 4;
   for (int q = threadIdx.x; q < nq; q += blockDim.x) {
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -132,7 +133,9 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdCombineArgs a) {
       acc[2] = fmaf(d, wr[2], acc[2]);
       acc[3] = fmaf(d, wr[3], acc[3]);
     }
-    if (DT == kBF16) {
+    if (a.dx_f32) {
+      reinterpret_cast<f32x4_t *>(a.dx_f32 + t * a.H)[q] = acc;
+    } else if (DT == kBF16) {
       u32x2_t o;
       o[0] = pack_bf16x2(acc[0], acc[1]);
       o[1] = pack_bf16x2(acc[2], acc[3]);

@@ -28,6 +28,8 @@ constexpr int kRouterTB = 32;
 constexpr int kRouterMaxSlices = 16;
 // Tokens per block of the bf16 router's logit kernel.
 constexpr int kRouterMT = 128;
+// Rows per partial sum of the RMSNorm weight gradient (block backward).
+constexpr int kNormBwdRows = 64;
 
 // bf16 grouped GEMM tiles: rows x 256 weight rows x k step, LDS stages.
 // The row-tile list holds tiles of HI3_GEMM_BM rows (the up/gate tile); the
@@ -233,6 +235,9 @@ struct Plan {
   size_t dls;     // [T*K] fp32: logit gradient by slot
   size_t wslot;   // [T*K] fp32: routing weight by slot
   size_t dwrpart; // [max_tiles, H] fp32: router weight gradient per row tile
+  size_t dxn;     // [T, H] fp32: dL/dxn (block backward)
+  size_t rrow;    // [T] fp32: RMSNorm r per row (block backward)
+  size_t nwpart;  // [ceil(T / kNormBwdRows), H] fp32: norm weight gradient partials
   size_t zrow;    // 512 bytes of zeros
   int P;
   size_t total;
@@ -303,6 +308,9 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
     p.dls = take(TK * 4);
     p.wslot = take(TK * 4);
     p.dwrpart = take(static_cast<size_t>(p.max_tiles) * H * 4);
+    p.dxn = take(T * H * 4);
+    p.rrow = take(T * 4);
+    p.nwpart = take(static_cast<size_t>((T + kNormBwdRows - 1) / kNormBwdRows) * H * 4);
     p.zrow = take(512);
   }
   p.total = o;
@@ -423,6 +431,25 @@ struct NormArgs {
 };
 hipError_t launch_rmsnorm(const NormArgs &a, int dtype, hipStream_t s);
 
+// Backward of the block's RMSNorm plus its residual: per real row, r as the
+// forward computes it, dx = r w g - r^3 x (sum x w g) / H, dh = dout + dx
+// (rounded once to the layer dtype); dweight = sum over rows of g n.
+struct NormBwdArgs {
+  const void *x;       // [T,H] dtype: the block input h
+  const void *weight;  // [H] dtype
+  const uint8_t *pad;  // [T] or null
+  int64_t T;
+  int H;
+  float eps;
+  const float *g;      // [T,H] fp32: dL/dxn
+  const void *dout;    // [T,H] dtype: dL/dout (the residual's share)
+  void *dh;            // [T,H] dtype out, nullable
+  float *r;            // [T] fp32 scratch: r of each real row
+  float *part;         // [ceil(T / kNormBwdRows), H] fp32 scratch
+  void *dweight;       // [H] dtype out, nullable
+};
+hipError_t launch_rmsnorm_backward(const NormBwdArgs &a, int dtype, hipStream_t s);
+
 // partial: [slices][T][E] fp32 scratch (one slice for fp32 layers).
 hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStream_t s);
 hipError_t launch_histogram(const int32_t *idx, const uint8_t *pad, int64_t T, int E,
@@ -479,6 +506,7 @@ struct BwdCombineArgs {
   int H, K;
   float *dls;            // [T*K] logit gradient by slot
   void *dx;              // nullable
+  float *dx_f32;         // nullable: dx kept in fp32 (by token) instead of dx
 };
 hipError_t launch_bwd_combine(const BwdCombineArgs &a, int dtype, hipStream_t s);
 

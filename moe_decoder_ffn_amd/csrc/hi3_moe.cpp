@@ -160,21 +160,25 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
                   int32_t K, int32_t I, int32_t Is, int32_t dtype, void *dx, float *dw_router,
                   void *dw_up_gate, void *dw_down, void *dw_shared_up_gate,
                   void *dw_shared_down, void *workspace, size_t workspace_bytes,
-                  void *hip_stream, void *const *events, bool reuse = false) {
+                  void *hip_stream, void *const *events, bool reuse = false,
+                  const void *norm_weight = nullptr, float eps = 0.0f,
+                  void *dnorm_weight = nullptr) {
   int st = check_sizes(T, H, E, K, I, Is, dtype, true);
   if (st != HI3_OK) return st;
+  if (norm_weight && !eps_ok(eps)) return HI3_E_UNSUPPORTED;
   // with no rows the inputs are not read (they may be NULL)
   if (T > 0 &&
       (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !dout))
     return HI3_E_NULL;
   st = all_aligned({x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
                     dout, dx, dw_router, dw_up_gate, dw_down, dw_shared_up_gate, dw_shared_down,
-                    workspace});
+                    workspace, norm_weight, dnorm_weight});
   if (st != HI3_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const size_t es = dtype == HI3_BF16 ? 2 : 4;
   if (T == 0) {
     // no rows: every requested weight gradient is zero
+    HI3_TRY(launch_zero(dnorm_weight, dnorm_weight ? size_t(H) * es : 0, s));
     HI3_TRY(launch_zero(dw_router, dw_router ? size_t(E) * H * 4 : 0, s));
     HI3_TRY(launch_zero(dw_up_gate, dw_up_gate ? size_t(E) * 2 * I * H * es : 0, s));
     HI3_TRY(launch_zero(dw_down, dw_down ? size_t(E) * H * I * es : 0, s));
@@ -202,6 +206,19 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   const int32_t *counts = static_cast<const int32_t *>(at(p.counts));
   const int32_t *misc = static_cast<const int32_t *>(at(p.misc));
   Recorder rec{events, s};
+
+  // the block's backward: the layer runs on the normalised rows, and its dx
+  // (dL/dxn) stays in fp32 for RMSNorm's backward at the end
+  const void *h_in = x;
+  const bool norm = norm_weight != nullptr;
+  void *dh = dx;
+  if (norm) {
+    NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
+    HI3_TRY(launch_rmsnorm(na, dtype, s));
+    x = at(p.xn);
+    dx = nullptr;
+  }
+  const bool want_dxn = norm && (dh || dnorm_weight);
 
   // 0-2: routes, offsets, slots (as in the forward); 3: the [up; gate]
   // projection again: h as the forward stores it, u and g in fp32. After
@@ -267,7 +284,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   HI3_TRY(launch_gemm_dgrad_down(d2, p.max_tiles, p.BM, dtype, s));
   // 6: dx by slot / by real row = W13^T [du; dg]
   rec.at(6);
-  if (dx) {
+  if (dx || want_dxn) {
     GemmArgs d3{};
     d3.cls[0] = GemmClass{at(p.dd), 2 * I, nullptr, w_up_gate, int64_t{2} * I * H, at(p.y), H,
                           H, 2 * I};
@@ -285,7 +302,8 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   float *dls = static_cast<float *>(at(p.dls));
   BwdCombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                     static_cast<const float *>(at(p.apart)), p.P, slotof, idx, vidx, wts,
-                    w_router, pad_mask, T, H, K, dls, dx};
+                    w_router, pad_mask, T, H, K, dls, dx,
+                    want_dxn ? static_cast<float *>(at(p.dxn)) : nullptr};
   HI3_TRY(launch_bwd_combine(ca, dtype, s));
   // 8: router weight gradient
   rec.at(8);
@@ -332,6 +350,13 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   }
   HI3_TRY(launch_gemm_wgrad(w13, E, dtype, s));
   rec.at(11);
+  if (want_dxn) {
+    NormBwdArgs nb{h_in, norm_weight, pad_mask, T, H, eps,
+                   static_cast<const float *>(at(p.dxn)), dout, dh,
+                   static_cast<float *>(at(p.rrow)), static_cast<float *>(at(p.nwpart)),
+                   dnorm_weight};
+    HI3_TRY(launch_rmsnorm_backward(nb, dtype, s));
+  }
   return rec.ok ? HI3_OK : HI3_E_HIP;
 }
 
@@ -533,6 +558,22 @@ int hi3_moe_backward_after_forward(const void *x, const float *w_router, const v
                        dout, T, H, E, K, I, I_shared, dtype, dx, dw_router, dw_up_gate, dw_down,
                        dw_shared_up_gate, dw_shared_down, workspace, workspace_bytes, hip_stream,
                        nullptr, true);
+}
+
+int hi3_moe_backward_norm_residual(const void *h, const void *norm_weight, float eps,
+                                   const float *w_router, const void *w_up_gate,
+                                   const void *w_down, const void *w_shared_up_gate,
+                                   const void *w_shared_down, const uint8_t *pad_mask,
+                                   const void *dout, int64_t T, int32_t H, int32_t E, int32_t K,
+                                   int32_t I, int32_t I_shared, int32_t dtype, void *dh,
+                                   void *dnorm_weight, float *dw_router, void *dw_up_gate,
+                                   void *dw_down, void *dw_shared_up_gate, void *dw_shared_down,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (!norm_weight && T > 0) return HI3_E_NULL;
+  return backward_impl(h, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask,
+                       dout, T, H, E, K, I, I_shared, dtype, dh, dw_router, dw_up_gate, dw_down,
+                       dw_shared_up_gate, dw_shared_down, workspace, workspace_bytes, hip_stream,
+                       nullptr, false, norm_weight, eps, dnorm_weight);
 }
 
 const char *hi3_moe_backward_stage_name(int stage) {

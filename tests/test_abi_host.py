@@ -275,3 +275,21 @@ def test_training_pair_validation():
     bad = list(bargs)
     bad[7] = None
     assert g(*bad, need_b, None) == m.HI3_E_NULL
+
+
+def test_backward_norm_residual_validation():
+    f = m.lib.hi3_moe_backward_norm_residual
+    need = m.hi3_moe_backward_workspace_size(64, 256, 8, 2, 128, 128, m.HI3_BF16)
+
+    def call(**kw):
+        a = dict(h=P, nw=P, eps=1e-5, dout=P, T=64, dh=P, dnw=P, ws=P, wsb=need)
+        a.update(kw)
+        return f(a["h"], a["nw"], a["eps"], P, P, P, P, P, None, a["dout"], a["T"], 256, 8, 2,
+                 128, 128, 1, a["dh"], a["dnw"], P, P, P, P, P, a["ws"], a["wsb"], None)
+
+    assert call(nw=None) == m.HI3_E_NULL
+    assert call(h=None) == m.HI3_E_NULL
+    assert call(eps=-1.0) == m.HI3_E_UNSUPPORTED
+    assert call(eps=float("nan")) == m.HI3_E_UNSUPPORTED
+    assert call(dnw=UNALIGNED) == m.HI3_E_UNSUPPORTED
+    assert call(wsb=need - 1) == m.HI3_E_WORKSPACE

@@ -237,6 +237,75 @@ def test_autograd_function_matches_entry_points():
     assert torch.equal(gx, ref["dx"])
 
 
+BLOCK = [
+    # name, dtype, H, E, K, I, Is, seq_lens, padded_len
+    ("block_f32_pad", wk.F32, 192, 8, 3, 192, 64, (150, 37), 160),
+    ("block_bf16", wk.BF16, 512, 8, 2, 256, 192, (700,), None),
+    ("block_bf16_e16_pad", wk.BF16, 256, 16, 4, 320, 128, (300, 129, 7), 300),
+]
+
+
+@pytest.mark.parametrize("name,dtype,H,E,K,I,Is,seq,plen", BLOCK)
+def test_block_backward_all_elements(name, dtype, H, E, K, I, Is, seq, plen):
+    # hi3_moe_backward_norm_residual against oracle.moe_norm_residual_backward:
+    # dh, the norm weight's gradient and the layer's weight gradients, every
+    # element, by the gradient rule
+    import moe_decoder_ffn_amd as m
+    _say(f"[backward] {name}")
+    d, pad = make_case(dtype, H, E, K, I, Is, seq, plen)
+    shape = wk.LayerShape(H=H, E=E, K=K, I=I, Is=Is, dtype=dtype)
+    nw = wk.make_norm_weight(shape, 7)
+    dd = upload(d)
+    padd = to_dev(pad)
+    nwd = to_dev(nw)
+    w = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
+    g = m.moe_backward_norm_residual(dd["x"], nwd, *w, dd["dout"], K, pad_mask=padd)
+    _, idx, wts, _ = m.moe_forward_norm_residual(dd["x"], nwd, *w, K, pad_mask=padd,
+                                                 return_routes=True)
+    torch.cuda.synchronize()
+    g = {k: to_host(v) for k, v in g.items()}
+    idx, wts = to_host(idx), to_host(wts)
+    xn = oracle.rmsnorm(d["x"], nw, 1e-5, pad)
+    ref = oracle.route(xn, d["w_router"], K, pad_mask=pad)
+    near, ref_idx, ref_w = check_routes(idx, wts, ref, pad, E, K)
+    exp = oracle.moe_norm_residual_backward(d["x"], nw, d["w_router"], d["w13"], d["w2"],
+                                            d["ws13"], d["ws2"], d["dout"], K, 1e-5,
+                                            pad_mask=pad, idx=ref_idx, w=ref_w, magnitudes=True)
+    valid = np.ones(d["x"].shape[0], bool) if pad is None else pad == 0
+    names = {"dh": "dh", "dnorm_weight": "dnorm_weight", "dw_router": "dw_router",
+             "dw_up_gate": "dw13", "dw_down": "dw2", "dw_shared_up_gate": "dws13",
+             "dw_shared_down": "dws2"}
+    errs = {}
+    for k, ok in names.items():
+        if k == "dh":
+            errs[k] = check_grad(g[k][valid], exp[ok][valid], exp["m_" + ok][valid], dtype, k)
+            if pad is not None:
+                assert np.all(g[k][~valid] == 0), "padding rows of dh were written"
+        else:
+            errs[k] = check_grad(g[k], exp[ok], exp["m_" + ok], dtype, k)
+    _say("  max err / RMS: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+def test_block_backward_layer_grads_match_layer_backward():
+    # the block's expert and router weight gradients are the layer's at the
+    # normalised rows: bit-identical to hi3_moe_backward on RMSNorm(h)
+    import moe_decoder_ffn_amd as m
+    _say("[backward] block vs layer at xn")
+    d, pad = make_case(wk.BF16, 256, 16, 4, 192, 128, (300, 129, 7), 300)
+    shape = wk.LayerShape(H=256, E=16, K=4, I=192, Is=128, dtype=wk.BF16)
+    nw = to_dev(wk.make_norm_weight(shape, 7))
+    dd = upload(d)
+    padd = to_dev(pad)
+    w = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
+    gb = m.moe_backward_norm_residual(dd["x"], nw, *w, dd["dout"], 4, pad_mask=padd)
+    xn = torch.zeros_like(dd["x"])
+    m.hi3_moe_rmsnorm(dd["x"], nw, 1e-5, padd, xn)
+    gl = m.moe_backward(xn, *w, dd["dout"], 4, pad_mask=padd)
+    torch.cuda.synchronize()
+    for k in ("dw_router", "dw_up_gate", "dw_down", "dw_shared_up_gate", "dw_shared_down"):
+        assert torch.equal(gb[k], gl[k]), k
+
+
 @pytest.mark.parametrize("name", ["image_1024"])
 def test_backward_full_size_sampled_rows(name):
     # full size, the launch configuration the benchmark times: dx of sampled
