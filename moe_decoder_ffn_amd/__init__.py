@@ -442,3 +442,44 @@ def moe_layer(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, K
     """Differentiable layer output (MoEFunction.apply)."""
     return MoEFunction.apply(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
                              K, pad_mask)
+
+
+class MoENormResidualFunction(torch.autograd.Function):
+    """The block entry point (h + layer(RMSNorm(h))) as an autograd function:
+    forward runs hi3_moe_forward_norm_residual, backward
+    hi3_moe_backward_norm_residual (which recomputes the forward's routes and
+    activations). Gradients: h, the norm weight, the router weight and the
+    four expert weights."""
+
+    @staticmethod
+    def forward(ctx, h, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate,
+                w_shared_down, K, eps=1e-5, pad_mask=None):
+        out = moe_forward_norm_residual(h, norm_weight, w_router, w_up_gate, w_down,
+                                        w_shared_up_gate, w_shared_down, K, eps=eps,
+                                        pad_mask=pad_mask)
+        ctx.save_for_backward(h, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate,
+                              w_shared_down, pad_mask)
+        ctx.K, ctx.eps = K, eps
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        h, nw, wr, w13, w2, ws13, ws2, pad_mask = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        T, H = h.shape
+        E, I, Is = wr.shape[0], w13.shape[1] // 2, ws13.shape[0] // 2
+        g = [torch.zeros_like(h) if need[0] else None]
+        for i, t in ((1, nw), (2, wr), (3, w13), (4, w2), (5, ws13), (6, ws2)):
+            g.append(torch.empty_like(t) if need[i] else None)
+        n = hi3_moe_backward_workspace_size(T, H, E, ctx.K, I, Is, dtype_code(h.dtype))
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=h.device)
+        hi3_moe_backward_norm_residual(h, nw, ctx.eps, wr, w13, w2, ws13, ws2, pad_mask,
+                                       dout.contiguous(), ctx.K, g[0], g[1], *g[2:], ws)
+        return (*g, None, None, None)
+
+
+def moe_block(h, norm_weight, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, K,
+              eps=1e-5, pad_mask=None):
+    """Differentiable block output h + layer(RMSNorm(h)) (MoENormResidualFunction)."""
+    return MoENormResidualFunction.apply(h, norm_weight, w_router, w_up_gate, w_down,
+                                         w_shared_up_gate, w_shared_down, K, eps, pad_mask)

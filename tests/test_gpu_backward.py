@@ -306,6 +306,32 @@ def test_block_backward_layer_grads_match_layer_backward():
         assert torch.equal(gb[k], gl[k]), k
 
 
+def test_block_autograd_function():
+    import moe_decoder_ffn_amd as m
+    _say("[backward] block autograd function")
+    d, pad = make_case(wk.BF16, 256, 16, 4, 192, 128, (300, 129, 7), 300)
+    shape = wk.LayerShape(H=256, E=16, K=4, I=192, Is=128, dtype=wk.BF16)
+    nw = to_dev(wk.make_norm_weight(shape, 7))
+    dd = upload(d)
+    padd = to_dev(pad)
+    names = ("x", "w_router", "w13", "w2", "ws13", "ws2")
+    leaves = {k: dd[k].clone().requires_grad_(True) for k in names}
+    nwl = nw.clone().requires_grad_(True)
+    out = m.moe_block(leaves["x"], nwl, *(leaves[k] for k in names[1:]), 4, pad_mask=padd)
+    out.backward(dd["dout"])
+    ref_out = m.moe_forward_norm_residual(dd["x"], nw, *(dd[k] for k in names[1:]), 4,
+                                          pad_mask=padd)
+    ref = m.moe_backward_norm_residual(dd["x"], nw, *(dd[k] for k in names[1:]), dd["dout"], 4,
+                                       pad_mask=padd)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    assert torch.equal(leaves["x"].grad, ref["dh"]) and torch.equal(nwl.grad, ref["dnorm_weight"])
+    keys = {"w_router": "dw_router", "w13": "dw_up_gate", "w2": "dw_down",
+            "ws13": "dw_shared_up_gate", "ws2": "dw_shared_down"}
+    for k, r in keys.items():
+        assert torch.equal(leaves[k].grad, ref[r]), k
+
+
 @pytest.mark.parametrize("name", ["image_1024"])
 def test_backward_full_size_sampled_rows(name):
     # full size, the launch configuration the benchmark times: dx of sampled
