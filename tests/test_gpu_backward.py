@@ -375,3 +375,60 @@ def test_backward_full_size_sampled_rows(name):
     # the router's weight gradient cancel up to rounding
     dwr = g["dw_router"].astype(np.float64)
     assert np.abs(dwr.sum(axis=0)).max() <= 1e-3 * np.abs(dwr).sum(axis=0).max()
+
+
+def test_block_backward_and_training_pair_full_size():
+    # image_1024: the block backward's dh on sampled rows against the oracle
+    # (dh of a row depends on that row alone) and its exact doubling with
+    # dout; the training pair bit-identical to the standalone calls
+    import moe_decoder_ffn_amd as m
+    _say("[backward] full size block + training pair")
+    wl = wk.workload("image_1024")
+    d = wk.make_inputs(wl, 0)
+    d["dout"] = wk.make_dout(wl, 0)
+    pad = d.pop("pad_mask")
+    pad = pad if pad.any() else None
+    sh = wl.shape
+    K, E = sh.K, sh.E
+    nw = wk.make_norm_weight(sh, 0)
+    dd = upload(d)
+    nwd = to_dev(nw)
+    padd = to_dev(pad) if pad is not None else None
+    w = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
+    gb = m.moe_backward_norm_residual(dd["x"], nwd, *w, dd["dout"], K, pad_mask=padd)
+    dout2 = to_dev(wk.f32_to_bf16_bits(wk.bf16_bits_to_f32(d["dout"]) * np.float32(2.0)))
+    gb2 = m.moe_backward_norm_residual(dd["x"], nwd, *w, dout2, K, pad_mask=padd)
+    _, idx, wts, _ = m.moe_forward_norm_residual(dd["x"], nwd, *w, K, pad_mask=padd,
+                                                 return_routes=True)
+    torch.cuda.synchronize()
+    for k in gb:
+        a, b = gb[k].float(), gb2[k].float()
+        assert torch.equal(2 * a, b), k
+    dh = to_host(gb["dh"])
+    idx, wts = to_host(idx), to_host(wts)
+    xn = oracle.rmsnorm(d["x"], nw, 1e-5, pad)
+    ref = oracle.route(xn, d["w_router"], K, pad_mask=pad)
+    near, ref_idx, ref_w = check_routes(idx, wts, ref, pad, E, K)
+    T = d["x"].shape[0]
+    rows = np.array([0, T // 3, T - 1])
+    exp = oracle.moe_norm_residual_backward(d["x"][rows], nw, d["w_router"], d["w13"], d["w2"],
+                                            d["ws13"], d["ws2"], d["dout"][rows], K, 1e-5,
+                                            idx=ref_idx[rows], w=ref_w[rows], magnitudes=True)
+    check_grad(dh[rows], exp["dh"], exp["m_dh"], sh.dtype, "dh")
+    # training pair at full size
+    x = dd["x"]
+    g1 = m.moe_backward(x, *w, dd["dout"], K, pad_mask=padd)
+    out1 = m.moe_forward(x, *w, K, pad_mask=padd)
+    nws = m.hi3_moe_backward_workspace_size(T, sh.H, E, K, sh.I, sh.Is, m.dtype_code(x.dtype))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    out2 = torch.zeros_like(x)
+    m.hi3_moe_forward_train(x, *w, padd, K, out2, workspace=ws)
+    g2 = {k: torch.zeros_like(v) if k == "dx" else torch.empty_like(v) for k, v in g1.items()}
+    m.hi3_moe_backward_after_forward(x, *w, padd, dd["dout"], K, g2["dx"], g2["dw_router"],
+                                     g2["dw_up_gate"], g2["dw_down"], g2["dw_shared_up_gate"],
+                                     g2["dw_shared_down"], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
