@@ -44,10 +44,10 @@ constexpr int kNormBwdRows = 64;
 #define HI3_GEMM_STAGES 2
 #endif
 #ifndef HI3_GEMM_DOWN_SPLIT
-#define HI3_GEMM_DOWN_SPLIT 2
+#define HI3_GEMM_DOWN_SPLIT 1
 #endif
 #ifndef HI3_GEMM_DOWN_STAGES
-#define HI3_GEMM_DOWN_STAGES 3
+#define HI3_GEMM_DOWN_STAGES 2
 #endif
 #ifndef HI3_GEMM_WN
 #define HI3_GEMM_WN 4
