@@ -124,9 +124,7 @@ constexpr int kWgradBM = HI3_WGRAD_BM;
 constexpr int kWgradWN = kWgradBM == 256 ? kGemmWN : 2;
 constexpr int kWgradBK = HI3_WGRAD_BK;
 constexpr int kWgradStages = HI3_WGRAD_STAGES;
-// (the dh epilogue stages its whole tile in LDS: at most 128 rows)
-static_assert(kGemmBM % kDgradDownSplit == 0 && (kGemmBM / kDgradDownSplit) % 64 == 0 &&
-                  kGemmBM / kDgradDownSplit <= 128,
+static_assert(kGemmBM % kDgradDownSplit == 0 && (kGemmBM / kDgradDownSplit) % 64 == 0,
               "dgrad tile rows");
 // fp32 grouped GEMM tile.
 constexpr int kGemmF32BM = 64;

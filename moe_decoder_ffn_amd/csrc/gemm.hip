@@ -670,82 +670,92 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     // takes columns 4 l .. 4 l + 3, and the u, g, h reads and the du, dg
     // writes are contiguous row segments.
     constexpr int SLD = BN + 4;  // staged row stride in floats (16 B pad: bank spread)
-    static_assert(BM <= 128 && NST * (BM + BN) * BK * 2 >= BM * SLD * 4,
-                  "the dh tile fits in the LDS ring");
+    constexpr int RING = NST * (BM + BN) * BK * 2;
+    // rows staged at a time: the whole tile when it fits the ring
+    constexpr int CH = BM * SLD * 4 <= RING ? BM : (BM / 2) * SLD * 4 <= RING ? BM / 2 : BM / 4;
+    static_assert(CH * SLD * 4 <= RING && CH % 32 == 0 && BM % CH == 0,
+                  "the dh chunk fits in the LDS ring");
     float *stg = reinterpret_cast<float *>(sA0);
-    // every wave's last LDS reads have completed (the MFMAs consumed them)
-    // and the last step ended with a workgroup barrier: the ring is free
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * (BM / 2) + mi * 32 + r;
-          const int c = wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
-          *reinterpret_cast<f32x4_t *>(stg + row * SLD + c) =
-              f32x4_t{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
-                      acc[mi][ni][4 * q + 3]};
-        }
-    __syncthreads();
     uint16_t *D = static_cast<uint16_t *>(Cv);
     const float *ugp = cl.ug;
     const uint16_t *hp = static_cast<const uint16_t *>(cl.hsave);
     const int col = j.nt * BN + 4 * lane;
     const bool cok = col < N;
     constexpr int UR = kDgradEpilogueRows;  // rows per wave in flight
+    // every wave's last LDS reads have completed (the MFMAs consumed them)
+    // and the last step ended with a workgroup barrier: the ring is free
 #pragma unroll 1
-    for (int r0 = wave; r0 < j.rows; r0 += NW * UR) {
-      f32x4_t u4[UR], g4[UR];
-      u32x2_t h2[UR];
-      float rs[UR];
+    for (int ch = 0; ch < BM / CH && ch * CH < j.rows; ++ch) {
+      if (ch > 0) __syncthreads();
+      static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
+        constexpr int mi = decltype(Mv)::value;
+        const int rb = wm * (BM / 2) + mi * 32;
+        if (rb / CH != ch) return;
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
-        const int row = r0 + NW * u;
-        const int64_t grow = static_cast<int64_t>(j.row0) + row;
-        u4[u] = g4[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        h2[u] = u32x2_t{0u, 0u};
-        rs[u] = 1.0f;
-        if (row < j.rows) {
-          if (cl.rowscale) rs[u] = cl.rowscale[grow];
-          if (cok) {
-            u4[u] = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + col);
-            g4[u] = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + N + col);
-            h2[u] = *reinterpret_cast<const u32x2_t *>(hp + grow * N + col);
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * (BN / WN) + ni * 32 + 8 * q + 4 * g;
+            *reinterpret_cast<f32x4_t *>(stg + (rb - ch * CH + r) * SLD + c) =
+                f32x4_t{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                        acc[mi][ni][4 * q + 3]};
+          }
+      });
+      __syncthreads();
+      const int nr = min(CH, j.rows - ch * CH);
+#pragma unroll 1
+      for (int r0 = wave; r0 < nr; r0 += NW * UR) {
+        f32x4_t u4[UR], g4[UR];
+        u32x2_t h2[UR];
+        float rs[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const int row = r0 + NW * u;
+          const int64_t grow = static_cast<int64_t>(j.row0) + ch * CH + row;
+          u4[u] = g4[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          h2[u] = u32x2_t{0u, 0u};
+          rs[u] = 1.0f;
+          if (row < nr) {
+            if (cl.rowscale) rs[u] = cl.rowscale[grow];
+            if (cok) {
+              u4[u] = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + col);
+              g4[u] = *reinterpret_cast<const f32x4_t *>(ugp + grow * 2 * N + N + col);
+              h2[u] = *reinterpret_cast<const u32x2_t *>(hp + grow * N + col);
+            }
           }
         }
-      }
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
-        const int row = r0 + NW * u;
-        if (row >= j.rows) break;  // wave-uniform
-        const int64_t grow = static_cast<int64_t>(j.row0) + row;
-        const f32x4_t acc4 = *reinterpret_cast<const f32x4_t *>(stg + row * SLD + 4 * lane);
-        float du[4], dg[4], asum = 0.0f;
+        for (int u = 0; u < UR; ++u) {
+          const int row = r0 + NW * u;
+          if (row >= nr) break;  // wave-uniform
+          const int64_t grow = static_cast<int64_t>(j.row0) + ch * CH + row;
+          const f32x4_t acc4 = *reinterpret_cast<const f32x4_t *>(stg + row * SLD + 4 * lane);
+          float du[4], dg[4], asum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dh = rs[u] * acc4[e];
-          const float gt = g4[u][e];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
-          du[e] = dh * (gt * sg);
-          dg[e] = dh * u4[u][e] * (sg * (1.0f + gt * (1.0f - sg)));
-          const uint32_t hw = h2[u][e >> 1];
-          asum += dh * __uint_as_float((e & 1) ? (hw & 0xffff0000u) : (hw << 16));
+          for (int e = 0; e < 4; ++e) {
+            const float dh = rs[u] * acc4[e];
+            const float gt = g4[u][e];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+            du[e] = dh * (gt * sg);
+            dg[e] = dh * u4[u][e] * (sg * (1.0f + gt * (1.0f - sg)));
+            const uint32_t hw = h2[u][e >> 1];
+            asum += dh * __uint_as_float((e & 1) ? (hw & 0xffff0000u) : (hw << 16));
+          }
+          if (cok) {
+            u32x2_t o;
+            o[0] = pack_bf16x2(du[0], du[1]);
+            o[1] = pack_bf16x2(du[2], du[3]);
+            *reinterpret_cast<u32x2_t *>(D + grow * ldc + col) = o;
+            o[0] = pack_bf16x2(dg[0], dg[1]);
+            o[1] = pack_bf16x2(dg[2], dg[3]);
+            *reinterpret_cast<u32x2_t *>(D + grow * ldc + N + col) = o;
+          } else {
+            asum = 0.0f;
+          }
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) asum += __shfl_xor(asum, o, kWave);
+          if (cl.apart && lane == 0) cl.apart[grow * cl.apart_ld + j.nt] = asum;
         }
-        if (cok) {
-          u32x2_t o;
-          o[0] = pack_bf16x2(du[0], du[1]);
-          o[1] = pack_bf16x2(du[2], du[3]);
-          *reinterpret_cast<u32x2_t *>(D + grow * ldc + col) = o;
-          o[0] = pack_bf16x2(dg[0], dg[1]);
-          o[1] = pack_bf16x2(dg[2], dg[3]);
-          *reinterpret_cast<u32x2_t *>(D + grow * ldc + N + col) = o;
-        } else {
-          asum = 0.0f;
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) asum += __shfl_xor(asum, o, kWave);
-        if (cl.apart && lane == 0) cl.apart[grow * cl.apart_ld + j.nt] = asum;
       }
     }
   } else if constexpr (kGemmStagedStore) {
