@@ -128,6 +128,9 @@ __device__ __forceinline__ bool resolve_wgrad(const GemmArgs &a, TileJob &j) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Word 3 of a raw buffer resource (32-bit data format; untyped loads).
+constexpr int kBufferFlags = 0x00020000;
+
 // Direct global -> LDS copy of 16 bytes per lane; lane i writes
 // lds_base + 16 i (lds_base must be the same for the whole wave).
 // Written as the same three instructions the compiler emits for this copy
@@ -150,6 +153,11 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait for this wave's LDS operations (lgkmcnt 0), nothing else.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 // LDS layout of one operand stage: BK-wide k slices, CPR 16-byte chunks per
@@ -388,6 +396,65 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
                 std::integral_constant<int, CPW>{});
   };
 
+  // RS (4-wave blocks, forward modes): the copies go through registers
+  // instead of straight into LDS. Each wave loads its chunks of step k + 3
+  // into a register set during step k and writes the set it loaded two
+  // steps earlier (step k + 1) into the free LDS stage, so two steps of
+  // loads (128 KiB per CU) are in flight, each with two steps to land; the
+  // LDS holds the same layout as the direct copies produce. Two sets of
+  // CPW 16-byte chunks per lane; the 4-wave block leaves the registers for
+  // them (512 per lane at one wave per SIMD).
+  constexpr bool RS = kGemmRegStage && WN == 2 && !AT && !BT && NST == 2;
+  u32x4_t rsr[2][RS ? CPW : 1];
+  // byte offset of chunk q (A chunks first, then B) from the operand base:
+  // 32 bits (the launch checks that the operands allow it), so the loads
+  // take the uniform base plus step offset in scalar registers
+  uint32_t rs_off[RS ? CPW : 1];
+  if constexpr (RS) {
+#pragma unroll
+    for (int q = 0; q < A_CP; ++q) {
+      const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
+      const int c = (lane % L::CPR) ^ L::swz(row);
+      rs_off[q] = static_cast<uint32_t>((static_cast<int64_t>(arow_src[q]) * lda + c * 8) * 2);
+    }
+#pragma unroll
+    for (int q = 0; q < B_CP; ++q) {
+      const int row = (wave * B_CP + q) * L::RPC + lane / L::CPR;
+      const int c = (lane % L::CPR) ^ L::swz(row);
+      int brow;
+      if (MODE == 0) {
+        const int Ih = N / 2;
+        const int col = min(j.nt * (BN / 2) + (row & (BN / 2 - 1)), Ih - 1);
+        brow = row < BN / 2 ? col : Ih + col;
+      } else {
+        brow = min(j.nt * BN + row, N - 1);
+      }
+      rs_off[A_CP + q] = static_cast<uint32_t>((static_cast<int64_t>(brow) * Kd + c * 8) * 2);
+    }
+  }
+  // chunk q of step kc into register set `set`, through a buffer resource
+  // over A or this group's B (the launch guarantees that both fit 31-bit
+  // byte offsets, the range a resource takes here); the step's byte offset
+  // is uniform and goes in the scalar offset
+  auto rs_load = [&](auto SETv, int q, int kc) __attribute__((always_inline)) {
+    constexpr int set = decltype(SETv)::value;
+    if constexpr (RS) {
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(q < A_CP ? A : B), 0, 0x7fffffff, kBufferFlags);
+      rsr[set][q] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(rs_off[q]),
+                                                         kc * BK * 2, 0));
+    }
+  };
+  // chunk q of register set `set` into LDS stage (la, lb)
+  auto rs_write = [&](auto SETv, int q, u32x4_t *la, u32x4_t *lb) __attribute__((always_inline)) {
+    constexpr int set = decltype(SETv)::value;
+    if constexpr (RS) {
+      if (q < A_CP) la[(wave * A_CP + q) * 64 + lane] = rsr[set][q];
+      else lb[(wave * B_CP + (q - A_CP)) * 64 + lane] = rsr[set][q];
+    }
+  };
+
   // weight rows of the wave's sub-tiles: with [up; gate] the first NI/2 are
   // up rows and the last NI/2 the gate rows of the same columns
   int nrow[NI];
@@ -423,27 +490,46 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   static_assert(NG >= 2, "copies go after the first MFMA group");
   // copies per group: one while they last (PER = 1) unless there are more
   // copies than groups after the first
-  constexpr int PER = (CPW + NG - 2) / (NG - 1);
+  // (with the register-staged read-ahead the copies, and the barrier after
+  // them, must end before the last sub-step, which reads the next stage)
+  constexpr int CG = RS && kGemmReadAhead ? (NSUB - 1) * MI - 1 : NG - 1;  // groups for copies
+  static_assert(CG >= 1, "copy groups");
+  constexpr int PER = (CPW + CG - 1) / CG;
+  static_assert(!(RS && kGemmReadAhead) || (CPW + PER - 1) / PER < (NSUB - 1) * MI,
+                "read-ahead: the next stage is published before the last sub-step");
+  // RA (register-staged blocks): the writes of the next stage end in the
+  // first half of a step; a barrier there publishes that stage, and the
+  // last sub-step reads the next step's first fragments, so the MFMAs
+  // resume right after the end-of-step barrier instead of waiting for LDS.
+  constexpr bool RA = RS && kGemmReadAhead;
+  bf16x8_t af[2][MI], bf[2][NI];
+  // fragment read i (A fragments first, then B) of sub-step s of stage
+  // (la, lb) into buffer buf
+  auto read = [&](const u32x4_t *la, const u32x4_t *lb, int buf, int s, int i)
+      __attribute__((always_inline)) {
+    const int ch = 2 * s + g;
+    if (i < MI) {
+      if constexpr (AT)
+        af[buf][i] = read_frag_km<BM>(la, s, wm * (BM / 2) + i * 32, lane);
+      else
+        af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
+    } else {
+      if constexpr (BT)
+        bf[buf][i - MI] = read_frag_km<BN>(lb, s, nrow[i - MI], lane);
+      else
+        bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
+    }
+  };
+  // RS: the register set RSSETv is drained into (pa, pb) this step (in the
+  // last steps it holds a repeat of the last step: written to the idle
+  // stage, never read), then takes step rs_kl (clamped to the last step, so
+  // that the loads need no branch)
   auto compute = [&](const u32x4_t *la, const u32x4_t *lb, bool pre, int kn, u32x4_t *pa,
-                     u32x4_t *pb) __attribute__((always_inline)) {
-    bf16x8_t af[2][MI], bf[2][NI];
-    // fragment read i (A fragments first, then B) of sub-step s into buffer buf
-    auto read = [&](int buf, int s, int i) __attribute__((always_inline)) {
-      const int ch = 2 * s + g;
-      if (i < MI) {
-        if constexpr (AT)
-          af[buf][i] = read_frag_km<BM>(la, s, wm * (BM / 2) + i * 32, lane);
-        else
-          af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
-      } else {
-        if constexpr (BT)
-          bf[buf][i - MI] = read_frag_km<BN>(lb, s, nrow[i - MI], lane);
-        else
-          bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
-      }
-    };
+                     u32x4_t *pb, auto RSSETv, int rs_kl) __attribute__((always_inline)) {
+    if constexpr (!RA) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) read(0, 0, i);
+      for (int i = 0; i < NR; ++i) read(la, lb, 0, 0, i);
+    }
     static_for<NSUB>([&](auto Sv) __attribute__((always_inline)) {
       constexpr int s = decltype(Sv)::value;
       constexpr int cur = s & 1;
@@ -454,10 +540,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
                                                                 acc[mi][ni], 0, 0, 0);
-        if constexpr (s + 1 < NSUB) {
+        if constexpr (s + 1 < NSUB || RA) {
           constexpr int i0 = mi * NR / MI, i1 = (mi + 1) * NR / MI;
 #pragma unroll
-          for (int i = i0; i < i1; ++i) read(cur ^ 1, s + 1, i);
+          for (int i = i0; i < i1; ++i) {
+            if constexpr (s + 1 < NSUB) read(la, lb, cur ^ 1, s + 1, i);
+            else read(pa, pb, cur ^ 1, 0, i);  // RA: the stage written this step
+          }
           // MFMA, read, MFMA, read, ...
           constexpr int NT_ = NI > i1 - i0 ? NI : i1 - i0;
           static_for<NT_>([&](auto Tv) __attribute__((always_inline)) {
@@ -472,9 +561,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         constexpr int q0 = (grp - 1) * PER < CPW ? (grp - 1) * PER : CPW;
         constexpr int q1 = grp * PER < CPW ? grp * PER : CPW;
         if constexpr (grp >= 1 && q0 < q1) {
-          if (pre)
+          if constexpr (RS) {
+            // drain chunk q of the set into LDS, then refill it
+#pragma unroll
+            for (int q = q0; q < q1; ++q) {
+              rs_write(RSSETv, q, pa, pb);
+              rs_load(RSSETv, q, rs_kl);
+            }
+            if constexpr (RA && q1 == CPW) {
+              // every wave's writes of the next stage done: publish it
+              wait_lgkm0();
+              barrier_no_fence();
+            }
+          } else if (pre) {
             issue_range(kn, pa, pb, std::integral_constant<int, q0>{},
                         std::integral_constant<int, q1>{});
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -514,19 +616,44 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   auto step = [&](auto S, int k) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     constexpr int p = StageRing<s, NST>::prev;
+    // RS: register set (k + 1) % 2 holds step k + 1: it goes into the free
+    // stage, then takes step k + 3
+    constexpr int rset = (s + 1) % 2;
     compute(stage_a(S), stage_b(S), k + NST - 1 < nk, k + NST - 1,
-            stage_a(std::integral_constant<int, p>{}), stage_b(std::integral_constant<int, p>{}));
-    wait_stages(max(min(k + NST - 1, nk - 1) - (k + 1), 0));
+            stage_a(std::integral_constant<int, p>{}), stage_b(std::integral_constant<int, p>{}),
+            std::integral_constant<int, rset>{}, min(k + 3, nk - 1));
+    if constexpr (RS) wait_lgkm0();  // this wave's LDS writes done before the barrier
+    else wait_stages(max(min(k + NST - 1, nk - 1) - (k + 1), 0));
     barrier_no_fence();
   };
 
-  // prologue: stages 0 .. NST - 2 (those that exist), then stage 0 landed
-  static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
-    constexpr int v = decltype(S)::value;
-    if (v < nk) issue(v, stage_a(S), stage_b(S));
-  });
-  wait_stages(min(NST - 2, nk - 1));
-  barrier_no_fence();
+  if constexpr (RS) {
+    // prologue: steps 0 and 1 into the register sets, step 0 into stage 0,
+    // step 2 into set 0
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) rs_load(std::integral_constant<int, 0>{}, q, 0);
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) rs_load(std::integral_constant<int, 1>{}, q, min(1, nk - 1));
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+      rs_write(std::integral_constant<int, 0>{}, q, sA0, sB0);
+      rs_load(std::integral_constant<int, 0>{}, q, min(2, nk - 1));
+    }
+    wait_lgkm0();
+    barrier_no_fence();
+    if constexpr (RA) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) read(sA0, sB0, 0, 0, i);
+    }
+  } else {
+    // prologue: stages 0 .. NST - 2 (those that exist), then stage 0 landed
+    static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
+      constexpr int v = decltype(S)::value;
+      if (v < nk) issue(v, stage_a(S), stage_b(S));
+    });
+    wait_stages(min(NST - 2, nk - 1));
+    barrier_no_fence();
+  }
   int kc = 0;
   for (; kc + NST <= nk; kc += NST)
     static_for<NST>([&](auto S) __attribute__((always_inline)) { step(S, kc + decltype(S)::value); });
@@ -1099,15 +1226,30 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
   const dim3 block(128 * kGemmWN);
 #define HI3_LAUNCH(M, BMv, BKv, NSTv)                                                      \
   hipLaunchKernelGGL((gemm_bf16_kernel<M, BMv, BKv, NSTv, kGemmWN>), dim3(grid), block, 0, s, a)
+#define HI3_LAUNCH_FWD(M, BMv, BKv, NSTv)                                                  \
+  hipLaunchKernelGGL((gemm_bf16_kernel<M, BMv, BKv, NSTv, kGemmFwdWN>), dim3(grid),        \
+                     dim3(128 * kGemmFwdWN), 0, s, a)
+  // the forward's register-staged 4-wave blocks (where the caller asks for
+  // them) address A and each group's B with byte offsets below 2^31: A has
+  // at most max_tiles * BM rows
+  bool fwd_fits = kGemmFwdWN != kGemmWN && a.four_wave;
+  for (int c = 0; c < 2; ++c) {
+    const GemmClass &k = a.cls[c];
+    const int64_t a_bytes = static_cast<int64_t>(max_tiles) * kGemmBM * k.lda * 2;
+    const int64_t b_bytes = static_cast<int64_t>(k.N) * k.Kd * 2;
+    if (a_bytes >= (int64_t{1} << 31) || b_bytes >= (int64_t{1} << 31)) fwd_fits = false;
+  }
   if (dtype == kBF16) {
     constexpr int DBM = kGemmBM / kGemmDownSplit;
     switch (mode) {
       case 0:
         if (stream) HI3_LAUNCH(0, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages);
+        else if (fwd_fits) HI3_LAUNCH_FWD(0, kGemmBM, kGemmBK, kGemmStages);
         else HI3_LAUNCH(0, kGemmBM, kGemmBK, kGemmStages);
         break;
       case 1:
         if (stream) HI3_LAUNCH(1, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages);
+        else if (fwd_fits) HI3_LAUNCH_FWD(1, DBM, kGemmBK, kGemmDownStages);
         else HI3_LAUNCH(1, DBM, kGemmBK, kGemmDownStages);
         break;
       case 2:
@@ -1128,6 +1270,7 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
     }
   }
 #undef HI3_LAUNCH
+#undef HI3_LAUNCH_FWD
   return hipGetLastError();
 }
 
