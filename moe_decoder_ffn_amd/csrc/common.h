@@ -77,22 +77,10 @@ constexpr int kGemmDownSplit = HI3_GEMM_DOWN_SPLIT;
 constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
 static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
 constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
-// Waves along the columns of the forward GEMMs' blocks (modes 0 and 1,
-// default tiles); with 2 (4-wave blocks, one wave per SIMD) the copies are
-// staged in registers, two steps ahead of the LDS ring.
-#ifndef HI3_GEMM_FWD_WN
-#define HI3_GEMM_FWD_WN 2
-#endif
-#ifndef HI3_GEMM_REG_STAGE
-#define HI3_GEMM_REG_STAGE 1
-#endif
-#ifndef HI3_GEMM_READ_AHEAD
-#define HI3_GEMM_READ_AHEAD 1
-#endif
-// The [up; gate] GEMM runs on 4-wave blocks up to this many rows per expert
-// (T K / E); the down GEMM always does.
-#ifndef HI3_GEMM_UPGATE_4W_ROWS
-#define HI3_GEMM_UPGATE_4W_ROWS 384
+// Forward GEMMs (8-wave blocks, 2-stage ring): a third LDS stage for the
+// weight operand, whose copies then run two steps ahead.
+#ifndef HI3_GEMM_DEEP_B
+#define HI3_GEMM_DEEP_B 1
 #endif
 // Backward GEMMs: the gradient through the down projection (mode 2) runs each
 // listed row tile as HI3_DGRAD_DOWN_SPLIT blocks; the gradient through
@@ -122,10 +110,7 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 #define HI3_GEMM_STAGED_STORE 1
 #endif
 constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
-constexpr bool kGemmRegStage = HI3_GEMM_REG_STAGE != 0;
-constexpr int kGemmFwdWN = HI3_GEMM_FWD_WN;
-constexpr bool kGemmReadAhead = HI3_GEMM_READ_AHEAD != 0;
-constexpr int kGemmUpGate4wRows = HI3_GEMM_UPGATE_4W_ROWS;
+constexpr bool kGemmDeepB = HI3_GEMM_DEEP_B != 0;
 constexpr int kDgradDownSplit = HI3_DGRAD_DOWN_SPLIT;
 constexpr int kDgradDownStages = HI3_DGRAD_DOWN_STAGES;
 // Rows per wave in flight in the mode-2 epilogue (its u, g, h reads).
@@ -219,7 +204,6 @@ struct Plan {
   int Epad;       // E rounded up to 32 (router MFMA column tiles)
   int BM;         // grouped-GEMM tile rows (per dtype)
   int max_tiles;  // upper bound on grouped-GEMM row tiles
-  bool upgate_4w; // [up; gate] GEMM on 4-wave blocks (few rows per expert)
   size_t wsplit;  // [3][Epad][H] bf16: router weight split into 3 bf16 terms
   size_t rpart;   // [slices][T][E] fp32: router partial logits
   size_t idx;     // [T*K] int32 routes when the caller passes none
@@ -277,12 +261,10 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
   p.T = T; p.H = H; p.E = E; p.K = K; p.I = I; p.Is = Is; p.dtype = dtype;
   p.NB = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
   p.Epad = (E + 31) / 32 * 32;
-  if (dtype != kBF16) {
+  if (dtype != kBF16)
     p.BM = kGemmF32BM;
-  } else {
+  else
     p.BM = T * K <= static_cast<int64_t>(kGemmStreamMaxRows) * E ? kGemmStreamBM : kGemmBM;
-    p.upgate_4w = T * K <= static_cast<int64_t>(kGemmUpGate4wRows) * E;
-  }
   const int64_t TK = T * K;
   p.max_tiles = static_cast<int>((TK + p.BM - 1) / p.BM + E + (T + p.BM - 1) / p.BM);
   const size_t es = dtype == kBF16 ? 2 : 4;
@@ -427,9 +409,6 @@ struct GemmArgs {
   const int32_t *nreal;
   const void *zrow;
   int wg_shared_blocks;  // set by the launcher
-  // modes 0 and 1 with the default tiles: run the register-staged 4-wave
-  // blocks (where the operands allow their 32-bit offsets)
-  int four_wave;
 };
 
 struct CombineArgs {

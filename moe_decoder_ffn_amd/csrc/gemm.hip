@@ -128,9 +128,6 @@ __device__ __forceinline__ bool resolve_wgrad(const GemmArgs &a, TileJob &j) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Word 3 of a raw buffer resource (32-bit data format; untyped loads).
-constexpr int kBufferFlags = 0x00020000;
-
 // Direct global -> LDS copy of 16 bytes per lane; lane i writes
 // lds_base + 16 i (lds_base must be the same for the whole wave).
 // Written as the same three instructions the compiler emits for this copy
@@ -153,11 +150,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Wait for this wave's LDS operations (lgkmcnt 0), nothing else.
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 // LDS layout of one operand stage: BK-wide k slices, CPR 16-byte chunks per
@@ -269,7 +261,10 @@ struct StageRing {
 // rows.
 // The tile body: BM is the row capacity of this body (the LDS stages may be
 // larger); the stage arrays are the kernel's.
-template <int MODE, int BM, int BK, int NST, int WN>
+// DB (8-wave forward blocks with a 2-stage ring): a third B stage; the B
+// copies (the weights, whose latency the L2 does not hide) run two steps
+// ahead, the A copies one.
+template <int MODE, int BM, int BK, int NST, int WN, bool DB = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u32x4_t *sA0,
                                           u32x4_t *sB0, u32x4_t *sA1, u32x4_t *sB1,
                                           u32x4_t *sA2, u32x4_t *sB2, u32x4_t *sA3,
@@ -288,6 +283,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   static_assert(!AT || BM == 128 || BM == 256, "k-major A tile");
   static_assert(!(AT || BT) || BK == 32 || BK == 64, "k-major k step");
   static_assert(NST >= 2 && NST <= 5, "stages");
+  static_assert(!DB || (NST == 2 && !AT && !BT), "deep B ring: 2 + 3 stages, k-contiguous operands");
   static_assert(BM * BK * 2 % (1024 * NW) == 0 && BN * BK * 2 % (1024 * NW) == 0,
                 "each wave copies a whole number of 1 KiB blocks");
   static_assert(A_CP >= 1 && B_CP >= 1 && (NST - 2) * CPW < 64, "copy counts");
@@ -342,12 +338,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   };
   const uint16_t *zrow = static_cast<const uint16_t *>(a.zrow) + 8 * (lane & 31);
   // Copies [q0, q1) of this wave (A copies first, then B) for k step kc.
-  auto issue_range = [&](int kc, u32x4_t *la, u32x4_t *lb, auto Q0, auto Q1) __attribute__((always_inline)) {
+  // (DB: the B copies are of step kcb; okA / okB select the operands)
+  auto issue_range = [&](int kc, u32x4_t *la, u32x4_t *lb, auto Q0, auto Q1, int kcb = -1,
+                         bool okA = true, bool okB = true) __attribute__((always_inline)) {
     constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
     const int ko = kc * BK;
+    const int kob = (DB ? kcb : kc) * BK;
 #pragma unroll
     for (int q = 0; q < A_CP; ++q) {
       if (q < q0 || q >= q1) continue;
+      if (!okA) continue;
       if constexpr (AT) {
         km_copy(std::integral_constant<int, BM>{}, wave * A_CP + q, j.row0, cl.M, la,
                 [&](int krow, int col) {
@@ -365,6 +365,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 #pragma unroll
     for (int q = 0; q < B_CP; ++q) {
       if (A_CP + q < q0 || A_CP + q >= q1) continue;
+      if (!okB) continue;
       if constexpr (AT) {
         km_copy(std::integral_constant<int, BN>{}, wave * B_CP + q, j.nt * BN, N, lb,
                 [&](int krow, int col) {
@@ -386,7 +387,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         } else {
           brow = min(j.nt * BN + row, N - 1);
         }
-        lds_dma16(B + static_cast<int64_t>(brow) * Kd + ko + c * 8,
+        lds_dma16(B + static_cast<int64_t>(brow) * Kd + kob + c * 8,
                   lb + (wave * B_CP + q) * 64);
       }
     }
@@ -394,65 +395,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   auto issue = [&](int kc, u32x4_t *la, u32x4_t *lb) __attribute__((always_inline)) {
     issue_range(kc, la, lb, std::integral_constant<int, 0>{},
                 std::integral_constant<int, CPW>{});
-  };
-
-  // RS (4-wave blocks, forward modes): the copies go through registers
-  // instead of straight into LDS. Each wave loads its chunks of step k + 3
-  // into a register set during step k and writes the set it loaded two
-  // steps earlier (step k + 1) into the free LDS stage, so two steps of
-  // loads (128 KiB per CU) are in flight, each with two steps to land; the
-  // LDS holds the same layout as the direct copies produce. Two sets of
-  // CPW 16-byte chunks per lane; the 4-wave block leaves the registers for
-  // them (512 per lane at one wave per SIMD).
-  constexpr bool RS = kGemmRegStage && WN == 2 && !AT && !BT && NST == 2;
-  u32x4_t rsr[2][RS ? CPW : 1];
-  // byte offset of chunk q (A chunks first, then B) from the operand base:
-  // 32 bits (the launch checks that the operands allow it), so the loads
-  // take the uniform base plus step offset in scalar registers
-  uint32_t rs_off[RS ? CPW : 1];
-  if constexpr (RS) {
-#pragma unroll
-    for (int q = 0; q < A_CP; ++q) {
-      const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
-      const int c = (lane % L::CPR) ^ L::swz(row);
-      rs_off[q] = static_cast<uint32_t>((static_cast<int64_t>(arow_src[q]) * lda + c * 8) * 2);
-    }
-#pragma unroll
-    for (int q = 0; q < B_CP; ++q) {
-      const int row = (wave * B_CP + q) * L::RPC + lane / L::CPR;
-      const int c = (lane % L::CPR) ^ L::swz(row);
-      int brow;
-      if (MODE == 0) {
-        const int Ih = N / 2;
-        const int col = min(j.nt * (BN / 2) + (row & (BN / 2 - 1)), Ih - 1);
-        brow = row < BN / 2 ? col : Ih + col;
-      } else {
-        brow = min(j.nt * BN + row, N - 1);
-      }
-      rs_off[A_CP + q] = static_cast<uint32_t>((static_cast<int64_t>(brow) * Kd + c * 8) * 2);
-    }
-  }
-  // chunk q of step kc into register set `set`, through a buffer resource
-  // over A or this group's B (the launch guarantees that both fit 31-bit
-  // byte offsets, the range a resource takes here); the step's byte offset
-  // is uniform and goes in the scalar offset
-  auto rs_load = [&](auto SETv, int q, int kc) __attribute__((always_inline)) {
-    constexpr int set = decltype(SETv)::value;
-    if constexpr (RS) {
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(q < A_CP ? A : B), 0, 0x7fffffff, kBufferFlags);
-      rsr[set][q] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(rs_off[q]),
-                                                         kc * BK * 2, 0));
-    }
-  };
-  // chunk q of register set `set` into LDS stage (la, lb)
-  auto rs_write = [&](auto SETv, int q, u32x4_t *la, u32x4_t *lb) __attribute__((always_inline)) {
-    constexpr int set = decltype(SETv)::value;
-    if constexpr (RS) {
-      if (q < A_CP) la[(wave * A_CP + q) * 64 + lane] = rsr[set][q];
-      else lb[(wave * B_CP + (q - A_CP)) * 64 + lane] = rsr[set][q];
-    }
   };
 
   // weight rows of the wave's sub-tiles: with [up; gate] the first NI/2 are
@@ -490,46 +432,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   static_assert(NG >= 2, "copies go after the first MFMA group");
   // copies per group: one while they last (PER = 1) unless there are more
   // copies than groups after the first
-  // (with the register-staged read-ahead the copies, and the barrier after
-  // them, must end before the last sub-step, which reads the next stage)
-  constexpr int CG = RS && kGemmReadAhead ? (NSUB - 1) * MI - 1 : NG - 1;  // groups for copies
-  static_assert(CG >= 1, "copy groups");
-  constexpr int PER = (CPW + CG - 1) / CG;
-  static_assert(!(RS && kGemmReadAhead) || (CPW + PER - 1) / PER < (NSUB - 1) * MI,
-                "read-ahead: the next stage is published before the last sub-step");
-  // RA (register-staged blocks): the writes of the next stage end in the
-  // first half of a step; a barrier there publishes that stage, and the
-  // last sub-step reads the next step's first fragments, so the MFMAs
-  // resume right after the end-of-step barrier instead of waiting for LDS.
-  constexpr bool RA = RS && kGemmReadAhead;
-  bf16x8_t af[2][MI], bf[2][NI];
-  // fragment read i (A fragments first, then B) of sub-step s of stage
-  // (la, lb) into buffer buf
-  auto read = [&](const u32x4_t *la, const u32x4_t *lb, int buf, int s, int i)
-      __attribute__((always_inline)) {
-    const int ch = 2 * s + g;
-    if (i < MI) {
-      if constexpr (AT)
-        af[buf][i] = read_frag_km<BM>(la, s, wm * (BM / 2) + i * 32, lane);
-      else
-        af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
-    } else {
-      if constexpr (BT)
-        bf[buf][i - MI] = read_frag_km<BN>(lb, s, nrow[i - MI], lane);
-      else
-        bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
-    }
-  };
-  // RS: the register set RSSETv is drained into (pa, pb) this step (in the
-  // last steps it holds a repeat of the last step: written to the idle
-  // stage, never read), then takes step rs_kl (clamped to the last step, so
-  // that the loads need no branch)
+  constexpr int PER = (CPW + NG - 2) / (NG - 1);
+  // (DB: the B copies are of step knb, into stage pbb)
   auto compute = [&](const u32x4_t *la, const u32x4_t *lb, bool pre, int kn, u32x4_t *pa,
-                     u32x4_t *pb, auto RSSETv, int rs_kl) __attribute__((always_inline)) {
-    if constexpr (!RA) {
+                     u32x4_t *pb, int knb = 0, u32x4_t *pbb = nullptr)
+      __attribute__((always_inline)) {
+    bf16x8_t af[2][MI], bf[2][NI];
+    // fragment read i (A fragments first, then B) of sub-step s into buffer buf
+    auto read = [&](int buf, int s, int i) __attribute__((always_inline)) {
+      const int ch = 2 * s + g;
+      if (i < MI) {
+        if constexpr (AT)
+          af[buf][i] = read_frag_km<BM>(la, s, wm * (BM / 2) + i * 32, lane);
+        else
+          af[buf][i] = __builtin_bit_cast(bf16x8_t, la[L::pos(wm * (BM / 2) + i * 32 + r, ch)]);
+      } else {
+        if constexpr (BT)
+          bf[buf][i - MI] = read_frag_km<BN>(lb, s, nrow[i - MI], lane);
+        else
+          bf[buf][i - MI] = __builtin_bit_cast(bf16x8_t, lb[L::pos(nrow[i - MI] + r, ch)]);
+      }
+    };
 #pragma unroll
-      for (int i = 0; i < NR; ++i) read(la, lb, 0, 0, i);
-    }
+    for (int i = 0; i < NR; ++i) read(0, 0, i);
     static_for<NSUB>([&](auto Sv) __attribute__((always_inline)) {
       constexpr int s = decltype(Sv)::value;
       constexpr int cur = s & 1;
@@ -540,13 +465,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][ni], af[cur][mi],
                                                                 acc[mi][ni], 0, 0, 0);
-        if constexpr (s + 1 < NSUB || RA) {
+        if constexpr (s + 1 < NSUB) {
           constexpr int i0 = mi * NR / MI, i1 = (mi + 1) * NR / MI;
 #pragma unroll
-          for (int i = i0; i < i1; ++i) {
-            if constexpr (s + 1 < NSUB) read(la, lb, cur ^ 1, s + 1, i);
-            else read(pa, pb, cur ^ 1, 0, i);  // RA: the stage written this step
-          }
+          for (int i = i0; i < i1; ++i) read(cur ^ 1, s + 1, i);
           // MFMA, read, MFMA, read, ...
           constexpr int NT_ = NI > i1 - i0 ? NI : i1 - i0;
           static_for<NT_>([&](auto Tv) __attribute__((always_inline)) {
@@ -561,22 +483,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         constexpr int q0 = (grp - 1) * PER < CPW ? (grp - 1) * PER : CPW;
         constexpr int q1 = grp * PER < CPW ? grp * PER : CPW;
         if constexpr (grp >= 1 && q0 < q1) {
-          if constexpr (RS) {
-            // drain chunk q of the set into LDS, then refill it
-#pragma unroll
-            for (int q = q0; q < q1; ++q) {
-              rs_write(RSSETv, q, pa, pb);
-              rs_load(RSSETv, q, rs_kl);
-            }
-            if constexpr (RA && q1 == CPW) {
-              // every wave's writes of the next stage done: publish it
-              wait_lgkm0();
-              barrier_no_fence();
-            }
-          } else if (pre) {
+          if constexpr (DB)
+            issue_range(kn, pa, pbb, std::integral_constant<int, q0>{},
+                        std::integral_constant<int, q1>{}, knb);
+          else if (pre)
             issue_range(kn, pa, pb, std::integral_constant<int, q0>{},
                         std::integral_constant<int, q1>{});
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -616,35 +528,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   auto step = [&](auto S, int k) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     constexpr int p = StageRing<s, NST>::prev;
-    // RS: register set (k + 1) % 2 holds step k + 1: it goes into the free
-    // stage, then takes step k + 3
-    constexpr int rset = (s + 1) % 2;
     compute(stage_a(S), stage_b(S), k + NST - 1 < nk, k + NST - 1,
-            stage_a(std::integral_constant<int, p>{}), stage_b(std::integral_constant<int, p>{}),
-            std::integral_constant<int, rset>{}, min(k + 3, nk - 1));
-    if constexpr (RS) wait_lgkm0();  // this wave's LDS writes done before the barrier
-    else wait_stages(max(min(k + NST - 1, nk - 1) - (k + 1), 0));
+            stage_a(std::integral_constant<int, p>{}), stage_b(std::integral_constant<int, p>{}));
+    wait_stages(max(min(k + NST - 1, nk - 1) - (k + 1), 0));
     barrier_no_fence();
   };
 
-  if constexpr (RS) {
-    // prologue: steps 0 and 1 into the register sets, step 0 into stage 0,
-    // step 2 into set 0
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) rs_load(std::integral_constant<int, 0>{}, q, 0);
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) rs_load(std::integral_constant<int, 1>{}, q, min(1, nk - 1));
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      rs_write(std::integral_constant<int, 0>{}, q, sA0, sB0);
-      rs_load(std::integral_constant<int, 0>{}, q, min(2, nk - 1));
-    }
-    wait_lgkm0();
+  // DB step k (A stage k % 2, B stage k % 3): copy A of step k + 1 into
+  // the A stage read in step k - 1, then B of step k + 2 into the B stage
+  // read in step k - 1; at the end wait for step k + 1's copies (the B
+  // copies of step k + 2, issued last, may stay in flight). Near the end
+  // the copies repeat the last step into those free stages, which are not
+  // read again, so that they need no branch.
+  auto step_db = [&](auto S6, int k) __attribute__((always_inline)) {
+    constexpr int s6 = decltype(S6)::value;
+    constexpr int sa = s6 % 2, sb = s6 % 3, na = (s6 + 1) % 2, nb = (s6 + 2) % 3;
+    compute(stage_a(std::integral_constant<int, sa>{}), stage_b(std::integral_constant<int, sb>{}),
+            true, min(k + 1, nk - 1), stage_a(std::integral_constant<int, na>{}),
+            stage_b(std::integral_constant<int, sb>{}), min(k + 2, nk - 1),
+            stage_b(std::integral_constant<int, nb>{}));
+    wait_vmem<B_CP>();
     barrier_no_fence();
-    if constexpr (RA) {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) read(sA0, sB0, 0, 0, i);
-    }
+  };
+
+  int kc = 0;
+  if constexpr (DB) {
+    // prologue: A and B of step 0, then B of step 1; wait for step 0
+    issue_range(0, sA0, sB0, std::integral_constant<int, 0>{}, std::integral_constant<int, CPW>{},
+                0);
+    issue_range(0, sA0, sB1, std::integral_constant<int, 0>{}, std::integral_constant<int, CPW>{},
+                min(1, nk - 1), false, true);
+    wait_vmem<B_CP>();
+    barrier_no_fence();
+    for (; kc + 6 <= nk; kc += 6)
+      static_for<6>([&](auto S) __attribute__((always_inline)) { step_db(S, kc + decltype(S)::value); });
+    static_for<5>([&](auto S) __attribute__((always_inline)) {
+      if (kc + decltype(S)::value < nk) step_db(S, kc + decltype(S)::value);
+    });
+    // the last B copies are still in flight: drain them before the
+    // epilogue reuses the ring
+    wait_vmem<0>();
+    barrier_no_fence();
   } else {
     // prologue: stages 0 .. NST - 2 (those that exist), then stage 0 landed
     static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
@@ -653,13 +577,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     });
     wait_stages(min(NST - 2, nk - 1));
     barrier_no_fence();
+    for (; kc + NST <= nk; kc += NST)
+      static_for<NST>([&](auto S) __attribute__((always_inline)) { step(S, kc + decltype(S)::value); });
+    static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
+      if (kc + decltype(S)::value < nk) step(S, kc + decltype(S)::value);
+    });
   }
-  int kc = 0;
-  for (; kc + NST <= nk; kc += NST)
-    static_for<NST>([&](auto S) __attribute__((always_inline)) { step(S, kc + decltype(S)::value); });
-  static_for<NST - 1>([&](auto S) __attribute__((always_inline)) {
-    if (kc + decltype(S)::value < nk) step(S, kc + decltype(S)::value);
-  });
 
   if constexpr (MODE == 0 && kGemmStagedStore) {
     // h = SiLU(g) u (the layer dtype), and with ug also u and g (fp32),
@@ -993,12 +916,17 @@ __global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(G
   constexpr int BN = kGemmBN;
   constexpr int AE = BM * BK / 8, BE = BN * BK / 8;  // 16-byte chunks per stage
   static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
-  // one array: stage s holds A at (AE + BE) s and B right after it; the
-  // whole ring is reused by the epilogues that stage their tile in LDS
-  __shared__ u32x4_t smem[NST * (AE + BE)];
+  // the 8-wave forward blocks take a third B stage where it fits
+  constexpr bool DB = kGemmDeepB && WN == 4 && NST == 2 && BK == 64 && (MODE == 0 || MODE == 1) &&
+                      (NST * (BM + BN) + BN) * BK * 2 <= 160 * 1024;
+  // one array: stage s holds A at (AE + BE) s and B right after it (with DB
+  // the third B stage follows); the whole ring is reused by the epilogues
+  // that stage their tile in LDS
+  __shared__ u32x4_t smem[NST * (AE + BE) + (DB ? BE : 0)];
   u32x4_t *sA0 = smem, *sB0 = smem + AE;
   u32x4_t *sA1 = smem + (AE + BE), *sB1 = sA1 + AE;
-  u32x4_t *sA2 = NST > 2 ? smem + 2 * (AE + BE) : smem, *sB2 = NST > 2 ? sA2 + AE : smem;
+  u32x4_t *sA2 = NST > 2 ? smem + 2 * (AE + BE) : smem;
+  u32x4_t *sB2 = NST > 2 ? sA2 + AE : DB ? smem + 2 * (AE + BE) : smem;
   u32x4_t *sA3 = NST > 3 ? smem + 3 * (AE + BE) : smem, *sB3 = NST > 3 ? sA3 + AE : smem;
   u32x4_t *sA4 = NST > 4 ? smem + 4 * (AE + BE) : smem, *sB4 = NST > 4 ? sA4 + AE : smem;
 
@@ -1014,17 +942,17 @@ __global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(G
     constexpr bool whole_s = [] (int bm) constexpr { return bm * BK * 2 % (1024 * 2 * WN) == 0; }(BMS);
     if constexpr (BMS >= 64 && BMS % 64 == 0 && whole_s) {
       if (j.rows <= BMS) {
-        gemm_tile<MODE, BMS, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+        gemm_tile<MODE, BMS, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
         return;
       }
     }
     if constexpr (BM3 > BMS && BM3 % 64 == 0 && whole) {
       if (j.rows <= BM3) {
-        gemm_tile<MODE, BM3, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+        gemm_tile<MODE, BM3, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
         return;
       }
     }
-    gemm_tile<MODE, BM, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+    gemm_tile<MODE, BM, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
   }
 }
 
@@ -1226,30 +1154,15 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
   const dim3 block(128 * kGemmWN);
 #define HI3_LAUNCH(M, BMv, BKv, NSTv)                                                      \
   hipLaunchKernelGGL((gemm_bf16_kernel<M, BMv, BKv, NSTv, kGemmWN>), dim3(grid), block, 0, s, a)
-#define HI3_LAUNCH_FWD(M, BMv, BKv, NSTv)                                                  \
-  hipLaunchKernelGGL((gemm_bf16_kernel<M, BMv, BKv, NSTv, kGemmFwdWN>), dim3(grid),        \
-                     dim3(128 * kGemmFwdWN), 0, s, a)
-  // the forward's register-staged 4-wave blocks (where the caller asks for
-  // them) address A and each group's B with byte offsets below 2^31: A has
-  // at most max_tiles * BM rows
-  bool fwd_fits = kGemmFwdWN != kGemmWN && a.four_wave;
-  for (int c = 0; c < 2; ++c) {
-    const GemmClass &k = a.cls[c];
-    const int64_t a_bytes = static_cast<int64_t>(max_tiles) * kGemmBM * k.lda * 2;
-    const int64_t b_bytes = static_cast<int64_t>(k.N) * k.Kd * 2;
-    if (a_bytes >= (int64_t{1} << 31) || b_bytes >= (int64_t{1} << 31)) fwd_fits = false;
-  }
   if (dtype == kBF16) {
     constexpr int DBM = kGemmBM / kGemmDownSplit;
     switch (mode) {
       case 0:
         if (stream) HI3_LAUNCH(0, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages);
-        else if (fwd_fits) HI3_LAUNCH_FWD(0, kGemmBM, kGemmBK, kGemmStages);
         else HI3_LAUNCH(0, kGemmBM, kGemmBK, kGemmStages);
         break;
       case 1:
         if (stream) HI3_LAUNCH(1, kGemmStreamBM, kGemmStreamBK, kGemmStreamStages);
-        else if (fwd_fits) HI3_LAUNCH_FWD(1, DBM, kGemmBK, kGemmDownStages);
         else HI3_LAUNCH(1, DBM, kGemmBK, kGemmDownStages);
         break;
       case 2:
@@ -1270,7 +1183,6 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
     }
   }
 #undef HI3_LAUNCH
-#undef HI3_LAUNCH_FWD
   return hipGetLastError();
 }
 

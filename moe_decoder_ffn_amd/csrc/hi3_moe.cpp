@@ -126,7 +126,6 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   up.tiles = tiles;
   up.gto = gto;
   up.E = E;
-  up.four_wave = p.upgate_4w;
   HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
   // 4: grouped down projection
   rec.at(4);
@@ -136,7 +135,6 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   dn.tiles = tiles;
   dn.gto = gto;
   dn.E = E;
-  dn.four_wave = 1;
   HI3_TRY(launch_gemm_down(dn, p.max_tiles, p.BM, dtype, s));
   // 5: combine
   rec.at(5);
@@ -256,7 +254,6 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
     up.tiles = tiles;
     up.gto = gto;
     up.E = E;
-    up.four_wave = p.upgate_4w;
     HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
   }
   // 4: x and w dout by slot; x and dout by real row when there is padding
