@@ -77,8 +77,9 @@ constexpr int kGemmDownSplit = HI3_GEMM_DOWN_SPLIT;
 constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
 static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
 constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
-// Forward GEMMs (8-wave blocks, 2-stage ring): a third LDS stage for the
-// weight operand, whose copies then run two steps ahead.
+// GEMMs whose B operand is a weight (8-wave blocks, 2-stage ring: the
+// forward and the backward's dx GEMM): a third LDS stage for the weights,
+// whose copies then run two steps ahead.
 #ifndef HI3_GEMM_DEEP_B
 #define HI3_GEMM_DEEP_B 1
 #endif

@@ -261,9 +261,10 @@ struct StageRing {
 // rows.
 // The tile body: BM is the row capacity of this body (the LDS stages may be
 // larger); the stage arrays are the kernel's.
-// DB (8-wave forward blocks with a 2-stage ring): a third B stage; the B
-// copies (the weights, whose latency the L2 does not hide) run two steps
-// ahead, the A copies one.
+// DB (8-wave blocks with a 2-stage ring whose B operand is a weight: the
+// forward GEMMs and the backward's dx GEMM): a third B stage; the B copies
+// (the weights, whose latency the L2 does not hide) run two steps ahead,
+// the A copies one.
 template <int MODE, int BM, int BK, int NST, int WN, bool DB = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u32x4_t *sA0,
                                           u32x4_t *sB0, u32x4_t *sA1, u32x4_t *sB1,
@@ -283,7 +284,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   static_assert(!AT || BM == 128 || BM == 256, "k-major A tile");
   static_assert(!(AT || BT) || BK == 32 || BK == 64, "k-major k step");
   static_assert(NST >= 2 && NST <= 5, "stages");
-  static_assert(!DB || (NST == 2 && !AT && !BT), "deep B ring: 2 + 3 stages, k-contiguous operands");
+  static_assert(!DB || (NST == 2 && !AT), "deep B ring: 2 + 3 stages, k-contiguous A");
   static_assert(BM * BK * 2 % (1024 * NW) == 0 && BN * BK * 2 % (1024 * NW) == 0,
                 "each wave copies a whole number of 1 KiB blocks");
   static_assert(A_CP >= 1 && B_CP >= 1 && (NST - 2) * CPW < 64, "copy counts");
@@ -375,7 +376,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
                 });
       } else if constexpr (BT) {
         km_copy(std::integral_constant<int, BN>{}, wave * B_CP + q, j.nt * BN, N, lb,
-                [&](int krow, int col) { return B + static_cast<int64_t>(ko + krow) * ldb + col; });
+                [&](int krow, int col) { return B + static_cast<int64_t>(kob + krow) * ldb + col; });
       } else {
         const int row = (wave * B_CP + q) * L::RPC + lane / L::CPR;
         const int c = (lane % L::CPR) ^ L::swz(row);
@@ -916,8 +917,10 @@ __global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(G
   constexpr int BN = kGemmBN;
   constexpr int AE = BM * BK / 8, BE = BN * BK / 8;  // 16-byte chunks per stage
   static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
-  // the 8-wave forward blocks take a third B stage where it fits
-  constexpr bool DB = kGemmDeepB && WN == 4 && NST == 2 && BK == 64 && (MODE == 0 || MODE == 1) &&
+  // the 8-wave blocks whose B is a weight (modes 0, 1, 3) take a third B
+  // stage where it fits
+  constexpr bool DB = kGemmDeepB && WN == 4 && NST == 2 && BK == 64 &&
+                      (MODE == 0 || MODE == 1 || MODE == 3) &&
                       (NST * (BM + BN) + BN) * BK * 2 <= 160 * 1024;
   // one array: stage s holds A at (AE + BE) s and B right after it (with DB
   // the third B stage follows); the whole ring is reused by the epilogues
