@@ -58,12 +58,23 @@ __device__ __forceinline__ int class_col_tiles(const GemmClass &c) {
   return MODE == 0 ? (c.N / 2 + BN / 2 - 1) / (BN / 2) : (c.N + BN - 1) / BN;
 }
 
+// The job list: groups in order. Modes 0 and 1: within a group, chunks of
+// kGemmColChunk column tiles, each chunk taking every row (sub-)tile of the
+// group, row tile major, so the blocks that share a weight tile or a row
+// tile's rows are neighbours; block b runs on XCD b % 8, and XCD x takes
+// the contiguous part [x per, (x + 1) per) of the list (per = ceil(jobs /
+// 8)): a group's weights and rows are fetched into one XCD's L2 (two at a
+// part boundary), where the neighbours run at the same time. Modes 2 and 3
+// (measured faster so): row tile major, column fastest, block b = job b.
 template <int MODE, int BN>
 __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   const int ntiles = a.gto[a.E + 1];
   const int SP = a.split;
   const int W = ntiles * SP * a.NTn;
-  const int L = blockIdx.x;
+  constexpr bool XM = MODE <= 1;
+  const int per = (W + 7) / 8;
+  if (XM && static_cast<int>(blockIdx.x) / 8 >= per) return false;
+  const int L = XM ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
   if (L >= W) return false;
   // group: the largest g with gto[g] * SP * NTn <= L (empty groups have
   // empty ranges)
@@ -75,8 +86,20 @@ __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   const int g = lo;
   const int first = a.gto[g] * SP;              // first row sub-tile of the group
   const int off = L - first * a.NTn;
-  const int nt = off % a.NTn;
-  const int ms = first + off / a.NTn;
+  const int R = a.gto[g + 1] * SP - first;      // row sub-tiles of the group
+  constexpr int CC = XM ? kGemmColChunk : (1 << 30);  // one chunk: column fastest
+  const int full = a.NTn / CC;                  // whole chunks; the last may be narrower
+  int nt, rt;
+  if (off < full * CC * R) {
+    const int c = off / (CC * R), rem = off - c * CC * R;
+    rt = rem / CC;
+    nt = c * CC + rem % CC;
+  } else {
+    const int cw = a.NTn - full * CC, rem = off - full * CC * R;
+    rt = rem / cw;
+    nt = full * CC + rem % cw;
+  }
+  const int ms = first + rt;
   const int4 tile = a.tiles[ms / SP];
   const int part = ms % SP;
   j.g = tile.x;
