@@ -130,10 +130,16 @@ constexpr int kDgradUpStages = HI3_DGRAD_UP_STAGES;
 // Weight-gradient output tile rows: 256 (8 waves, one block per CU) or 128
 // (4 waves, two blocks per CU, so one block's prologue and epilogue overlap
 // the other's main loop).
+// Weight-gradient tile order: groups of this many row tiles, walked down
+// the rows first.
+#ifndef HI3_WGRAD_GROUP_ROWS
+#define HI3_WGRAD_GROUP_ROWS 8
+#endif
 #ifndef HI3_WGRAD_BM
 #define HI3_WGRAD_BM 128
 #endif
 constexpr int kWgradBM = HI3_WGRAD_BM;
+constexpr int kWgradGroupRows = HI3_WGRAD_GROUP_ROWS;
 constexpr int kWgradWN = kWgradBM == 256 ? kGemmWN : 2;
 constexpr int kWgradBK = HI3_WGRAD_BK;
 constexpr int kWgradStages = HI3_WGRAD_STAGES;

@@ -137,11 +137,17 @@ __device__ __forceinline__ bool resolve_wgrad(const GemmArgs &a, TileJob &j) {
   const GemmClass &c = a.cls[cls];
   const int NT = (c.N + BN - 1) / BN, MT = (c.M + BM - 1) / BM;
   if (tt >= MT * NT) return false;
+  // tiles in groups of GR row tiles, down the group's rows first and then
+  // across its columns, so the tiles resident together read a few row
+  // slices of A and a few column slices of B (which then stay in the L2)
+  constexpr int GR = kWgradGroupRows;
+  const int grp = tt / (GR * NT), rem = tt - grp * GR * NT;
+  const int gr = min(GR, MT - grp * GR);  // rows in this group (the last may have fewer)
   j.g = g;
   j.cls = cls;
-  j.row0 = (tt / NT) * BM;
+  j.row0 = (grp * GR + rem % gr) * BM;
   j.rows = min(BM, c.M - j.row0);
-  j.nt = tt % NT;
+  j.nt = rem / gr;
   j.kstart = cls ? 0 : a.goff[g];
   j.kcount = cls ? *a.nreal : a.gcnt[g];
   return true;
