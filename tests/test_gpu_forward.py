@@ -87,14 +87,24 @@ def test_forward_small_all_rows(name, dtype, H, E, K, I, Is, seq, plen):
         assert np.isfinite(as_f64(out[pad == 0])).all()
 
 
+@pytest.mark.parametrize("H,I,Is", [(64, 64, 64), (128, 64, 128), (64, 128, 192), (192, 320, 64)])
+def test_forward_short_reductions(H, I, Is):
+    """Reductions of 1 to 5 k steps of 64 on the default (256-row) tiles:
+    the weight ring runs its copies two steps ahead and repeats the last
+    step near the end, so the first and last steps meet at these sizes."""
+    _say(f"[forward] short reductions H={H} I={I} Is={Is}")
+    shape = wk.LayerShape(H=H, E=2, K=1, I=I, Is=Is, dtype=wk.BF16)
+    d = wk.make_inputs(wk.custom(shape, (600,)), 13)
+    full_check(d, 1, None, None)
+
+
 @pytest.mark.parametrize("T", [1, 64, 65, 112, 113, 128, 129, 192, 193, 256, 257, 513])
 def test_forward_tile_boundaries(T):
     """One expert (E = K = 1), so every row goes to it and the row-tile
     edges are hit by construction. Up to 112 rows per expert the layer runs
-    the streaming tiles (64 rows). Above, the up/gate tile holds 256 rows and
-    runs a half-height body at <= 128 rows and a three-quarter body at <= 192;
-    the down projection runs each tile as two 128-row halves (the second
-    empty below 129 rows) with a half-height body at <= 64 rows."""
+    the streaming tiles (64 rows). Above, both projections use 256-row tiles
+    with a half-height body at <= 128 rows and a three-quarter body at
+    <= 192."""
     _say(f"[forward] tile boundaries T={T}")
     shape = wk.LayerShape(H=256, E=1, K=1, I=128, Is=192, dtype=wk.BF16)
     d = wk.make_inputs(wk.custom(shape, (T,)), 11)
