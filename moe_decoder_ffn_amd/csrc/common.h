@@ -77,6 +77,10 @@ constexpr int kGemmDownSplit = HI3_GEMM_DOWN_SPLIT;
 constexpr int kGemmDownStages = HI3_GEMM_DOWN_STAGES;
 static_assert(kGemmBM % kGemmDownSplit == 0, "down tile rows");
 constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the rows)
+// Row tiles of at most a quarter of the tile rows run a quarter-height body.
+#ifndef HI3_GEMM_QUARTER_BODY
+#define HI3_GEMM_QUARTER_BODY 1
+#endif
 // Grouped GEMM job list (modes 0-3): column tiles per chunk (each chunk
 // takes every row tile of its group before the next chunk).
 #ifndef HI3_GEMM_COL_CHUNK
@@ -118,6 +122,7 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
 constexpr bool kGemmDeepB = HI3_GEMM_DEEP_B != 0;
 constexpr int kGemmColChunk = HI3_GEMM_COL_CHUNK;
+constexpr bool kGemmQuarterBody = HI3_GEMM_QUARTER_BODY != 0;
 constexpr int kDgradDownSplit = HI3_DGRAD_DOWN_SPLIT;
 constexpr int kDgradDownStages = HI3_DGRAD_DOWN_STAGES;
 // Rows per wave in flight in the mode-2 epilogue (its u, g, h reads).

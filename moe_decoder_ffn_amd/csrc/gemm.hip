@@ -968,10 +968,17 @@ __global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(G
     gemm_tile<MODE, BM, BK, NST, WN>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
   } else {
     if (!resolve_job<MODE, BN>(a, j)) return;
-    constexpr int BMS = BM / 2, BM3 = BM / 4 * 3;
+    constexpr int BMS = BM / 2, BM3 = BM / 4 * 3, BMQ = BM / 4;
     // a body exists where its A stage splits into whole 1 KiB copies per wave
     constexpr bool whole = [] (int bm) constexpr { return bm * BK * 2 % (1024 * 2 * WN) == 0; }(BM3);
     constexpr bool whole_s = [] (int bm) constexpr { return bm * BK * 2 % (1024 * 2 * WN) == 0; }(BMS);
+    constexpr bool whole_q = [] (int bm) constexpr { return bm * BK * 2 % (1024 * 2 * WN) == 0; }(BMQ);
+    if constexpr (kGemmQuarterBody && BMQ >= 64 && BMQ % 64 == 0 && whole_q) {
+      if (j.rows <= BMQ) {
+        gemm_tile<MODE, BMQ, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+        return;
+      }
+    }
     if constexpr (BMS >= 64 && BMS % 64 == 0 && whole_s) {
       if (j.rows <= BMS) {
         gemm_tile<MODE, BMS, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
