@@ -25,15 +25,10 @@
 //
 // Work list: the row tiles of all groups (written on the device by the scan
 // kernel, expert-major, the shared expert last) times the column tiles; the
-// down projection may run each listed row tile as `split` blocks of
-// sub_rows rows (a smaller tile suits its shape better). The grid is sized
-// for the largest possible tile count; surplus blocks exit.
-// Schedule: the column tile is the fastest index of the work list and block
-// b runs on XCD b % 8 (the hardware's round-robin). The blocks of one row
-// tile run at the same time, spread over the XCDs; when the column-tile
-// count is a multiple of 8 (24 and 16 at H = 4096, I = 3072) each column
-// tile of a group always lands on the same XCD, whose L2 serves its weight
-// slice to all of the group's row tiles, which run close together in time.
+// gradient through the down projection (mode 2) runs each listed row tile as
+// `split` blocks of sub_rows rows. The grid is sized for the largest
+// possible tile count; surplus blocks exit. Block b runs on XCD b % 8 (the
+// hardware's round-robin); how jobs map to blocks is resolve_job's.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -934,11 +929,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
 }
 
 // Block: one (row tile, column tile) job. Row tiles hold up to BM rows; a
-// group's last tile is often much shorter: one with at most BM / 2 rows runs
-// the half-height body (half the MFMAs and A copies, the same B copies), one
-// with at most 3 BM / 4 rows the three-quarter body (when those heights are
-// multiples of 64). The bodies are straight-line code over the same LDS
-// ring. Mode 4 jobs are whole output tiles (one body).
+// group's last tile is often much shorter: one with at most BM / 4, BM / 2
+// or 3 BM / 4 rows runs the quarter-, half- or three-quarter-height body
+// (that share of the MFMAs and A copies, the same B copies; each where the
+// height is a multiple of 64). The bodies are straight-line code over the
+// same LDS ring. Mode 4 jobs are whole output tiles (one body).
 // OCC: blocks per CU the register allocation must allow (the 128-row
 // weight-gradient tile runs two per CU).
 template <int MODE, int BM, int BK, int NST, int WN, int OCC = 1>
