@@ -87,23 +87,27 @@ def stage_bytes(wl):
 RIDGE_ROWS = 312
 
 
-def upgate_bytes(wl):
-    """Algorithmic HBM bytes of the [up; gate] GEMM: every expert's and the
-    shared expert's [up; gate] weights once, each routed or shared row of x
-    once per use, h written once."""
+def upgate_bytes(wl, shared=True):
+    """Algorithmic HBM bytes of the [up; gate] GEMM: every expert's and (with
+    shared) the shared expert's [up; gate] weights once, each routed or
+    shared row of x once per use, h written once."""
     sh = wl.shape
     es = 2 if sh.dtype == wk.BF16 else 4
-    rows = wl.T_valid * (sh.K + 1)
-    return (sh.E * 2 * sh.I * sh.H + 2 * sh.Is * sh.H) * es + rows * sh.H * es + \
-        (wl.T_valid * sh.K * sh.I + wl.T_valid * sh.Is) * es
+    sf = 1 if shared else 0
+    rows = wl.T_valid * (sh.K + sf)
+    return (sh.E * 2 * sh.I * sh.H + sf * 2 * sh.Is * sh.H) * es + rows * sh.H * es + \
+        (wl.T_valid * sh.K * sh.I + sf * wl.T_valid * sh.Is) * es
 
 
-def gemm_flops(wl):
+def gemm_flops(wl, shared=True):
+    """Algorithmic FLOP of the forward's GEMM stages; shared=False when the
+    shared expert's GEMMs run on the side stream, outside these stages."""
     sh = wl.shape
     Tv = wl.T_valid
+    sf = 1 if shared else 0
     return {
-        "gemm_up_gate_swiglu": Tv * (sh.K * 2 * sh.H * 2 * sh.I + 2 * sh.H * 2 * sh.Is),
-        "gemm_down": Tv * (sh.K * 2 * sh.I * sh.H + 2 * sh.Is * sh.H),
+        "gemm_up_gate_swiglu": Tv * (sh.K * 2 * sh.H * 2 * sh.I + sf * 2 * sh.H * 2 * sh.Is),
+        "gemm_down": Tv * (sh.K * 2 * sh.I * sh.H + sf * 2 * sh.Is * sh.H),
     }
 
 
@@ -543,7 +547,11 @@ def main():
     flops = wl.T_valid * wk.flop_per_valid_token(sh)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    gf = gemm_flops(wl)
+    # the shared expert's GEMMs on the side stream: the GEMM stages (and the
+    # dominant kernel) are the routed experts' alone
+    side = m.hi3_moe_forward_shared_on_side(wl.T, sh.H, sh.E, sh.K, sh.I, sh.Is, sh.dtype,
+                                            pad is not None)
+    gf = gemm_flops(wl, shared=not side)
     sb = stage_bytes(wl)
     stages = {}
     for s, name in enumerate(names):
@@ -560,18 +568,19 @@ def main():
 
     dom = "gemm_up_gate_swiglu"
     dom_ms = stage_ms[names.index(dom)]
+    kname = ("gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU, routed experts; the shared "
+             "expert runs as gemm_bf16_dense_kernel<0> on a side stream)" if side else
+             "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)")
     if sh.dtype == wk.BF16 and wl.T_valid * sh.K <= RIDGE_ROWS * sh.E:
         # few rows per expert: the weights are the traffic (HBM roofline)
-        gb = upgate_bytes(wl)
+        gb = upgate_bytes(wl, shared=not side)
         achieved = gb / (dom_ms * 1e-3) / 1e9
-        roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
-                    "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(wl.name)}
     else:
         achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
-        roofline = {"kernel": "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)",
-                    "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+        roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(wl.name)}
 

@@ -133,6 +133,15 @@ int hi3_moe_dispatch(const int32_t *topk_idx, const uint8_t *pad_mask, const voi
 /*
  * The whole layer: router, dispatch, grouped [up; gate] projection with the
  * SwiGLU epilogue, grouped down projection, shared expert, combine.
+ * Streams: when hi3_moe_forward_shared_on_side says so, the shared expert's
+ * two GEMMs run on a side stream of hip_stream's device (the current
+ * device), alongside the routing: it waits for an event recorded on
+ * hip_stream when the call starts, and hip_stream waits for its end before
+ * the combine, so later work on hip_stream is ordered after the whole call
+ * as usual. The library creates that stream (default priority) and its two
+ * events on the device's first such call and keeps them until the process
+ * ends; they hold no device memory. Calls from several host threads
+ * enqueue one at a time (a mutex per device).
  *   x                [T, H] dtype.
  *   w_router         [E, H] fp32.
  *   w_up_gate        [E, 2*I, H] dtype; rows [0, I) up, [I, 2I) gate.
@@ -158,8 +167,11 @@ int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
  * hi3_moe_forward with per-stage timing: stage_events holds
  * HI3_NUM_STAGES + 1 hipEvent_t handles created by the caller; event i is
  * recorded on hip_stream just before stage i is enqueued and the last one
- * after the final stage (stage names: hi3_moe_stage_name). Same results as
- * hi3_moe_forward. stage_events must not be NULL.
+ * after the final stage (stage names: hi3_moe_stage_name). Same results and
+ * the same streams as hi3_moe_forward: when the shared expert runs on the
+ * side stream, the GEMM stages time the routed experts alone, and the
+ * shared expert's GEMMs run during the routing stages and the first GEMM.
+ * stage_events must not be NULL.
  */
 int hi3_moe_forward_instrumented(const void *x, const float *w_router,
                                  const void *w_up_gate, const void *w_down,
@@ -339,6 +351,16 @@ int hi3_moe_backward_after_forward(const void *x, const float *w_router,
 
 /* Static name of backward stage i (0 <= i < HI3_NUM_BWD_STAGES), else "?". */
 const char *hi3_moe_backward_stage_name(int stage);
+
+/*
+ * 1 when hi3_moe_forward (and its instrumented and block variants) with
+ * these sizes runs the shared expert's GEMMs on the side stream described
+ * at hi3_moe_forward, else 0 (also for sizes the forward rejects): bf16,
+ * no padding mask, and enough routed rows for the default GEMM tiles.
+ * Host-only.
+ */
+int hi3_moe_forward_shared_on_side(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                                   int32_t I_shared, int32_t dtype, int32_t has_pad_mask);
 
 /* Static name of timed stage i (0 <= i < HI3_NUM_STAGES), else "?". */
 const char *hi3_moe_stage_name(int stage);

@@ -32,6 +32,7 @@ EXPORTED = (
     "hi3_moe_dispatch",
     "hi3_moe_forward",
     "hi3_moe_forward_instrumented",
+    "hi3_moe_forward_shared_on_side",
     "hi3_moe_rmsnorm",
     "hi3_moe_forward_norm_residual",
     "hi3_moe_backward_workspace_size",
@@ -70,6 +71,8 @@ def _load():
     lib.hi3_moe_forward.restype = ctypes.c_int
     lib.hi3_moe_forward_instrumented.argtypes = fwd + [P]
     lib.hi3_moe_forward_instrumented.restype = ctypes.c_int
+    lib.hi3_moe_forward_shared_on_side.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
+    lib.hi3_moe_forward_shared_on_side.restype = ctypes.c_int
     f32 = ctypes.c_float
     lib.hi3_moe_rmsnorm.argtypes = [P, P, f32, P, i64, i32, i32, P, P]
     lib.hi3_moe_rmsnorm.restype = ctypes.c_int
@@ -189,6 +192,11 @@ def hi3_moe_forward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_gat
     _check(lib.hi3_moe_forward_instrumented(*_forward_args(
         x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
         topk_idx, topk_w, expert_counts, workspace, stream), arr))
+
+
+def hi3_moe_forward_shared_on_side(T, H, E, K, I, I_shared, dtype, has_pad_mask) -> bool:
+    return bool(lib.hi3_moe_forward_shared_on_side(T, H, E, K, I, I_shared, dtype,
+                                                   1 if has_pad_mask else 0))
 
 
 def hi3_moe_rmsnorm(x, weight, eps, pad_mask, xn, stream=None):

@@ -86,6 +86,11 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 #ifndef HI3_GEMM_COL_CHUNK
 #define HI3_GEMM_COL_CHUNK 4
 #endif
+// The forward runs the shared expert's GEMMs on a side stream alongside the
+// routing (when every row is real).
+#ifndef HI3_OVERLAP_SHARED
+#define HI3_OVERLAP_SHARED 1
+#endif
 // GEMMs whose B operand is a weight (8-wave blocks, 2-stage ring: the
 // forward and the backward's dx GEMM): a third LDS stage for the weights,
 // whose copies then run two steps ahead.
@@ -121,6 +126,7 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 #endif
 constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
 constexpr bool kGemmDeepB = HI3_GEMM_DEEP_B != 0;
+constexpr bool kOverlapShared = HI3_OVERLAP_SHARED != 0;
 constexpr int kGemmColChunk = HI3_GEMM_COL_CHUNK;
 constexpr bool kGemmQuarterBody = HI3_GEMM_QUARTER_BODY != 0;
 constexpr int kDgradDownSplit = HI3_DGRAD_DOWN_SPLIT;
@@ -366,6 +372,9 @@ struct ScanArgs {
   int32_t *misc;
   int32_t *gto;
   int4 *tiles;
+  // when set, the shared group gets no row tiles here (its GEMMs run as
+  // dense launches, launch_gemm_dense)
+  int no_shared;
 };
 
 struct ScatterArgs {
@@ -427,6 +436,7 @@ struct GemmArgs {
   const int32_t *nreal;
   const void *zrow;
   int wg_shared_blocks;  // set by the launcher
+  int dense_rows;        // dense launches: the rows of class 1 (no tile list)
 };
 
 struct CombineArgs {
@@ -486,6 +496,10 @@ hipError_t launch_gemm_upgate(const GemmArgs &a, int max_tiles, int tile_rows, i
                               hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, int max_tiles, int tile_rows, int dtype,
                             hipStream_t s);
+// The shared expert alone over rows 0 .. rows-1 of its A operand (every row
+// real), with no tile list: a.cls[1] describes it; mode 0 ([up; gate] +
+// SwiGLU) or 1 (down), bf16, the default tiles.
+hipError_t launch_gemm_dense(const GemmArgs &a, int rows, int mode, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int dtype, hipStream_t s);
 
 // ---------------------------------------------------------------- backward

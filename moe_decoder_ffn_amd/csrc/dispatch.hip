@@ -113,7 +113,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
       run += (tot[x] + a.BM - 1) / a.BM;
     }
     toff[a.E] = run;
-    run += (nvalid_s + a.BM - 1) / a.BM;
+    if (!a.no_shared) run += (nvalid_s + a.BM - 1) / a.BM;
     toff[a.E + 1] = run;
   }
   __syncthreads();
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
     for (int j = 0, m0 = 0; m0 < n; ++j, m0 += a.BM)
       a.tiles[toff[tid] + j] = make_int4(tid, eoff[tid] + m0, min(a.BM, n - m0), 0);
   }
-  {
+  if (!a.no_shared) {
     const int n = nvalid_s;
     const int nt = (n + a.BM - 1) / a.BM;
     for (int j = tid; j < nt; j += blockDim.x)

@@ -107,6 +107,37 @@ __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   return nt < class_col_tiles<MODE, BN>(c);
 }
 
+// A dense launch (modes 0 and 1): class 1 alone over rows 0 .. dense_rows-1,
+// in row tiles of BM, with resolve_job's job order (chunks of kGemmColChunk
+// column tiles over every row tile, each XCD a contiguous part).
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool resolve_dense(const GemmArgs &a, TileJob &j) {
+  const int R = (a.dense_rows + BM - 1) / BM;
+  const int W = R * a.NTn;
+  const int per = (W + 7) / 8;
+  if (static_cast<int>(blockIdx.x) / 8 >= per) return false;
+  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (L >= W) return false;
+  constexpr int CC = kGemmColChunk;
+  const int full = a.NTn / CC;
+  int nt, rt;
+  if (L < full * CC * R) {
+    const int c = L / (CC * R), rem = L - c * CC * R;
+    rt = rem / CC;
+    nt = c * CC + rem % CC;
+  } else {
+    const int cw = a.NTn - full * CC, rem = L - full * CC * R;
+    rt = rem / cw;
+    nt = full * CC + rem % cw;
+  }
+  j.g = 0;
+  j.cls = 1;
+  j.row0 = rt * BM;
+  j.rows = min(BM, a.dense_rows - j.row0);
+  j.nt = nt;
+  return nt < class_col_tiles<MODE, BN>(a.cls[1]);
+}
+
 // Mode 4: the shared group's output tiles come first (they reduce over every
 // real row, the longest jobs); then the routed experts, placed so that all
 // tiles of expert g run on XCD g % 8 (block b runs on XCD b % 8), where that
@@ -990,6 +1021,45 @@ __global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(G
   }
 }
 
+// The shared expert on its own (resolve_dense; the bodies and LDS ring of
+// gemm_bf16_kernel, modes 0 and 1). A kernel of its own name, so that
+// profiles keep it apart from the grouped launches.
+template <int MODE, int BM, int BK, int NST, int WN>
+__global__ __launch_bounds__(128 * WN, 2 * WN / 4) void gemm_bf16_dense_kernel(GemmArgs a) {
+  static_assert(MODE == 0 || MODE == 1, "dense launches: [up; gate] or down");
+  constexpr int BN = kGemmBN;
+  constexpr int AE = BM * BK / 8, BE = BN * BK / 8;
+  static_assert(NST * (BM + BN) * BK * 2 <= 160 * 1024, "LDS ring fits in 160 KiB");
+  constexpr bool DB = kGemmDeepB && WN == 4 && NST == 2 && BK == 64 &&
+                      (NST * (BM + BN) + BN) * BK * 2 <= 160 * 1024;
+  __shared__ u32x4_t smem[NST * (AE + BE) + (DB ? BE : 0)];
+  u32x4_t *sA0 = smem, *sB0 = smem + AE;
+  u32x4_t *sA1 = smem + (AE + BE), *sB1 = sA1 + AE;
+  u32x4_t *sA2 = NST > 2 ? smem + 2 * (AE + BE) : smem;
+  u32x4_t *sB2 = NST > 2 ? sA2 + AE : DB ? smem + 2 * (AE + BE) : smem;
+  u32x4_t *sA3 = NST > 3 ? smem + 3 * (AE + BE) : smem, *sB3 = NST > 3 ? sA3 + AE : smem;
+  u32x4_t *sA4 = NST > 4 ? smem + 4 * (AE + BE) : smem, *sB4 = NST > 4 ? sA4 + AE : smem;
+  TileJob j;
+  if (!resolve_dense<MODE, BM, BN>(a, j)) return;
+  // only the last row tile is short
+  constexpr int BMS = BM / 2, BMQ = BM / 4;
+  constexpr bool whole_s = BMS * BK * 2 % (1024 * 2 * WN) == 0;
+  constexpr bool whole_q = BMQ * BK * 2 % (1024 * 2 * WN) == 0;
+  if constexpr (kGemmQuarterBody && BMQ >= 64 && BMQ % 64 == 0 && whole_q) {
+    if (j.rows <= BMQ) {
+      gemm_tile<MODE, BMQ, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+      return;
+    }
+  }
+  if constexpr (BMS >= 64 && BMS % 64 == 0 && whole_s) {
+    if (j.rows <= BMS) {
+      gemm_tile<MODE, BMS, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+      return;
+    }
+  }
+  gemm_tile<MODE, BM, BK, NST, WN, DB>(a, j, sA0, sB0, sA1, sB1, sA2, sB2, sA3, sB3, sA4, sB4);
+}
+
 // --------------------------------------------------------------- fp32
 
 // fp32 layers: LDS-tiled FMA, 64 rows x 64 columns per block ([up; gate]:
@@ -1217,6 +1287,30 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
     }
   }
 #undef HI3_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_dense(const GemmArgs &a0, int rows, int mode, hipStream_t s) {
+  if (mode != 0 && mode != 1) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.cls[0] = a.cls[1];
+  a.E = 0;
+  a.split = 1;
+  a.sub_rows = 1 << 30;
+  a.dense_rows = rows;
+  a.NTn = col_tiles_host(a.cls[1].N, kGemmBN, mode == 0);
+  constexpr int DBM = kGemmBM / kGemmDownSplit;
+  const int BMv = mode == 0 ? kGemmBM : DBM;
+  const int64_t work = static_cast<int64_t>((rows + BMv - 1) / BMv) * a.NTn;
+  const unsigned grid = static_cast<unsigned>((work + 7) / 8 * 8);
+  if (grid == 0) return hipSuccess;
+  const dim3 block(128 * kGemmWN);
+  if (mode == 0)
+    hipLaunchKernelGGL((gemm_bf16_dense_kernel<0, kGemmBM, kGemmBK, kGemmStages, kGemmWN>),
+                       dim3(grid), block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_dense_kernel<1, DBM, kGemmBK, kGemmDownStages, kGemmWN>),
+                       dim3(grid), block, 0, s, a);
   return hipGetLastError();
 }
 

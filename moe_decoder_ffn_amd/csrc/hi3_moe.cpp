@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace hi3;
@@ -49,6 +51,54 @@ struct Recorder {
 // eps must be a finite number >= 0.
 bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }
 
+// One side stream per device (default priority) with a fork and a join
+// event, created on first use and kept until the process ends (no device
+// memory). The forward runs the shared expert's GEMMs there while the
+// routing runs on the caller's stream; a forward holds the device's mutex
+// while it enqueues, so concurrent callers cannot re-record its events.
+struct SideStream {
+  std::mutex m;
+  bool tried = false, ok = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+
+// The side stream of the device of stream s (created on first use), or null
+// when there is none (an unknown device, or its creation failed: the caller
+// then keeps everything on s). Called with no lock held.
+SideStream *side_stream_for(hipStream_t s) {
+  int dev = -1, cur = -1;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (hipGetDevice(&cur) != hipSuccess || cur != dev) return nullptr;
+  SideStream &ss = g_side[dev];
+  std::lock_guard<std::mutex> lk(ss.m);
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return ss.ok ? &ss : nullptr;
+}
+
+bool shared_on_side(const Plan &p, bool has_pad, bool save) {
+  return kOverlapShared && !has_pad && !save && p.dtype == kBF16 && p.BM == kGemmBM;
+}
+
+// Joins the side stream into s when a forward leaves early on an error, so
+// that nothing enqueued after the call can overtake the side stream's work.
+struct SideJoin {
+  SideStream *side = nullptr;
+  hipStream_t s = nullptr;
+  ~SideJoin() {
+    if (!side) return;
+    (void)hipEventRecord(side->join, side->s);
+    (void)hipStreamWaitEvent(s, side->join, 0);
+  }
+};
+
 // norm_weight != null: the block's RMSNorm runs first (x is the residual
 // stream h) and the combine adds h back; otherwise x feeds the layer directly.
 int forward_impl(const void *x, const void *norm_weight, float eps, const float *w_router,
@@ -76,6 +126,15 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+  // The shared expert's GEMMs on the side stream, alongside the routing:
+  // when every row is real (its rows are then 0 .. T-1 and need nothing
+  // from the routing), on the default tiles, outside the activation-saving
+  // forward (whose layout keeps the shared rows in the grouped list).
+  SideStream *side = nullptr;
+  if (shared_on_side(p, pad_mask != nullptr, save)) side = side_stream_for(s);
+  std::unique_lock<std::mutex> side_lock;
+  if (side) side_lock = std::unique_lock<std::mutex>(side->m);
+  SideJoin side_join;  // armed at the fork, disarmed at the join
   const void *resid = nullptr;
   if (norm_weight) {
     NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
@@ -83,6 +142,26 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     resid = x;
     x = at(p.xn);
   }
+  // fork: the side stream starts after everything enqueued on s so far;
+  // it runs the shared expert's rows, the tokens 0 .. T-1 in order
+  // (measured: forking here beats forking after the router or the
+  // scatter, though the shared GEMM's blocks then delay the routing's)
+  if (side) {
+    HI3_TRY(hipEventRecord(side->fork, s));
+    HI3_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
+    side_join.side = side;
+    side_join.s = s;
+    GemmArgs us{};
+    us.cls[1] = GemmClass{x, H, nullptr, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
+    HI3_TRY(launch_gemm_dense(us, static_cast<int>(T), 0, side->s));
+    GemmArgs ds{};
+    ds.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
+    HI3_TRY(launch_gemm_dense(ds, static_cast<int>(T), 1, side->s));
+    HI3_TRY(hipEventRecord(side->join, side->s));
+  }
+  // the main list holds the shared group's row tiles only when the side
+  // stream does not run them
+  const int main_tiles = p.max_tiles - (side ? static_cast<int>((T + p.BM - 1) / p.BM) : 0);
   int32_t *idx = topk_idx && !save ? topk_idx : static_cast<int32_t *>(at(p.idx));
   float *wts = topk_w && !save ? topk_w : static_cast<float *>(at(p.wts));
   int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
@@ -106,6 +185,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
               static_cast<int32_t *>(at(p.eoff)), expert_counts,
               static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
               static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
+  sa.no_shared = side ? 1 : 0;
   HI3_TRY(launch_scan(sa, s));
   // 2: stable slots
   rec.at(2);
@@ -126,7 +206,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   up.tiles = tiles;
   up.gto = gto;
   up.E = E;
-  HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
+  HI3_TRY(launch_gemm_upgate(up, main_tiles, p.BM, dtype, s));
   // 4: grouped down projection
   rec.at(4);
   GemmArgs dn{};
@@ -135,9 +215,13 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   dn.tiles = tiles;
   dn.gto = gto;
   dn.E = E;
-  HI3_TRY(launch_gemm_down(dn, p.max_tiles, p.BM, dtype, s));
-  // 5: combine
+  HI3_TRY(launch_gemm_down(dn, main_tiles, p.BM, dtype, s));
+  // 5: combine (after the shared expert's output, when the side stream made it)
   rec.at(5);
+  if (side) {
+    side_join.side = nullptr;
+    HI3_TRY(hipStreamWaitEvent(s, side->join, 0));
+  }
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                  slotof, vidx, wts, pad_mask, T, H, K, out, resid};
   HI3_TRY(launch_combine(ca, dtype, s));
@@ -495,6 +579,13 @@ int hi3_moe_rmsnorm(const void *x, const void *weight, float eps, const uint8_t 
   NormArgs na{x, weight, pad_mask, T, H, eps, xn};
   HI3_TRY(launch_rmsnorm(na, dtype, static_cast<hipStream_t>(hip_stream)));
   return HI3_OK;
+}
+
+int hi3_moe_forward_shared_on_side(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                                   int32_t I_shared, int32_t dtype, int32_t has_pad_mask) {
+  if (check_sizes(T, H, E, K, I, I_shared, dtype, true) != HI3_OK || T == 0) return 0;
+  return shared_on_side(make_plan(T, H, E, K, I, I_shared, dtype), has_pad_mask != 0, false)
+             ? 1 : 0;
 }
 
 size_t hi3_moe_backward_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,

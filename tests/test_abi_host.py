@@ -143,6 +143,19 @@ def test_instrumented_requires_events():
     assert f(*args, None) == m.HI3_E_NULL
 
 
+def test_shared_on_side_query():
+    q = m.hi3_moe_forward_shared_on_side
+    # bf16, no padding mask, enough routed rows for the default tiles
+    assert q(4131, 4096, 64, 8, 3072, 3072, 1, False)
+    assert q(700, 512, 8, 2, 256, 192, 1, False)
+    assert not q(4131, 4096, 64, 8, 3072, 3072, 1, True)    # padding mask
+    assert not q(4131, 4096, 64, 8, 3072, 3072, 0, False)   # fp32
+    assert not q(512, 4096, 64, 8, 3072, 3072, 1, False)    # few rows: streaming tiles
+    assert not q(0, 4096, 64, 8, 3072, 3072, 1, False)      # no rows
+    assert not q(4131, 4096, 64, 8, 3072, 0, 1, False)      # rejected sizes
+    assert not q(4131, 4100, 64, 8, 3072, 3072, 1, False)
+
+
 def test_package_has_no_fallback():
     # the binding calls the library for everything; nothing under oracle/ is
     # imported by the product package

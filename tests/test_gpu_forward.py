@@ -209,6 +209,55 @@ def test_forward_deterministic():
         assert np.array_equal(u, v)
 
 
+def _hip_events(n):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    return hip, evs
+
+
+@pytest.mark.parametrize("T,E,K,Is", [(700, 8, 2, 192), (999, 64, 8, 320), (4131, 64, 8, 256)])
+def test_forward_shared_side_stream_same_bits(T, E, K, Is):
+    """With no padding mask the shared expert's GEMMs run on the side stream
+    (dense launches over rows 0 .. T-1); an all-zero mask keeps them in the
+    grouped list on the caller's stream. Both tile the shared rows alike, so
+    every output bit, route and count must match, and the instrumented
+    forward (the same streams as the plain one) must match too."""
+    import moe_decoder_ffn_amd as m
+    shape = wk.LayerShape(H=512, E=E, K=K, I=256, Is=Is, dtype=wk.BF16)
+    assert m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.BF16, False)
+    assert not m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.BF16, True)
+    assert not m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.F32, False)
+    d = upload(wk.make_inputs(wk.custom(shape, (T,)), 11))
+    side = gpu_forward(d, K)
+    one = gpu_forward(d, K, pad=np.zeros(T, np.uint8))
+    for u, v in zip(side, one):
+        assert np.array_equal(u, v)
+    x = d["x"]
+    out = torch.zeros_like(x)
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((E,), dtype=torch.int32, device="cuda")
+    ws = m.workspace_for(x, E, K, shape.I, Is)
+    hip, evs = _hip_events(m.HI3_NUM_STAGES + 1)
+    try:
+        m.hi3_moe_forward_instrumented(x, d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
+                                       None, K, out, idx, w, cnt, ws, evs,
+                                       torch.cuda.current_stream())
+        torch.cuda.synchronize()
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
+    for u, v in zip(side, (out, idx, w, cnt)):
+        assert np.array_equal(u, to_host(v))
+
+
 # ---------------------------------------------------------------- full size
 
 @pytest.fixture(scope="module")
