@@ -141,7 +141,9 @@ int hi3_moe_dispatch(const int32_t *topk_idx, const uint8_t *pad_mask, const voi
  * as usual. The library creates that stream (default priority) and its two
  * events on the device's first such call and keeps them until the process
  * ends; they hold no device memory. Calls from several host threads
- * enqueue one at a time (a mutex per device).
+ * enqueue one at a time (a mutex per device). The first such call on a
+ * device creates them, which a stream capture may not allow: make one
+ * call before capturing a forward into a graph.
  *   x                [T, H] dtype.
  *   w_router         [E, H] fp32.
  *   w_up_gate        [E, 2*I, H] dtype; rows [0, I) up, [I, 2I) gate.
