@@ -258,6 +258,48 @@ def test_forward_shared_side_stream_same_bits(T, E, K, Is):
         assert np.array_equal(u, to_host(v))
 
 
+def test_forward_concurrent_host_threads():
+    """Two host threads, each on a stream of its own, enqueue forwards at the
+    same time (both use the device's one side stream and its events, behind
+    the library's mutex): every result matches a single-threaded forward bit
+    for bit."""
+    import threading
+    import moe_decoder_ffn_amd as m
+    shape = wk.LayerShape(H=512, E=64, K=8, I=256, Is=320, dtype=wk.BF16)
+    cases = ((999, 21), (1500, 22))
+    for T, _ in cases:
+        assert m.hi3_moe_forward_shared_on_side(T, shape.H, shape.E, shape.K, shape.I, shape.Is,
+                                                wk.BF16, False)
+    inputs = [upload(wk.make_inputs(wk.custom(shape, (T,)), seed)) for T, seed in cases]
+    ref = [gpu_forward(d, shape.K) for d in inputs]
+    results = [None, None]
+    errors = []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream()
+            d = inputs[i]
+            with torch.cuda.stream(st):
+                outs = [m.moe_forward(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
+                                      shape.K, return_routes=True) for _ in range(4)]
+            st.synchronize()
+            results[i] = [[to_host(t) for t in o] for o in outs]
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for i in range(2):
+        assert results[i] is not None
+        for o in results[i]:
+            for u, v in zip(ref[i], o):
+                assert np.array_equal(u, v)
+
+
 # ---------------------------------------------------------------- full size
 
 @pytest.fixture(scope="module")
