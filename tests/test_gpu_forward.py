@@ -222,15 +222,17 @@ def _hip_events(n):
     return hip, evs
 
 
-@pytest.mark.parametrize("T,E,K,Is", [(700, 8, 2, 192), (999, 64, 8, 320), (4131, 64, 8, 256)])
-def test_forward_shared_side_stream_same_bits(T, E, K, Is):
+@pytest.mark.parametrize("T,E,K,Is,H", [(700, 8, 2, 192, 512), (999, 64, 8, 320, 512),
+                                        (4131, 64, 8, 256, 512), (1000, 8, 2, 192, 320)])
+def test_forward_shared_side_stream_same_bits(T, E, K, Is, H):
     """With no padding mask the shared expert's GEMMs run on the side stream
     (dense launches over rows 0 .. T-1); an all-zero mask keeps them in the
     grouped list on the caller's stream. Both tile the shared rows alike, so
     every output bit, route and count must match, and the instrumented
-    forward (the same streams as the plain one) must match too."""
+    forward (the same streams as the plain one) must match too. H = 320
+    leaves the down projections a partial column tile and 5 k steps."""
     import moe_decoder_ffn_amd as m
-    shape = wk.LayerShape(H=512, E=E, K=K, I=256, Is=Is, dtype=wk.BF16)
+    shape = wk.LayerShape(H=H, E=E, K=K, I=256, Is=Is, dtype=wk.BF16)
     assert m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.BF16, False)
     assert not m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.BF16, True)
     assert not m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.F32, False)
