@@ -357,9 +357,8 @@ const char *hi3_moe_backward_stage_name(int stage);
 /*
  * 1 when hi3_moe_forward (and its instrumented and block variants) with
  * these sizes runs the shared expert's GEMMs on the side stream described
- * at hi3_moe_forward, else 0 (also for sizes the forward rejects): bf16,
- * no padding mask, and enough routed rows for the default GEMM tiles.
- * Host-only.
+ * at hi3_moe_forward, else 0 (also for sizes the forward rejects): bf16
+ * and no padding mask. Host-only.
  */
 int hi3_moe_forward_shared_on_side(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
                                    int32_t I_shared, int32_t dtype, int32_t has_pad_mask);

@@ -83,8 +83,11 @@ SideStream *side_stream_for(hipStream_t s) {
   return ss.ok ? &ss : nullptr;
 }
 
+// Whether a forward runs the shared expert on the side stream: bf16, every
+// row real, not the activation-saving forward (any tile plan: the dense
+// launches take 256-row tiles of their own).
 bool shared_on_side(const Plan &p, bool has_pad, bool save) {
-  return kOverlapShared && !has_pad && !save && p.dtype == kBF16 && p.BM == kGemmBM;
+  return kOverlapShared && !has_pad && !save && p.dtype == kBF16;
 }
 
 // Joins the side stream into s when a forward leaves early on an error, so
@@ -128,8 +131,8 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
   // The shared expert's GEMMs on the side stream, alongside the routing:
   // when every row is real (its rows are then 0 .. T-1 and need nothing
-  // from the routing), on the default tiles, outside the activation-saving
-  // forward (whose layout keeps the shared rows in the grouped list).
+  // from the routing), outside the activation-saving forward (whose layout
+  // keeps the shared rows in the grouped list).
   SideStream *side = nullptr;
   if (shared_on_side(p, pad_mask != nullptr, save)) side = side_stream_for(s);
   std::unique_lock<std::mutex> side_lock;

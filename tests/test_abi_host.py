@@ -145,12 +145,13 @@ def test_instrumented_requires_events():
 
 def test_shared_on_side_query():
     q = m.hi3_moe_forward_shared_on_side
-    # bf16, no padding mask, enough routed rows for the default tiles
+    # bf16 and no padding mask, whatever the tile plan
     assert q(4131, 4096, 64, 8, 3072, 3072, 1, False)
     assert q(700, 512, 8, 2, 256, 192, 1, False)
+    assert q(512, 4096, 64, 8, 3072, 3072, 1, False)        # few rows: streaming tiles
+    assert q(1, 4096, 64, 8, 3072, 3072, 1, False)
     assert not q(4131, 4096, 64, 8, 3072, 3072, 1, True)    # padding mask
     assert not q(4131, 4096, 64, 8, 3072, 3072, 0, False)   # fp32
-    assert not q(512, 4096, 64, 8, 3072, 3072, 1, False)    # few rows: streaming tiles
     assert not q(0, 4096, 64, 8, 3072, 3072, 1, False)      # no rows
     assert not q(4131, 4096, 64, 8, 3072, 0, 1, False)      # rejected sizes
     assert not q(4131, 4100, 64, 8, 3072, 3072, 1, False)
