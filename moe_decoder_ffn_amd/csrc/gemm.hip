@@ -28,7 +28,10 @@
 // gradient through the down projection (mode 2) runs each listed row tile as
 // `split` blocks of sub_rows rows. The grid is sized for the largest
 // possible tile count; surplus blocks exit. Block b runs on XCD b % 8 (the
-// hardware's round-robin); how jobs map to blocks is resolve_job's.
+// hardware's round-robin); how jobs map to blocks is resolve_job's. When no
+// row is padding, the forward runs the shared expert alone instead, as dense
+// launches over its rows 0 .. T-1 with no tile list (gemm_bf16_dense_kernel,
+// resolve_dense), on a stream beside the routing.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
