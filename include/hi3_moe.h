@@ -32,9 +32,11 @@
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless stated otherwise; tensors are dense,
  *    row-major, in the layouts given; every pointer must be 16-byte aligned.
- *  - The caller owns every buffer. The library allocates no device memory,
- *    keeps no pointer after returning and has no global mutable state: calls
- *    on different streams with different workspaces may run concurrently.
+ *  - The caller owns every buffer. The library allocates no device memory
+ *    and keeps no pointer after returning; its only global state is the
+ *    forward's side stream and its two events per device (see
+ *    hi3_moe_forward), guarded by a mutex: calls on different streams with
+ *    different workspaces may run concurrently.
  *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream)
  *    and the call returns without waiting. There is no device-to-host
  *    synchronisation inside any call.
