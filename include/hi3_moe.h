@@ -175,7 +175,8 @@ int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
  * the same streams as hi3_moe_forward: when the shared expert runs on the
  * side stream, the GEMM stages time the routed experts alone, and the
  * shared expert's GEMMs run during the routing stages and the first GEMM.
- * stage_events must not be NULL.
+ * stage_events must not be NULL; an entry that is NULL is not recorded (a
+ * caller timing one stage passes only the two events around it).
  */
 int hi3_moe_forward_instrumented(const void *x, const float *w_router,
                                  const void *w_up_gate, const void *w_down,

@@ -38,8 +38,9 @@ struct Recorder {
   void *const *ev;
   hipStream_t s;
   bool ok = true;
-  void at(int i) {
-    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) != hipSuccess) ok = false;
+  void at(int i) {  // NULL entries are skipped
+    if (ev && ev[i] && hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) != hipSuccess)
+      ok = false;
   }
 };
 
