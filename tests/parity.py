@@ -14,7 +14,12 @@ Rules (all against the oracle on the same seeded inputs):
   ids -1, weights 0.
 * Outputs. max |gpu - oracle| over the compared real rows must be at most
   2e-2 * RMS(oracle output) for bf16 layers and 1e-5 * RMS for fp32 layers,
-  against the oracle's fp64 value before the final rounding.
+  against the oracle's fp64 value before the final rounding. For bf16 this
+  literal bar applies wherever the oracle's own correctly rounded output
+  meets it (max |bf16(exact) - exact| <= 2e-2 RMS over the compared rows);
+  only where even that misses the bar (an output element so far above the
+  RMS that half a bf16 ulp exceeds 2e-2 RMS) may an element instead be
+  within one bf16 ulp of the exact value.
 * Integer work (counts, offsets, permutations, gathered rows) is compared
   bit for bit.
 
@@ -32,6 +37,8 @@ import workloads as wk
 GAP_TOL = 1e-4
 ROUTE_W_TOL = 2e-5
 OUT_TOL = {wk.BF16: 2e-2, wk.F32: 1e-5}
+# per-term relative bound of the bf16 gradients (check_grad)
+GRAD_REL = 3 * 2.0 ** -8
 
 
 def to_dev(a, device="cuda"):
@@ -109,10 +116,11 @@ def bf16_ulp(v):
     return 2.0 ** (e - 7)
 
 
-def check_output(gpu_rows, exact_rows, dtype, what=""):
-    """Asserts the output rule above; returns max |err| / RMS."""
+def check_output(gpu_rows, exact_rows, dtype, what="", stats=None):
+    """Asserts the output rule above; returns max |err| / RMS. stats (a
+    dict), when given, receives the rule applied and the measured ratios."""
     g = as_f64(gpu_rows)
-    rms = float(np.sqrt(np.mean(exact_rows ** 2)))
+    rms = float(np.sqrt(np.mean(exact_rows ** 2))) if exact_rows.size else 0.0
     assert np.isfinite(g).all(), f"{what}: non-finite output"
     if g.size == 0:
         return 0.0
@@ -120,32 +128,52 @@ def check_output(gpu_rows, exact_rows, dtype, what=""):
     err = float(diff.max())
     if dtype == wk.F32:
         tol = OUT_TOL[dtype] * rms
+        rule = "1e-5 * RMS"
         assert err <= tol, f"{what}: max err {err:.4g} > {tol:.4g} (1e-5 * RMS {rms:.4g})"
     else:
-        bound = np.maximum(OUT_TOL[dtype] * rms, bf16_ulp(exact_rows))
-        bad = np.argwhere(diff > bound)
-        assert bad.size == 0, (f"{what}: {len(bad)} elements outside max(2e-2 * RMS, 1 ulp); "
-                               f"first {bad[:3].tolist()}, max err / RMS {err / rms:.4f}")
+        # how far the oracle's own output moves when rounded once to bf16
+        rounding = float(np.max(np.abs(as_f64(oracle.round_bf16(exact_rows)) - exact_rows)))
+        if rounding <= OUT_TOL[dtype] * rms:
+            rule = "literal: max err <= 2e-2 * RMS"
+            assert err <= OUT_TOL[dtype] * rms, (
+                f"{what}: max err / RMS {err / rms:.4f} > 2e-2 (the rounded oracle output "
+                f"itself is within {rounding / rms:.4f} * RMS)")
+        else:
+            rule = "max(2e-2 * RMS, 1 ulp): the rounded oracle output misses 2e-2 * RMS"
+            bound = np.maximum(OUT_TOL[dtype] * rms, bf16_ulp(exact_rows))
+            bad = np.argwhere(diff > bound)
+            assert bad.size == 0, (f"{what}: {len(bad)} elements outside max(2e-2 * RMS, 1 ulp); "
+                                   f"first {bad[:3].tolist()}, max err / RMS {err / rms:.4f}")
         erms = float(np.sqrt(np.mean(diff ** 2)))
         assert erms <= 5e-3 * rms, f"{what}: RMS error {erms / rms:.4g} * RMS"
+        if stats is not None:
+            stats["oracle_rounding_over_rms"] = rounding / rms
+            stats["rms_err_over_rms"] = erms / rms
+    if stats is not None:
+        stats.update(rule=rule, max_err_over_rms=err / rms, rms=rms, elements=int(g.size))
     return err / rms
 
 
 def check_grad(gpu, exact, mag, dtype, what=""):
     """Gradient rule (the backward's outputs): fp32 layers as the forward
     (max |err| <= 1e-5 RMS). bf16 layers, every element:
-        |err| <= ulp(exact) + 2^-8 * mag
+        |err| <= ulp(exact) + GRAD_REL * mag,  GRAD_REL = 3 * 2^-8
     where mag is the sum of the absolute values of the terms the oracle sums
-    into that element: each term reaches the GPU through at most two bf16
-    roundings of relative size <= 2^-9 (an MFMA operand and its producer)
-    and fp32 sums, and the result is rounded once more (<= 1 ulp of the
-    exact value, allowing for a binade change). Plus, for the whole tensor,
-    RMS error <= 5e-3 RMS: the roundings are unbiased, so a systematic
-    mistake (a missing or doubled row) shows there even where the per-element
-    worst case is wide. Differences below 2^-16 of the tensor's largest
-    magnitude are not resolved: the oracle's router values are fp32, and its
-    evaluation of the softmax chain leaves residues of that order where the
-    exact derivative is zero (the logits of unselected experts).
+    into that element. Each term differs from the oracle's by at most three
+    bf16 roundings of relative size <= 2^-8 (bf16's unit roundoff, 8
+    significant bits): at most two on the GPU's path (an MFMA operand and
+    its producer), and, for terms holding the SwiGLU activation h, the
+    oracle's own rounding of h from the exact pre-activation, which may fall
+    on the other side of a rounding midpoint than the GPU's rounding from
+    its fp32 pre-activation (the two h then differ by one ulp); fp32 sums add
+    far less. The result is rounded once more (<= 1 ulp of the exact value,
+    allowing for a binade change). Plus, for the whole tensor, RMS error <=
+    5e-3 RMS: the roundings are unbiased, so a systematic mistake (a missing
+    or doubled row) shows there even where the per-element worst case is
+    wide. Differences below 2^-16 of the tensor's largest magnitude are not
+    resolved: the oracle's router values are fp32, and its evaluation of the
+    softmax chain leaves residues of that order where the exact derivative is
+    zero (the logits of unselected experts).
     Returns max |err| / RMS."""
     g = as_f64(gpu)
     assert np.isfinite(g).all(), f"{what}: non-finite output"
@@ -158,14 +186,44 @@ def check_grad(gpu, exact, mag, dtype, what=""):
         tol = OUT_TOL[dtype] * rms
         assert err <= tol, f"{what}: max err {err:.4g} > {tol:.4g} (1e-5 * RMS {rms:.4g})"
     else:
-        bound = bf16_ulp(exact) + 2.0 ** -8 * mag + 2.0 ** -16 * float(np.max(mag))
+        bound = bf16_ulp(exact) + GRAD_REL * mag + 2.0 ** -16 * float(np.max(mag))
         bad = np.argwhere(diff > bound)
-        assert bad.size == 0, (f"{what}: {len(bad)} elements outside ulp + 2^-8 * sum|terms|; "
+        assert bad.size == 0, (f"{what}: {len(bad)} elements outside ulp + 3 * 2^-8 * sum|terms|; "
                                f"first {bad[:3].tolist()}, worst err / bound "
                                f"{float((diff / bound).max()):.3f}")
         erms = float(np.sqrt(np.mean(diff ** 2)))
         assert erms <= 5e-3 * rms, f"{what}: RMS error {erms / rms:.4g} * RMS"
     return err / max(rms, 1e-300)
+
+
+def check_grad_chunked(gpu, exact, mag, dtype, what=""):
+    """check_grad for a large gradient, one slice of the first axis at a
+    time (the same per-element bound; the RMS error rule over the whole
+    tensor from accumulated sums), so that no full-size float64 temporary
+    is made. Returns max |err| / RMS."""
+    assert dtype == wk.BF16
+    mmax = float(np.max(mag))
+    sq_err = sq_ref = 0.0
+    worst = 0.0
+    n = 0
+    for i in range(exact.shape[0]):
+        g = as_f64(gpu[i])
+        e = exact[i]
+        assert np.isfinite(g).all(), f"{what}[{i}]: non-finite output"
+        diff = np.abs(g - e)
+        bound = bf16_ulp(e) + GRAD_REL * mag[i] + 2.0 ** -16 * mmax
+        bad = np.argwhere(diff > bound)
+        assert bad.size == 0, (f"{what}[{i}]: {len(bad)} elements outside ulp + 3 * 2^-8 * "
+                               f"sum|terms|; first {bad[:3].tolist()}, worst err / bound "
+                               f"{float((diff / bound).max()):.3f}")
+        sq_err += float(np.sum(diff ** 2))
+        sq_ref += float(np.sum(e ** 2))
+        worst = max(worst, float(diff.max()))
+        n += e.size
+    rms = np.sqrt(sq_ref / n)
+    erms = np.sqrt(sq_err / n)
+    assert erms <= 5e-3 * rms, f"{what}: RMS error {erms / rms:.4g} * RMS"
+    return worst / max(rms, 1e-300)
 
 
 def oracle_rows(d, K, rows, idx, w, pad=None):
