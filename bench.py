@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE feed-forward layer on one MI355X.
 
-One step = one hi3_moe_forward call over one batch of synthetic tokens: the
-router, dispatch, grouped [up; gate] + SwiGLU GEMM, grouped down GEMM,
-shared expert and combine. Inputs are resident in HBM before timing starts.
+One step = one hi3_moe_forward_overlap call over one batch of synthetic
+tokens: the router, dispatch, grouped [up; gate] + SwiGLU GEMM, grouped down
+GEMM, shared expert (on a second stream of the caller's where every row is
+real) and combine. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s over the real tokens (the metric), with the
 layer's TFLOP/s and fraction of the bf16 MFMA peak, the roofline entry of the
 dominant kernel (its duration measured with HIP events recorded on the
-launch stream inside the timed region), per-stage times, and the CPU oracle
-timed on a bounded sample of the same workload on this host's cores.
+launch stream inside the timed region), per-stage times with the side stream
+and on one stream (where each kernel has the GPU to itself), the achievable
+peaks measured on this GPU next to the published ones, the batch's per-expert
+load, and the CPU oracle timed on a bounded sample of the same workload on
+this host's cores.
 """
 import argparse
 import ctypes
@@ -154,6 +158,74 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def achievable_peaks(m):
+    """What this GPU sustains in practice, beside the published peaks: the
+    library's matrix-core probe (bf16 MFMA chains, no memory traffic), a
+    dense bf16 GEMM through torch (hipBLASLt), and a device copy through
+    torch (bytes read + written per second)."""
+    import torch
+    hip = HipEvents()
+    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    st = torch.cuda.current_stream()
+    ev = hip.create(2)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        hip.hip.hipEventRecord(ev[0], ctypes.c_void_p(st.cuda_stream))
+        for _ in range(reps):
+            fn()
+        hip.hip.hipEventRecord(ev[1], ctypes.c_void_p(st.cuda_stream))
+        return hip.elapsed_ms(ev[0], ev[1]) / reps
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    # operands with the statistics of the layer's (bf16 values of N(0, 1)),
+    # whose bit switching sets the clock the matrix cores hold
+    bits = torch.randn(8192, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty(1024 * 4, dtype=torch.float32, device="cuda")
+    flop = [0]
+
+    def probe():
+        flop[0] = m.hi3_moe_probe_mfma_bf16(bits, out, 1024, 4096)
+
+    mfma_ms = timed(probe, 3)
+    n = 8192
+    a = (torch.randn((n, n), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    b = (torch.randn((n, n), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    gemm_ms = timed(lambda: torch.mm(a, b, out=c), 5)
+    del a, b, c
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src), 5)
+    del src, dst
+    hip.destroy(ev)
+    return {"mfma_bf16_probe_tflops": round(flop[0] / (mfma_ms * 1e-3) / 1e12, 1),
+            "hipblaslt_bf16_gemm_8192_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "device_copy_gbs": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)}
+
+
+def expert_load(cnt):
+    """Per-expert routed rows: how skewed the routing of this batch is."""
+    c = np.asarray(cnt, dtype=np.float64)
+    mean = c.mean()
+    return {"max_over_mean": round(float(c.max() / mean), 3), "min": int(c.min()),
+            "max": int(c.max()), "experts_below_1pct_of_mean": int((c < 0.01 * mean).sum())}
+
+
 def cpu_baseline(wl, d, K, target_s):
     """The CPU oracle as it stands, on a bounded sample of real tokens."""
     import oracle
@@ -174,6 +246,7 @@ def cpu_baseline(wl, d, K, target_s):
         total_t += time.perf_counter() - t0
         total_n += n2
     return {"value": total_n / total_t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{total_n} real tokens of {wl.name} (full layer per token, fp64 C, "
                       f"OpenMP over tokens), {total_t:.1f} s"}
 
@@ -452,6 +525,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the achievable peaks (probe, library GEMM, copy)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--entry", default="forward",
@@ -496,15 +571,17 @@ def main():
     ws = m.workspace_for(x, sh.E, sh.K, sh.I, sh.Is)
     log(f"[bench] workspace {ws.numel() / 2**20:.0f} MiB")
     stream = torch.cuda.current_stream()
+    # the caller's second stream for hi3_moe_forward_overlap (default priority)
+    side_stream = torch.cuda.Stream()
+    wargs = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
 
-    def step(events=None):
+    def step(events=None, side=side_stream):
         if events is None:
-            m.hi3_moe_forward(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"],
-                              pad, sh.K, out, idx, wts, cnt, ws, stream)
+            m.hi3_moe_forward_overlap(x, *wargs, pad, sh.K, out, idx, wts, cnt, ws,
+                                      side_stream=side, stream=stream)
         else:
-            m.hi3_moe_forward_instrumented(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
-                                           dd["ws2"], pad, sh.K, out, idx, wts, cnt, ws,
-                                           events, stream)
+            m.hi3_moe_forward_instrumented(x, *wargs, pad, sh.K, out, idx, wts, cnt, ws,
+                                           events, stream=stream, side_stream=side)
 
     if args.entry == "norm_residual":
         norm_residual_bench(args, m, wl, d, dd, pad, ws, stream)
@@ -540,24 +617,32 @@ def main():
     for pr in pairs:
         hip.destroy(pr)
 
-    # per-stage times: as many calls with every stage event, after the
-    # timed region
-    evsets = [hip.create(ns + 1) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evsets[i])
-    torch.cuda.synchronize()
-    log(f"[bench] {args.steps} per-stage steps done")
+    def stage_pass(side):
+        """As many calls as timed steps with every stage's events, after the
+        timed region; returns per-stage ms and per-call ms."""
+        evsets = [hip.create(ns + 1) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(evsets[i], side)
+        torch.cuda.synchronize()
+        st_ms = np.zeros(ns)
+        call = []
+        for evs in evsets:
+            for k in range(ns):
+                st_ms[k] += hip.elapsed_ms(evs[k], evs[k + 1])
+            call.append(hip.elapsed_ms(evs[0], evs[ns]))
+        for evs in evsets:
+            hip.destroy(evs)
+        return st_ms / args.steps, call
 
-    stage_ms = np.zeros(ns)
-    step_ms = []
-    for evs in evsets:
-        for s in range(ns):
-            stage_ms[s] += hip.elapsed_ms(evs[s], evs[s + 1])
-        step_ms.append(hip.elapsed_ms(evs[0], evs[ns]))
-    stage_ms /= args.steps
-    for evs in evsets:
-        hip.destroy(evs)
+    # with the side stream (the timed entry point) ...
+    stage_ms, step_ms = stage_pass(side_stream)
+    log(f"[bench] {args.steps} per-stage steps done (side stream)")
+    # ... and on one stream, where every kernel has the GPU to itself: the
+    # routing stages' own times and the grouped GEMMs' own rates (routed and
+    # shared rows in one launch)
+    alone_ms, alone_call = stage_pass(None)
+    log(f"[bench] {args.steps} per-stage steps done (one stream)")
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_s = wl.T_valid / (ms_per_step * 1e-3)
@@ -569,35 +654,61 @@ def main():
     side = m.hi3_moe_forward_shared_on_side(wl.T, sh.H, sh.E, sh.K, sh.I, sh.Is, sh.dtype,
                                             pad is not None)
     gf = gemm_flops(wl, shared=not side)
+    gf_all = gemm_flops(wl, shared=True)
     sb = stage_bytes(wl)
-    stages = {}
-    for s, name in enumerate(names):
-        e = {"us": round(stage_ms[s] * 1e3, 2)}
-        if name in gf and stage_ms[s] > 0:
-            e["tflops"] = round(gf[name] / (stage_ms[s] * 1e-3) / 1e12, 1)
-            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
-        if name in sb and stage_ms[s] > 0:
-            e["gbs"] = round(sb[name] / (stage_ms[s] * 1e-3) / 1e9, 1)
-            e["frac_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
-        stages[name] = e
-    for name, e in stages.items():
-        log(f"  {name:22s} {e}")
+
+    def stage_table(st_ms, g):
+        out_ = {}
+        for k, name in enumerate(names):
+            e = {"us": round(st_ms[k] * 1e3, 2)}
+            if name in g and st_ms[k] > 0:
+                e["tflops"] = round(g[name] / (st_ms[k] * 1e-3) / 1e12, 1)
+                e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+            if name in sb and st_ms[k] > 0:
+                e["gbs"] = round(sb[name] / (st_ms[k] * 1e-3) / 1e9, 1)
+                e["frac_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+            out_[name] = e
+        return out_
+
+    stages = stage_table(stage_ms, gf)
+    stages_alone = stage_table(alone_ms, gf_all)
+    for name in names:
+        log(f"  {name:22s} side: {stages[name]}  alone: {stages_alone[name]}")
 
     kname = ("gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU, routed experts; the shared "
-             "expert runs as gemm_bf16_dense_kernel<0> on a side stream)" if side else
+             "expert runs as gemm_bf16_dense_kernel<0> on the side stream)" if side else
              "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)")
+    ui = names.index("gemm_up_gate_swiglu")
+    wi = names.index("gemm_down")
     if sh.dtype == wk.BF16 and wl.T_valid * sh.K <= RIDGE_ROWS * sh.E:
         # few rows per expert: the weights are the traffic (HBM roofline)
         gb = upgate_bytes(wl, shared=not side)
         achieved = gb / (dom_ms * 1e-3) / 1e9
-        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(wl.name)}
+        a_alone = upgate_bytes(wl, shared=True) / (alone_ms[ui] * 1e-3) / 1e9
+        roofline_alone = {"kernel": "gemm_bf16_kernel<0> (routed and shared rows, one stream)",
+                          "achieved": round(a_alone, 1), "unit": "GB/s",
+                          "frac": round(a_alone / PEAK_HBM_GBS, 4)}
     else:
         achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
-        roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(wl.name)}
+        a_alone = gf_all[dom] / (alone_ms[ui] * 1e-3) / 1e12
+        roofline_alone = {"kernel": "gemm_bf16_kernel<0> (routed and shared rows, one stream)",
+                          "achieved": round(a_alone, 1), "unit": "TFLOP/s",
+                          "frac": round(a_alone / PEAK_BF16_TFLOPS, 4)}
+    gemm_alone_ms = alone_ms[ui] + alone_ms[wi]
+    gemm_alone = sum(gf_all.values()) / (gemm_alone_ms * 1e-3) / 1e12
+
+    peaks = None
+    if not args.no_peaks:
+        log("[bench] measuring the achievable peaks")
+        peaks = achievable_peaks(m)
+    load = expert_load(to_np(cnt))
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -609,18 +720,32 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if sh.dtype == wk.BF16 else "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "T_valid": wl.T_valid, "H": sh.H,
-                   "E": sh.E, "K": sh.K, "I": sh.I, "I_shared": sh.Is, "seed": args.seed},
+        "config": {"workload": wl.name, "entry": "forward_overlap", "T": wl.T,
+                   "T_valid": wl.T_valid, "H": sh.H, "E": sh.E, "K": sh.K, "I": sh.I,
+                   "I_shared": sh.Is, "seed": args.seed},
         "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        # per call of the per-stage pass, first to last kernel on the stream
+        # per call of the per-stage passes, first to last kernel on the stream
         # (HIP events); the dominant kernel's time (roofline) is the timed
         # steps' own: dominant_kernel_us
         "call_ms": {"median": round(float(np.median(step_ms)), 4),
-                    "min": round(float(np.min(step_ms)), 4)},
+                    "min": round(float(np.min(step_ms)), 4),
+                    "one_stream_median": round(float(np.median(alone_call)), 4)},
         "dominant_kernel_us": round(dom_ms * 1e3, 2),
-        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+        "stages": stages, "stages_one_stream": stages_alone,
+        "roofline": roofline, "roofline_one_stream": roofline_alone,
+        "gemms_one_stream": {"us": round(gemm_alone_ms * 1e3, 1),
+                             "tflops": round(gemm_alone, 1),
+                             "frac_bf16_peak": round(gemm_alone / PEAK_BF16_TFLOPS, 4)},
+        "peaks": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                  "achievable": peaks},
+        "expert_load": load,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def to_np(t):
+    return t.cpu().numpy()
 
 
 if __name__ == "__main__":

@@ -32,11 +32,10 @@
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless stated otherwise; tensors are dense,
  *    row-major, in the layouts given; every pointer must be 16-byte aligned.
- *  - The caller owns every buffer. The library allocates no device memory
- *    and keeps no pointer after returning; its only global state is the
- *    forward's side stream and its two events per device (see
- *    hi3_moe_forward), guarded by a mutex: calls on different streams with
- *    different workspaces may run concurrently.
+ *  - The caller owns every buffer and every stream. The library allocates
+ *    no device memory, keeps no pointer after returning and has no global
+ *    mutable state: calls on different streams with different workspaces
+ *    may run concurrently from any host threads.
  *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream)
  *    and the call returns without waiting. There is no device-to-host
  *    synchronisation inside any call.
@@ -134,18 +133,9 @@ int hi3_moe_dispatch(const int32_t *topk_idx, const uint8_t *pad_mask, const voi
 
 /*
  * The whole layer: router, dispatch, grouped [up; gate] projection with the
- * SwiGLU epilogue, grouped down projection, shared expert, combine.
- * Streams: when hi3_moe_forward_shared_on_side says so, the shared expert's
- * two GEMMs run on a side stream of hip_stream's device (the current
- * device), alongside the routing: it waits for an event recorded on
- * hip_stream when the call starts, and hip_stream waits for its end before
- * the combine, so later work on hip_stream is ordered after the whole call
- * as usual. The library creates that stream (default priority) and its two
- * events on the device's first such call and keeps them until the process
- * ends; they hold no device memory. Calls from several host threads
- * enqueue one at a time (a mutex per device). The first such call on a
- * device creates them, which a stream capture may not allow: make one
- * call before capturing a forward into a graph.
+ * SwiGLU epilogue, grouped down projection, shared expert, combine; every
+ * kernel on hip_stream (the shared expert's rows ride in the grouped
+ * launches as one more group).
  *   x                [T, H] dtype.
  *   w_router         [E, H] fp32.
  *   w_up_gate        [E, 2*I, H] dtype; rows [0, I) up, [I, 2I) gate.
@@ -168,15 +158,42 @@ int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
                     void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
- * hi3_moe_forward with per-stage timing: stage_events holds
- * HI3_NUM_STAGES + 1 hipEvent_t handles created by the caller; event i is
- * recorded on hip_stream just before stage i is enqueued and the last one
- * after the final stage (stage names: hi3_moe_stage_name). Same results and
- * the same streams as hi3_moe_forward: when the shared expert runs on the
- * side stream, the GEMM stages time the routed experts alone, and the
- * shared expert's GEMMs run during the routing stages and the first GEMM.
- * stage_events must not be NULL; an entry that is NULL is not recorded (a
- * caller timing one stage passes only the two events around it).
+ * hi3_moe_forward with the shared expert (model API page, HunyuanImage3Block:
+ * the fused shared expert beside the routed ones) on a second stream of the
+ * caller's: its rows need nothing from the routing, so its two GEMMs run
+ * alongside the router and dispatch. Same arguments, results (bit for bit)
+ * and workspace as hi3_moe_forward, plus:
+ *   side_stream  a hipStream_t of the same device, other than hip_stream, or
+ *                NULL. It is used only when hi3_moe_forward_shared_on_side
+ *                says so (bf16, no padding mask); otherwise, and when NULL or
+ *                equal to hip_stream, the call is exactly hi3_moe_forward.
+ * The side stream waits for an event recorded on hip_stream at the start of
+ * the call, and hip_stream waits for an event recorded on the side stream
+ * before the combine: work enqueued on hip_stream after the call is ordered
+ * after all of it, work enqueued on side_stream after the call is not. The
+ * two events are created and destroyed inside the call (no device memory);
+ * a stream capture of hip_stream takes the side stream's work into the
+ * same graph (fork and join).
+ */
+int hi3_moe_forward_overlap(const void *x, const float *w_router, const void *w_up_gate,
+                            const void *w_down, const void *w_shared_up_gate,
+                            const void *w_shared_down, const uint8_t *pad_mask,
+                            int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                            int32_t I_shared, int32_t dtype, void *out,
+                            int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                            void *workspace, size_t workspace_bytes, void *hip_stream,
+                            void *side_stream);
+
+/*
+ * hi3_moe_forward_overlap (hi3_moe_forward when side_stream is NULL) with
+ * per-stage timing: stage_events holds HI3_NUM_STAGES + 1 hipEvent_t handles
+ * created by the caller; event i is recorded on hip_stream just before stage
+ * i is enqueued and the last one after the final stage (stage names:
+ * hi3_moe_stage_name). Same results as the untimed calls. When the shared
+ * expert runs on the side stream, the GEMM stages time the routed experts
+ * alone, and the shared expert's GEMMs run during the routing stages and the
+ * first GEMM. stage_events must not be NULL; an entry that is NULL is not
+ * recorded (a caller timing one stage passes only the two events around it).
  */
 int hi3_moe_forward_instrumented(const void *x, const float *w_router,
                                  const void *w_up_gate, const void *w_down,
@@ -187,7 +204,7 @@ int hi3_moe_forward_instrumented(const void *x, const float *w_router,
                                  void *out, int32_t *topk_idx, float *topk_w,
                                  int32_t *expert_counts, void *workspace,
                                  size_t workspace_bytes, void *hip_stream,
-                                 void *const *stage_events);
+                                 void *side_stream, void *const *stage_events);
 
 /*
  * The block's RMSNorm ahead of the layer (layers API page, HunyuanRMSNorm:
@@ -358,13 +375,29 @@ int hi3_moe_backward_after_forward(const void *x, const float *w_router,
 const char *hi3_moe_backward_stage_name(int stage);
 
 /*
- * 1 when hi3_moe_forward (and its instrumented and block variants) with
- * these sizes runs the shared expert's GEMMs on the side stream described
- * at hi3_moe_forward, else 0 (also for sizes the forward rejects): bf16
- * and no padding mask. Host-only.
+ * 1 when hi3_moe_forward_overlap (and hi3_moe_forward_instrumented) given a
+ * side stream runs the shared expert's GEMMs on it for these sizes, else 0
+ * (also for sizes the forward rejects): bf16 and no padding mask.
+ * Host-only.
  */
 int hi3_moe_forward_shared_on_side(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
                                    int32_t I_shared, int32_t dtype, int32_t has_pad_mask);
+
+/*
+ * Measurement probe, not part of the layer: the bf16 matrix-core rate the
+ * GPU holds with no memory traffic, reported beside the published dense
+ * peak. Enqueues `blocks` blocks of 256 threads; each wave runs iters x 16
+ * v_mfma_f32_32x32x16_bf16 in four independent chains on operands read once
+ * from `operands` (device, 16-byte aligned, at least 8 KiB of bf16 values:
+ * pass values with the statistics of real operands, since how much the
+ * operands switch sets the clock the matrix cores hold under load).
+ *   out   [blocks * 4] fp32 out (device): one value per wave.
+ * Returns the FLOP the launch performs (> 0) or a negative status
+ * (HI3_E_NULL, HI3_E_SHAPE for blocks or iters <= 0, HI3_E_UNSUPPORTED for
+ * a misaligned pointer, HI3_E_HIP).
+ */
+int64_t hi3_moe_probe_mfma_bf16(const void *operands, float *out, int32_t blocks,
+                                int32_t iters, void *hip_stream);
 
 /* Static name of timed stage i (0 <= i < HI3_NUM_STAGES), else "?". */
 const char *hi3_moe_stage_name(int stage);

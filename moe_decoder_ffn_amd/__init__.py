@@ -31,6 +31,7 @@ EXPORTED = (
     "hi3_moe_route",
     "hi3_moe_dispatch",
     "hi3_moe_forward",
+    "hi3_moe_forward_overlap",
     "hi3_moe_forward_instrumented",
     "hi3_moe_forward_shared_on_side",
     "hi3_moe_rmsnorm",
@@ -44,6 +45,7 @@ EXPORTED = (
     "hi3_moe_backward_norm_residual",
     "hi3_moe_stage_name",
     "hi3_moe_status_string",
+    "hi3_moe_probe_mfma_bf16",
 )
 
 
@@ -69,7 +71,9 @@ def _load():
     fwd = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.hi3_moe_forward.argtypes = fwd
     lib.hi3_moe_forward.restype = ctypes.c_int
-    lib.hi3_moe_forward_instrumented.argtypes = fwd + [P]
+    lib.hi3_moe_forward_overlap.argtypes = fwd + [P]
+    lib.hi3_moe_forward_overlap.restype = ctypes.c_int
+    lib.hi3_moe_forward_instrumented.argtypes = fwd + [P, P]
     lib.hi3_moe_forward_instrumented.restype = ctypes.c_int
     lib.hi3_moe_forward_shared_on_side.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
     lib.hi3_moe_forward_shared_on_side.restype = ctypes.c_int
@@ -95,6 +99,8 @@ def _load():
     lib.hi3_moe_backward_stage_name.restype = ctypes.c_char_p
     lib.hi3_moe_stage_name.argtypes = [ctypes.c_int]
     lib.hi3_moe_stage_name.restype = ctypes.c_char_p
+    lib.hi3_moe_probe_mfma_bf16.argtypes = [P, P, i32, i32, P]
+    lib.hi3_moe_probe_mfma_bf16.restype = i64
     lib.hi3_moe_status_string.argtypes = [ctypes.c_int]
     lib.hi3_moe_status_string.restype = ctypes.c_char_p
     return lib
@@ -118,6 +124,15 @@ def _ptr(t):
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _side(stream):
+    """A side stream argument: None stays NULL (no side stream)."""
+    if stream is None:
+        return None
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -184,14 +199,26 @@ def hi3_moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_d
         topk_idx, topk_w, expert_counts, workspace, stream)))
 
 
+def hi3_moe_forward_overlap(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                            pad_mask, K, out, topk_idx=None, topk_w=None, expert_counts=None,
+                            workspace=None, side_stream=None, stream=None):
+    """side_stream: a second stream (torch.cuda.Stream, raw handle, or None)
+    on which the shared expert may run alongside the routing."""
+    _check(lib.hi3_moe_forward_overlap(*_forward_args(
+        x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
+        topk_idx, topk_w, expert_counts, workspace, stream), _side(side_stream)))
+
+
 def hi3_moe_forward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_gate,
                                  w_shared_down, pad_mask, K, out, topk_idx, topk_w,
-                                 expert_counts, workspace, stage_events, stream=None):
-    """stage_events: sequence of HI3_NUM_STAGES + 1 raw hipEvent_t handles (ints)."""
+                                 expert_counts, workspace, stage_events, stream=None,
+                                 side_stream=None):
+    """stage_events: sequence of HI3_NUM_STAGES + 1 raw hipEvent_t handles (ints);
+    side_stream as for hi3_moe_forward_overlap (None: one stream)."""
     arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
     _check(lib.hi3_moe_forward_instrumented(*_forward_args(
         x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
-        topk_idx, topk_w, expert_counts, workspace, stream), arr))
+        topk_idx, topk_w, expert_counts, workspace, stream), _side(side_stream), arr))
 
 
 def hi3_moe_forward_shared_on_side(T, H, E, K, I, I_shared, dtype, has_pad_mask) -> bool:
@@ -292,6 +319,15 @@ def hi3_moe_stage_name(i) -> str:
     return lib.hi3_moe_stage_name(i).decode()
 
 
+def hi3_moe_probe_mfma_bf16(operands, out, blocks, iters, stream=None) -> int:
+    """Enqueues the matrix-core probe; returns the FLOP of the launch."""
+    r = int(lib.hi3_moe_probe_mfma_bf16(_ptr(operands), _ptr(out), blocks, iters,
+                                        _stream(stream)))
+    if r < 0:
+        raise Hi3Error(r)
+    return r
+
+
 def hi3_moe_status_string(status) -> str:
     return lib.hi3_moe_status_string(status).decode()
 
@@ -306,9 +342,11 @@ def workspace_for(x, E, K, I=0, I_shared=0):
 
 
 def moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, K,
-                pad_mask=None, out=None, workspace=None, return_routes=False):
+                pad_mask=None, out=None, workspace=None, return_routes=False,
+                side_stream=None):
     """Allocates the outputs and the workspace with torch, then calls
-    hi3_moe_forward. Padding rows of a freshly allocated out are zero."""
+    hi3_moe_forward (hi3_moe_forward_overlap when side_stream is given).
+    Padding rows of a freshly allocated out are zero."""
     T, H = x.shape
     E = w_router.shape[0]
     I = w_up_gate.shape[1] // 2
@@ -320,8 +358,13 @@ def moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
     idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
     w = torch.empty((T, K), dtype=torch.float32, device=x.device)
     counts = torch.empty((E,), dtype=torch.int32, device=x.device)
-    hi3_moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
-                    pad_mask, K, out, idx, w, counts, workspace)
+    if side_stream is None:
+        hi3_moe_forward(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                        pad_mask, K, out, idx, w, counts, workspace)
+    else:
+        hi3_moe_forward_overlap(x, w_router, w_up_gate, w_down, w_shared_up_gate,
+                                w_shared_down, pad_mask, K, out, idx, w, counts, workspace,
+                                side_stream)
     if return_routes:
         return out, idx, w, counts
     return out

@@ -86,8 +86,8 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 #ifndef HI3_GEMM_COL_CHUNK
 #define HI3_GEMM_COL_CHUNK 4
 #endif
-// The forward runs the shared expert's GEMMs on a side stream alongside the
-// routing (when every row is real).
+// hi3_moe_forward_overlap runs the shared expert's GEMMs on the caller's side
+// stream alongside the routing (when every row is real).
 #ifndef HI3_OVERLAP_SHARED
 #define HI3_OVERLAP_SHARED 1
 #endif
@@ -125,6 +125,13 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 #define HI3_GEMM_STAGED_STORE 1
 #endif
 constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
+// GEMMs with k-contiguous operands (the forward) issue their direct
+// global -> LDS copies through the compiler's builtin (1) or as inline
+// assembly (0).
+#ifndef HI3_GEMM_DMA_BUILTIN
+#define HI3_GEMM_DMA_BUILTIN 1
+#endif
+constexpr bool kGemmDmaBuiltin = HI3_GEMM_DMA_BUILTIN != 0;
 constexpr bool kGemmDeepB = HI3_GEMM_DEEP_B != 0;
 constexpr bool kOverlapShared = HI3_OVERLAP_SHARED != 0;
 constexpr int kGemmColChunk = HI3_GEMM_COL_CHUNK;

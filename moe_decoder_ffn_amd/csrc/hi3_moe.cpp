@@ -5,8 +5,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <mutex>
-
 #include "common.h"
 
 using namespace hi3;
@@ -52,54 +50,41 @@ struct Recorder {
 // eps must be a finite number >= 0.
 bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }
 
-// One side stream per device (default priority) with a fork and a join
-// event, created on first use and kept until the process ends (no device
-// memory). The forward runs the shared expert's GEMMs there while the
-// routing runs on the caller's stream; a forward holds the device's mutex
-// while it enqueues, so concurrent callers cannot re-record its events.
-struct SideStream {
-  std::mutex m;
-  bool tried = false, ok = false;
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-
-// The side stream of the device of stream s (created on first use), or null
-// when there is none (an unknown device, or its creation failed: the caller
-// then keeps everything on s). Called with no lock held.
-SideStream *side_stream_for(hipStream_t s) {
-  int dev = -1, cur = -1;
-  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (hipGetDevice(&cur) != hipSuccess || cur != dev) return nullptr;
-  SideStream &ss = g_side[dev];
-  std::lock_guard<std::mutex> lk(ss.m);
-  if (!ss.tried) {
-    ss.tried = true;
-    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return ss.ok ? &ss : nullptr;
-}
-
-// Whether a forward runs the shared expert on the side stream: bf16, every
-// row real, not the activation-saving forward (any tile plan: the dense
-// launches take 256-row tiles of their own).
+// Whether a forward given a side stream runs the shared expert there: bf16,
+// every row real, not the activation-saving forward (any tile plan: the
+// dense launches take 256-row tiles of their own).
 bool shared_on_side(const Plan &p, bool has_pad, bool save) {
   return kOverlapShared && !has_pad && !save && p.dtype == kBF16;
 }
 
-// Joins the side stream into s when a forward leaves early on an error, so
-// that nothing enqueued after the call can overtake the side stream's work.
-struct SideJoin {
-  SideStream *side = nullptr;
-  hipStream_t s = nullptr;
-  ~SideJoin() {
-    if (!side) return;
-    (void)hipEventRecord(side->join, side->s);
-    (void)hipStreamWaitEvent(s, side->join, 0);
+// The fork and join of the caller's side stream for one forward: two events
+// made for this call and destroyed when it returns (a destroyed event's
+// pending record and waits still complete). If the call leaves early after
+// the fork, the destructor joins the side stream back into the main stream,
+// so nothing enqueued after the call can overtake the side stream's work.
+struct SideFork {
+  hipStream_t main = nullptr, side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool armed = false;
+  bool make() {
+    return hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess;
+  }
+  bool start() {  // the side stream waits for everything enqueued on main so far
+    if (hipEventRecord(fork, main) != hipSuccess) return false;
+    if (hipStreamWaitEvent(side, fork, 0) != hipSuccess) return false;
+    armed = true;
+    return true;
+  }
+  bool end() {  // main waits for everything enqueued on side so far
+    armed = false;
+    return hipEventRecord(join, side) == hipSuccess &&
+           hipStreamWaitEvent(main, join, 0) == hipSuccess;
+  }
+  ~SideFork() {
+    if (armed) (void)end();
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
   }
 };
 
@@ -111,7 +96,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
                  int32_t E, int32_t K, int32_t I, int32_t Is, int32_t dtype, void *out,
                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts, void *workspace,
                  size_t workspace_bytes, void *hip_stream, void *const *events,
-                 bool save = false) {
+                 bool save = false, void *side_stream = nullptr) {
   if (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !out)
     return HI3_E_NULL;
   int st = check_sizes(T, H, E, K, I, Is, dtype, true);
@@ -130,15 +115,19 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
-  // The shared expert's GEMMs on the side stream, alongside the routing:
-  // when every row is real (its rows are then 0 .. T-1 and need nothing
-  // from the routing), outside the activation-saving forward (whose layout
-  // keeps the shared rows in the grouped list).
-  SideStream *side = nullptr;
-  if (shared_on_side(p, pad_mask != nullptr, save)) side = side_stream_for(s);
-  std::unique_lock<std::mutex> side_lock;
-  if (side) side_lock = std::unique_lock<std::mutex>(side->m);
-  SideJoin side_join;  // armed at the fork, disarmed at the join
+  // The shared expert's GEMMs on the caller's side stream, alongside the
+  // routing: when the caller gives one, every row is real (the shared rows
+  // are then 0 .. T-1 and need nothing from the routing), outside the
+  // activation-saving forward (whose layout keeps the shared rows in the
+  // grouped list).
+  hipStream_t side_s = static_cast<hipStream_t>(side_stream);
+  const bool side = side_s && side_s != s && shared_on_side(p, pad_mask != nullptr, save);
+  SideFork fork;
+  if (side) {
+    fork.main = s;
+    fork.side = side_s;
+    if (!fork.make()) return HI3_E_HIP;
+  }
   const void *resid = nullptr;
   if (norm_weight) {
     NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
@@ -146,22 +135,18 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     resid = x;
     x = at(p.xn);
   }
-  // fork: the side stream starts after everything enqueued on s so far;
-  // it runs the shared expert's rows, the tokens 0 .. T-1 in order
-  // (measured: forking here beats forking after the router or the
-  // scatter, though the shared GEMM's blocks then delay the routing's)
+  // fork: the side stream starts after everything enqueued on s so far and
+  // runs the shared expert's rows, the tokens 0 .. T-1 in order (measured:
+  // forking here beats forking after the router or the scatter, though the
+  // shared GEMM's blocks then delay the routing's)
   if (side) {
-    HI3_TRY(hipEventRecord(side->fork, s));
-    HI3_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
-    side_join.side = side;
-    side_join.s = s;
+    if (!fork.start()) return HI3_E_HIP;
     GemmArgs us{};
     us.cls[1] = GemmClass{x, H, nullptr, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
-    HI3_TRY(launch_gemm_dense(us, static_cast<int>(T), 0, side->s));
+    HI3_TRY(launch_gemm_dense(us, static_cast<int>(T), 0, side_s));
     GemmArgs ds{};
     ds.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
-    HI3_TRY(launch_gemm_dense(ds, static_cast<int>(T), 1, side->s));
-    HI3_TRY(hipEventRecord(side->join, side->s));
+    HI3_TRY(launch_gemm_dense(ds, static_cast<int>(T), 1, side_s));
   }
   // the main list holds the shared group's row tiles only when the side
   // stream does not run them
@@ -222,10 +207,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   HI3_TRY(launch_gemm_down(dn, main_tiles, p.BM, dtype, s));
   // 5: combine (after the shared expert's output, when the side stream made it)
   rec.at(5);
-  if (side) {
-    side_join.side = nullptr;
-    HI3_TRY(hipStreamWaitEvent(s, side->join, 0));
-  }
+  if (side && !fork.end()) return HI3_E_HIP;
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                  slotof, vidx, wts, pad_mask, T, H, K, out, resid};
   HI3_TRY(launch_combine(ca, dtype, s));
@@ -542,6 +524,19 @@ int hi3_moe_forward(const void *x, const float *w_router, const void *w_up_gate,
                       topk_w, expert_counts, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
+int hi3_moe_forward_overlap(const void *x, const float *w_router, const void *w_up_gate,
+                            const void *w_down, const void *w_shared_up_gate,
+                            const void *w_shared_down, const uint8_t *pad_mask, int64_t T,
+                            int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                            int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
+                            int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                            void *hip_stream, void *side_stream) {
+  return forward_impl(x, nullptr, 0.0f, w_router, w_up_gate, w_down, w_shared_up_gate,
+                      w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
+                      topk_w, expert_counts, workspace, workspace_bytes, hip_stream, nullptr,
+                      false, side_stream);
+}
+
 int hi3_moe_forward_instrumented(const void *x, const float *w_router, const void *w_up_gate,
                                  const void *w_down, const void *w_shared_up_gate,
                                  const void *w_shared_down, const uint8_t *pad_mask,
@@ -549,12 +544,12 @@ int hi3_moe_forward_instrumented(const void *x, const float *w_router, const voi
                                  int32_t I_shared, int32_t dtype, void *out,
                                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
                                  void *workspace, size_t workspace_bytes, void *hip_stream,
-                                 void *const *stage_events) {
+                                 void *side_stream, void *const *stage_events) {
   if (!stage_events) return HI3_E_NULL;
   return forward_impl(x, nullptr, 0.0f, w_router, w_up_gate, w_down, w_shared_up_gate,
                       w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
                       topk_w, expert_counts, workspace, workspace_bytes, hip_stream,
-                      stage_events);
+                      stage_events, false, side_stream);
 }
 
 int hi3_moe_forward_norm_residual(const void *h, const void *norm_weight, float eps,

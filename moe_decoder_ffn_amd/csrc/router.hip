@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
     int rank = 0;
 #pragma unroll
     for (int e = 0; e < kMaxE; ++e) {
-      if (EC == 0 && e >= E) break;
+      if (EC == 0 && e >= E) continue;  // (wave-uniform)
       const float ve = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
       m = fmaxf(m, ve);
       rank += (ve > l || (ve == l && e < lane)) ? 1 : 0;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
     float z = 0.0f;
 #pragma unroll
     for (int e = 0; e < kMaxE; ++e) {
-      if (EC == 0 && e >= E) break;
+      if (EC == 0 && e >= E) continue;
       z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), e));
     }
     const float p = ex / z;

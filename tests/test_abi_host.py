@@ -139,8 +139,44 @@ def test_route_and_dispatch_validation():
 def test_instrumented_requires_events():
     f = m.lib.hi3_moe_forward_instrumented
     args = [P, P, P, P, P, P, None, 64, 256, 8, 2, 128, 128, 0, P, None, None, None, P,
-            1 << 40, None]
+            1 << 40, None, None]
     assert f(*args, None) == m.HI3_E_NULL
+
+
+def _fwd_overlap(side, **kw):
+    a = dict(x=P, wr=P, w13=P, w2=P, ws13=P, ws2=P, pad=None, T=64, H=256, E=8, K=2, I=128,
+             Is=128, dt=m.HI3_BF16, out=P, idx=None, w=None, cnt=None, ws=P,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return m.lib.hi3_moe_forward_overlap(a["x"], a["wr"], a["w13"], a["w2"], a["ws13"],
+                                         a["ws2"], a["pad"], a["T"], a["H"], a["E"], a["K"],
+                                         a["I"], a["Is"], a["dt"], a["out"], a["idx"], a["w"],
+                                         a["cnt"], a["ws"], a["wsb"], a["stream"], side)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), m.HI3_E_NULL),
+    (dict(ws2=None), m.HI3_E_NULL),
+    (dict(K=9), m.HI3_E_SHAPE),
+    (dict(H=250), m.HI3_E_UNSUPPORTED),
+    (dict(out=UNALIGNED), m.HI3_E_UNSUPPORTED),
+    (dict(wsb=1000), m.HI3_E_WORKSPACE),
+    (dict(T=0, ws=None), m.HI3_OK),
+])
+def test_forward_overlap_validation(kw, status):
+    # validation comes before any stream or event is touched: a bogus side
+    # stream handle is never used on these paths
+    assert _fwd_overlap(P, **kw) == status
+    assert _fwd_overlap(None, **kw) == status
+
+
+def test_no_global_state_in_library_source():
+    # the host side keeps nothing between calls: no static streams, events or
+    # mutexes (the side stream is the caller's, its events live for one call)
+    src = open(os.path.join(ROOT, "moe_decoder_ffn_amd", "csrc", "hi3_moe.cpp")).read()
+    for word in ("std::mutex", "static hipStream_t", "static hipEvent_t", "g_side",
+                 "hipStreamCreate"):
+        assert word not in src, word
 
 
 def test_shared_on_side_query():
@@ -307,3 +343,12 @@ def test_backward_norm_residual_validation():
     assert call(eps=float("nan")) == m.HI3_E_UNSUPPORTED
     assert call(dnw=UNALIGNED) == m.HI3_E_UNSUPPORTED
     assert call(wsb=need - 1) == m.HI3_E_WORKSPACE
+
+
+def test_probe_validation():
+    f = m.lib.hi3_moe_probe_mfma_bf16
+    assert f(None, P, 1, 1, None) == m.HI3_E_NULL
+    assert f(P, None, 1, 1, None) == m.HI3_E_NULL
+    assert f(P, P, 0, 1, None) == m.HI3_E_SHAPE
+    assert f(P, P, 1, 0, None) == m.HI3_E_SHAPE
+    assert f(UNALIGNED, P, 1, 1, None) == m.HI3_E_UNSUPPORTED

@@ -25,9 +25,9 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gpu_forward(dd, K, pad=None, sentinel=None):
-    """Runs hi3_moe_forward on device inputs dd; returns host out, idx, w,
-    counts."""
+def gpu_forward(dd, K, pad=None, sentinel=None, side_stream=None):
+    """Runs hi3_moe_forward (hi3_moe_forward_overlap with a side stream) on
+    device inputs dd; returns host out, idx, w, counts."""
     import moe_decoder_ffn_amd as m
     x = dd["x"]
     T, H = x.shape
@@ -38,7 +38,8 @@ def gpu_forward(dd, K, pad=None, sentinel=None):
         out = torch.full_like(x, sentinel)
     padd = to_dev(pad) if pad is not None else None
     out, idx, w, cnt = m.moe_forward(x, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
-                                     dd["ws2"], K, pad_mask=padd, out=out, return_routes=True)
+                                     dd["ws2"], K, pad_mask=padd, out=out, return_routes=True,
+                                     side_stream=side_stream)
     torch.cuda.synchronize()
     return to_host(out), to_host(idx), to_host(w), to_host(cnt)
 
@@ -223,55 +224,65 @@ def _hip_events(n):
 
 
 @pytest.mark.parametrize("T,E,K,Is,H", [(700, 8, 2, 192, 512), (999, 64, 8, 320, 512),
-                                        (4131, 64, 8, 256, 512), (1000, 8, 2, 192, 320)])
-def test_forward_shared_side_stream_same_bits(T, E, K, Is, H):
-    """With no padding mask the shared expert's GEMMs run on the side stream
-    (dense launches over rows 0 .. T-1); an all-zero mask keeps them in the
-    grouped list on the caller's stream. Both tile the shared rows alike, so
-    every output bit, route and count must match, and the instrumented
-    forward (the same streams as the plain one) must match too. H = 320
-    leaves the down projections a partial column tile and 5 k steps."""
+                                        (4131, 64, 8, 256, 512), (1000, 8, 2, 192, 320),
+                                        (100, 8, 2, 192, 512), (512, 64, 8, 256, 512)])
+def test_forward_overlap_same_bits(T, E, K, Is, H):
+    """hi3_moe_forward_overlap runs the shared expert's GEMMs on the caller's
+    side stream (dense launches over rows 0 .. T-1); hi3_moe_forward keeps
+    them in the grouped list on one stream. Every output element is the
+    same reduction in the same order either way (k steps of 64, the same
+    MFMA and epilogue), so every output bit, route and count must match,
+    and so must the instrumented forward with and without the side stream.
+    H = 320 leaves the down projections a partial column tile and 5 k
+    steps; T = 100 and 512 (at most 112 rows per expert) run the routed
+    GEMMs on the streaming tiles while the dense launches keep 256-row
+    tiles."""
     import moe_decoder_ffn_amd as m
+    _say(f"[forward] overlap vs one stream T={T} E={E} K={K} Is={Is} H={H}")
     shape = wk.LayerShape(H=H, E=E, K=K, I=256, Is=Is, dtype=wk.BF16)
     assert m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.BF16, False)
     assert not m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.BF16, True)
     assert not m.hi3_moe_forward_shared_on_side(T, shape.H, E, K, shape.I, Is, wk.F32, False)
     d = upload(wk.make_inputs(wk.custom(shape, (T,)), 11))
-    side = gpu_forward(d, K)
-    one = gpu_forward(d, K, pad=np.zeros(T, np.uint8))
+    one = gpu_forward(d, K)
+    side_stream = torch.cuda.Stream()
+    side = gpu_forward(d, K, side_stream=side_stream)
     for u, v in zip(side, one):
         assert np.array_equal(u, v)
+    # the same stream given as the side stream: one stream
+    same = gpu_forward(d, K, side_stream=torch.cuda.current_stream())
+    for u, v in zip(same, one):
+        assert np.array_equal(u, v)
     x = d["x"]
-    out = torch.zeros_like(x)
-    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
-    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
-    cnt = torch.empty((E,), dtype=torch.int32, device="cuda")
     ws = m.workspace_for(x, E, K, shape.I, Is)
-    hip, evs = _hip_events(m.HI3_NUM_STAGES + 1)
-    try:
-        m.hi3_moe_forward_instrumented(x, d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
-                                       None, K, out, idx, w, cnt, ws, evs,
-                                       torch.cuda.current_stream())
-        torch.cuda.synchronize()
-    finally:
-        for e in evs:
-            hip.hipEventDestroy(e)
-    for u, v in zip(side, (out, idx, w, cnt)):
-        assert np.array_equal(u, to_host(v))
+    for sst in (None, side_stream):
+        out = torch.zeros_like(x)
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        cnt = torch.empty((E,), dtype=torch.int32, device="cuda")
+        hip, evs = _hip_events(m.HI3_NUM_STAGES + 1)
+        try:
+            m.hi3_moe_forward_instrumented(x, d["w_router"], d["w13"], d["w2"], d["ws13"],
+                                           d["ws2"], None, K, out, idx, w, cnt, ws, evs,
+                                           torch.cuda.current_stream(), sst)
+            torch.cuda.synchronize()
+        finally:
+            for e in evs:
+                hip.hipEventDestroy(e)
+        for u, v in zip(one, (out, idx, w, cnt)):
+            assert np.array_equal(u, to_host(v))
 
 
 def test_forward_concurrent_host_threads():
-    """Two host threads, each on a stream of its own, enqueue forwards at the
-    same time (both use the device's one side stream and its events, behind
-    the library's mutex): every result matches a single-threaded forward bit
-    for bit."""
+    """Two host threads, each with a main and a side stream of its own,
+    enqueue overlapped and plain forwards at the same time (the library
+    keeps no state between calls): every result matches a single-threaded
+    forward bit for bit."""
     import threading
     import moe_decoder_ffn_amd as m
+    _say("[forward] two host threads")
     shape = wk.LayerShape(H=512, E=64, K=8, I=256, Is=320, dtype=wk.BF16)
     cases = ((999, 21), (1500, 22))
-    for T, _ in cases:
-        assert m.hi3_moe_forward_shared_on_side(T, shape.H, shape.E, shape.K, shape.I, shape.Is,
-                                                wk.BF16, False)
     inputs = [upload(wk.make_inputs(wk.custom(shape, (T,)), seed)) for T, seed in cases]
     ref = [gpu_forward(d, shape.K) for d in inputs]
     results = [None, None]
@@ -279,11 +290,13 @@ def test_forward_concurrent_host_threads():
 
     def run(i):
         try:
-            st = torch.cuda.Stream()
+            st, side = torch.cuda.Stream(), torch.cuda.Stream()
             d = inputs[i]
             with torch.cuda.stream(st):
-                outs = [m.moe_forward(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"],
-                                      shape.K, return_routes=True) for _ in range(4)]
+                outs = [m.moe_forward(d["x"], d["w_router"], d["w13"], d["w2"], d["ws13"],
+                                      d["ws2"], shape.K, return_routes=True,
+                                      side_stream=side if j % 2 == 0 else None)
+                        for j in range(4)]
             st.synchronize()
             results[i] = [[to_host(t) for t in o] for o in outs]
         except Exception as e:  # reported by the main thread
@@ -302,6 +315,87 @@ def test_forward_concurrent_host_threads():
                 assert np.array_equal(u, v)
 
 
+def test_forward_overlap_graph_capture():
+    """An overlapped forward captured into a graph (the side stream joins
+    the capture through the call's fork and leaves it at the join) while
+    another host thread runs eager forwards on streams of its own: every
+    replay, with eager work and synchronisations between replays, matches
+    the eager result bit for bit, and so does every eager forward of the
+    other thread. The forward's kernels write every workspace byte they read
+    (no memset in the graph)."""
+    import threading
+    import moe_decoder_ffn_amd as m
+    _say("[forward] graph capture of the overlapped forward")
+    shape = wk.LayerShape(H=512, E=64, K=8, I=256, Is=320, dtype=wk.BF16)
+    T = 999
+    d = upload(wk.make_inputs(wk.custom(shape, (T,)), 31))
+    d2 = upload(wk.make_inputs(wk.custom(shape, (T,)), 32))
+    ref = gpu_forward(d, shape.K)
+    ref2 = gpu_forward(d2, shape.K)
+    x = d["x"]
+    ws = m.workspace_for(x, shape.E, shape.K, shape.I, shape.Is)
+    out = torch.zeros_like(x)
+    idx = torch.empty((T, shape.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, shape.K), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((shape.E,), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    args = (x, d["w_router"], d["w13"], d["w2"], d["ws13"], d["ws2"], None, shape.K, out, idx,
+            w, cnt, ws)
+    # warm up on a side stream of torch's choosing, as graph capture wants
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
+        m.hi3_moe_forward_overlap(*args, side_stream=side)
+    torch.cuda.current_stream().wait_stream(warm)
+    torch.cuda.synchronize()
+    stop = threading.Event()
+    errors, eager = [], []
+    # the other thread's streams and buffers exist before the capture starts,
+    # so nothing is created or allocated while it runs
+    st2, side2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws2 = m.workspace_for(d2["x"], shape.E, shape.K, shape.I, shape.Is)
+    bufs2 = (torch.zeros_like(d2["x"]), torch.empty((T, shape.K), dtype=torch.int32, device="cuda"),
+             torch.empty((T, shape.K), dtype=torch.float32, device="cuda"),
+             torch.empty((shape.E,), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+    def other():
+        try:
+            with torch.cuda.stream(st2):
+                while not stop.is_set() and len(eager) < 20:
+                    m.hi3_moe_forward_overlap(d2["x"], d2["w_router"], d2["w13"], d2["w2"],
+                                              d2["ws13"], d2["ws2"], None, shape.K, *bufs2, ws2,
+                                              side_stream=side2, stream=st2)
+                    st2.synchronize()
+                    eager.append([to_host(t) for t in bufs2])
+        except Exception as e:
+            errors.append(e)
+
+    th = threading.Thread(target=other)
+    th.start()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
+            m.hi3_moe_forward_overlap(*args, side_stream=side)
+        for rep in range(3):
+            out.zero_()
+            idx.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            for u, v in zip(ref, (out, idx, w, cnt)):
+                assert np.array_equal(u, to_host(v)), f"replay {rep}"
+            # eager work between replays
+            gpu_forward(d2, shape.K)
+    finally:
+        stop.set()
+        th.join(timeout=120)
+    assert not errors, errors
+    assert eager
+    for o in eager:
+        for u, v in zip(ref2, o):
+            assert np.array_equal(u, v)
+
+
 # ---------------------------------------------------------------- full size
 
 @pytest.fixture(scope="module")
@@ -318,9 +412,18 @@ def _sample_rows(valid_rows, n, seed):
     return np.unique(np.concatenate([valid_rows[:2], valid_rows[-2:], pick]))
 
 
+# Workloads whose every real row's output is compared with the oracle (the
+# 1024x1024 image sequence: about 40 s of oracle time on 16 host cores); the
+# others compare every row's routes and a sample of rows' outputs.
+ALL_ROWS = ("image_1024",)
+
+
 @pytest.mark.parametrize("name", ["image_1024", "batch8_512", "skew_16k", "padded_mixed",
                                   "image_512", "prompt_512"])
 def test_forward_full_size(full_weights, name):
+    """The full-size workloads through hi3_moe_forward_overlap, the entry
+    point the benchmark times (its side stream is used where every row is
+    real): routes of every row, counts, and outputs against the oracle."""
     w_host, w_dev = full_weights
     wl = wk.workload(name, 0)
     sh = wl.shape
@@ -331,21 +434,31 @@ def test_forward_full_size(full_weights, name):
     dd = dict(w_dev)
     dd["x"] = to_dev(x)
     dd["w_router"] = to_dev(wr)
-    out, idx, w, cnt = gpu_forward(dd, sh.K, padarg, sentinel=0.5 if padarg is not None else None)
+    out, idx, w, cnt = gpu_forward(dd, sh.K, padarg, sentinel=0.5 if padarg is not None else None,
+                                   side_stream=torch.cuda.Stream())
     del dd
     ref = oracle.route(x, wr, sh.K, pad_mask=padarg)
     near, ref_idx, ref_w = check_routes(idx, w, ref, padarg, sh.E, sh.K)
     assert np.array_equal(cnt, np.bincount(idx[idx >= 0], minlength=sh.E))
     valid_rows = np.nonzero(pad == 0)[0]
-    rows = _sample_rows(valid_rows, 24, 1)
-    rows = np.unique(np.concatenate([rows, np.nonzero(near)[0][:4]]))
+    if name in ALL_ROWS:
+        rows = valid_rows
+    else:
+        rows = _sample_rows(valid_rows, 24, 1)
+        rows = np.unique(np.concatenate([rows, np.nonzero(near)[0][:4]]))
+    _say(f"  oracle on {rows.size} rows")
     d = dict(w_host)
     d["x"] = x
     d["w_router"] = wr
     exact = oracle_rows(d, sh.K, rows, ref_idx, ref_w, padarg)
-    rel = check_output(out[rows], exact, sh.dtype, name)
-    _say(f"  near-tie rows {int(near.sum())}, max err / RMS = {rel:.4f}, "
-         f"load max/mean = {cnt.max() / cnt.mean():.2f}, min = {cnt.min()}")
+    stats = {}
+    check_output(out[rows], exact, sh.dtype, name, stats)
+    rec = {"workload": name, "rows_compared": int(rows.size), "real_rows": int(valid_rows.size),
+           "near_tie_rows": int(near.sum()), "near_tie_rows_compared": int(near[rows].sum()),
+           **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in stats.items()},
+           "load_max_over_mean": round(float(cnt.max() / cnt.mean()), 3),
+           "load_min": int(cnt.min())}
+    _say("  parity " + json.dumps(rec))
     if padarg is not None:
         assert np.all(as_f64(out[pad == 1]) == 0.5)
     if wl.skew:
