@@ -73,6 +73,7 @@ extern "C" {
 #define HI3_E_UNSUPPORTED (-3) /* outside the builder's limits above */
 #define HI3_E_WORKSPACE (-4)   /* workspace smaller than required */
 #define HI3_E_HIP (-5)         /* a HIP launch failed */
+#define HI3_E_SCRATCH (-6)     /* sizes too large for hi3_moe_forward_noalloc */
 
 /* Number of timed stages of hi3_moe_forward_instrumented. */
 #define HI3_NUM_STAGES 6
@@ -183,6 +184,31 @@ int hi3_moe_forward_overlap(const void *x, const float *w_router, const void *w_
                             int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
                             void *workspace, size_t workspace_bytes, void *hip_stream,
                             void *side_stream);
+
+/*
+ * hi3_moe_forward for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results (bit for bit) as hi3_moe_forward, without the
+ * workspace: the library's own scratch stands in for it, a device array of
+ * HI3_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends (obtained on the first call with that device current;
+ * hip_stream must belong to the current device, else HI3_E_UNSUPPORTED).
+ * Sizes whose hi3_moe_workspace_size exceeds HI3_NOALLOC_SCRATCH_BYTES are
+ * rejected with HI3_E_SCRATCH before anything is enqueued (at H = 4096,
+ * E = 64, K = 8, I = I_shared = 3072 in bf16: up to about 620 tokens).
+ * The call allocates nothing. Every call on one GPU uses that GPU's one
+ * scratch: calls that overlap on a GPU (other streams, other host threads)
+ * race and must be ordered by the caller. The scratch keeps the last call's
+ * contents; no part of it needs to start at zero.
+ */
+#define HI3_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int hi3_moe_forward_noalloc(const void *x, const float *w_router, const void *w_up_gate,
+                            const void *w_down, const void *w_shared_up_gate,
+                            const void *w_shared_down, const uint8_t *pad_mask,
+                            int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
+                            int32_t I_shared, int32_t dtype, void *out,
+                            int32_t *topk_idx, float *topk_w, int32_t *expert_counts,
+                            void *hip_stream);
 
 /*
  * hi3_moe_forward_overlap (hi3_moe_forward when side_stream is NULL) with

@@ -23,6 +23,8 @@ HI3_E_SHAPE = -2
 HI3_E_UNSUPPORTED = -3
 HI3_E_WORKSPACE = -4
 HI3_E_HIP = -5
+HI3_E_SCRATCH = -6
+HI3_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 HI3_NUM_STAGES = 6
 HI3_NUM_BWD_STAGES = 11
 
@@ -32,6 +34,7 @@ EXPORTED = (
     "hi3_moe_dispatch",
     "hi3_moe_forward",
     "hi3_moe_forward_overlap",
+    "hi3_moe_forward_noalloc",
     "hi3_moe_forward_instrumented",
     "hi3_moe_forward_shared_on_side",
     "hi3_moe_rmsnorm",
@@ -71,6 +74,8 @@ def _load():
     fwd = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.hi3_moe_forward.argtypes = fwd
     lib.hi3_moe_forward.restype = ctypes.c_int
+    lib.hi3_moe_forward_noalloc.argtypes = fwd[:18] + [P]
+    lib.hi3_moe_forward_noalloc.restype = ctypes.c_int
     lib.hi3_moe_forward_overlap.argtypes = fwd + [P]
     lib.hi3_moe_forward_overlap.restype = ctypes.c_int
     lib.hi3_moe_forward_instrumented.argtypes = fwd + [P, P]
@@ -207,6 +212,16 @@ def hi3_moe_forward_overlap(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_
     _check(lib.hi3_moe_forward_overlap(*_forward_args(
         x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down, pad_mask, K, out,
         topk_idx, topk_w, expert_counts, workspace, stream), _side(side_stream)))
+
+
+def hi3_moe_forward_noalloc(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                            pad_mask, K, out, topk_idx=None, topk_w=None, expert_counts=None,
+                            stream=None):
+    """hi3_moe_forward on the library's own scratch (no workspace argument)."""
+    a = _forward_args(x, w_router, w_up_gate, w_down, w_shared_up_gate, w_shared_down,
+                      pad_mask, K, out, topk_idx, topk_w, expert_counts, None, stream)
+    # drop the workspace pointer and size
+    _check(lib.hi3_moe_forward_noalloc(*a[:18], a[20]))
 
 
 def hi3_moe_forward_instrumented(x, w_router, w_up_gate, w_down, w_shared_up_gate,

@@ -26,7 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhi3moe.so")
 SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "combine.hip", "norm.hip", "backward.hip",
-           "probe.hip", "hi3_moe.cpp"]
+           "probe.hip", "noalloc.hip", "hi3_moe.cpp"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))

@@ -559,4 +559,18 @@ hipError_t launch_dw_router(const float *dls, const void *xs, const int4 *tiles,
                             float *part, float *dwr, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
+// ---------------------------------------------------------------- entry points
+
+// hi3_moe_forward on a workspace the caller of this function provides (the
+// no-allocation entry point's static scratch); with validate_only the
+// arguments are checked exactly as the forward checks them and nothing is
+// enqueued.
+int forward_single_stream(const void *x, const float *w_router, const void *w_up_gate,
+                          const void *w_down, const void *w_shared_up_gate,
+                          const void *w_shared_down, const uint8_t *pad_mask, int64_t T,
+                          int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                          int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                          void *hip_stream, bool validate_only);
+
 }  // namespace hi3

@@ -96,7 +96,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
                  int32_t E, int32_t K, int32_t I, int32_t Is, int32_t dtype, void *out,
                  int32_t *topk_idx, float *topk_w, int32_t *expert_counts, void *workspace,
                  size_t workspace_bytes, void *hip_stream, void *const *events,
-                 bool save = false, void *side_stream = nullptr) {
+                 bool save = false, void *side_stream = nullptr, bool validate_only = false) {
   if (!x || !w_router || !w_up_gate || !w_down || !w_shared_up_gate || !w_shared_down || !out)
     return HI3_E_NULL;
   int st = check_sizes(T, H, E, K, I, Is, dtype, true);
@@ -111,6 +111,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   // the routes, slot maps, u, g and h where it reads them
   const Plan p = make_plan(T, H, E, K, I, Is, dtype, save);
   if (workspace_bytes < p.total) return HI3_E_WORKSPACE;
+  if (validate_only) return HI3_OK;
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
@@ -432,6 +433,26 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
 
 }  // namespace
 
+namespace hi3 {
+
+// hi3_moe_forward with the workspace given by the caller of this function
+// (the no-allocation entry point passes its static scratch); validate_only:
+// check the arguments as the forward does, enqueue nothing.
+int forward_single_stream(const void *x, const float *w_router, const void *w_up_gate,
+                          const void *w_down, const void *w_shared_up_gate,
+                          const void *w_shared_down, const uint8_t *pad_mask, int64_t T,
+                          int32_t H, int32_t E, int32_t K, int32_t I, int32_t I_shared,
+                          int32_t dtype, void *out, int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                          void *hip_stream, bool validate_only) {
+  return forward_impl(x, nullptr, 0.0f, w_router, w_up_gate, w_down, w_shared_up_gate,
+                      w_shared_down, pad_mask, T, H, E, K, I, I_shared, dtype, out, topk_idx,
+                      topk_w, expert_counts, workspace, workspace_bytes, hip_stream, nullptr,
+                      false, nullptr, validate_only);
+}
+
+}  // namespace hi3
+
 extern "C" {
 
 size_t hi3_moe_workspace_size(int64_t T, int32_t H, int32_t E, int32_t K, int32_t I,
@@ -692,6 +713,9 @@ const char *hi3_moe_status_string(int status) {
              "or a pointer not 16-byte aligned)";
     case HI3_E_WORKSPACE: return "workspace smaller than hi3_moe_workspace_size";
     case HI3_E_HIP: return "a HIP launch failed";
+    case HI3_E_SCRATCH:
+      return "the sizes need more scratch than hi3_moe_forward_noalloc holds "
+             "(HI3_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

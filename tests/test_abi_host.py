@@ -352,3 +352,25 @@ def test_probe_validation():
     assert f(P, P, 0, 1, None) == m.HI3_E_SHAPE
     assert f(P, P, 1, 0, None) == m.HI3_E_SHAPE
     assert f(UNALIGNED, P, 1, 1, None) == m.HI3_E_UNSUPPORTED
+
+
+def test_noalloc_validation():
+    # checked on the host before any HIP call (no GPU here)
+    f = m.lib.hi3_moe_forward_noalloc
+    big = (700, 4096, 64, 8, 3072, 3072, m.HI3_BF16)    # more than the scratch holds
+    small = (64, 256, 8, 2, 128, 128, m.HI3_BF16)
+
+    def call(sz, x=P, out=P, idx=None, T=None):
+        sz = list(sz)
+        if T is not None:
+            sz[0] = T
+        return f(x, P, P, P, P, P, None, *sz, out, idx, None, None, None)
+
+    assert m.hi3_moe_workspace_size(*big) > m.HI3_NOALLOC_SCRATCH_BYTES
+    assert call(big) == m.HI3_E_SCRATCH
+    assert call(small, x=None) == m.HI3_E_NULL
+    assert call(small, out=None) == m.HI3_E_NULL
+    assert call(small, idx=UNALIGNED) == m.HI3_E_UNSUPPORTED
+    assert call(small, T=-1) == m.HI3_E_SHAPE
+    assert call(small, T=0) == m.HI3_OK
+    assert m.hi3_moe_status_string(m.HI3_E_SCRATCH) != "unknown status"
