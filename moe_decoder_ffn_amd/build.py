@@ -42,12 +42,12 @@ FLAGS = [
 M0_WARNING = "inline asm clobber list contains reserved registers: m0"
 IGNORED_NOISE = ("'-packed-fp32-ops' is not a recognized feature for this target",
                  "warnings generated when compiling for")
-# Kernels of gemm.hip that issue their copies as inline assembly: the
-# backward GEMMs (modes 2, 3 and 4 of gemm_bf16_kernel).
-ASM_COPY_KERNEL = re.compile(r"gemm_bf16_kernelILi[234]E")
+# Kernels of gemm.hip that issue their copies as inline assembly: every
+# bf16 grouped and dense GEMM.
+ASM_COPY_KERNEL = re.compile(r"gemm_bf16_(dense_)?kernelILi\d+E")
 # Instructions that use M0 without naming it.
-IMPLICIT_M0 = re.compile(r"\b(s_sendmsg|s_movrel|v_movrel|s_set_gpr_idx|ds_gws|ds_append|"
-                         r"ds_consume|ds_ordered_count|v_interp|_lds_|_lds\b)")
+IMPLICIT_M0 = re.compile(r"^(s_sendmsg|s_movrel|v_movrel|s_set_gpr_idx|ds_gws|ds_append|"
+                         r"ds_consume|ds_ordered_count|v_interp)|(^|_)lds(_|$)")
 
 
 def _filter_warnings(src: str, stderr: str):
@@ -86,6 +86,13 @@ def check_m0(obj: str) -> int:
                         f"--output={co}"], check=True, capture_output=True)
         dis = subprocess.run([os.path.join(LLVM_BIN, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
                              check=True, capture_output=True, text=True).stdout
+    return audit_m0(dis)
+
+
+def audit_m0(dis: str) -> int:
+    """The M0 check of check_m0 on llvm-objdump -d text. Returns the number
+    of copy sequences; raises RuntimeError on any other M0 use in a kernel
+    that issues the inline-asm copies."""
     checked = 0
     func = None
     insts = []
@@ -98,7 +105,7 @@ def check_m0(obj: str) -> int:
         i = 0
         while i < len(ops):
             op = ops[i]
-            if re.match(r"s_mov_b32 m0, s\d+$", op):
+            if re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi|ttmp\d+)$", op):
                 if (i + 2 < len(ops) and ops[i + 1] == "s_nop 0" and
                         ops[i + 2].startswith("global_load_lds_dwordx4")):
                     checked += 1
@@ -148,7 +155,7 @@ def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
             print(f"[hipcc {src}] {line}", file=sys.stderr)
         if m0:
             n = check_m0(os.path.join(build_dir, os.path.splitext(src)[0] + ".o"))
-            print(f"[build] {src}: {m0} inline-asm M0 clobber warnings (the backward GEMMs' "
+            print(f"[build] {src}: {m0} inline-asm M0 clobber warnings (the GEMMs' "
                   f"direct-to-LDS copies); disassembly checked: {n} copy sequences, no other "
                   "M0 use in those kernels", file=sys.stderr)
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]

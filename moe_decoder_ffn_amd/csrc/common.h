@@ -125,13 +125,6 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 #define HI3_GEMM_STAGED_STORE 1
 #endif
 constexpr bool kGemmStagedStore = HI3_GEMM_STAGED_STORE != 0;
-// GEMMs with k-contiguous operands (the forward) issue their direct
-// global -> LDS copies through the compiler's builtin (1) or as inline
-// assembly (0).
-#ifndef HI3_GEMM_DMA_BUILTIN
-#define HI3_GEMM_DMA_BUILTIN 1
-#endif
-constexpr bool kGemmDmaBuiltin = HI3_GEMM_DMA_BUILTIN != 0;
 constexpr bool kGemmDeepB = HI3_GEMM_DEEP_B != 0;
 constexpr bool kOverlapShared = HI3_OVERLAP_SHARED != 0;
 constexpr int kGemmColChunk = HI3_GEMM_COL_CHUNK;

@@ -187,32 +187,26 @@ __device__ __forceinline__ bool resolve_wgrad(const GemmArgs &a, TileJob &j) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Direct global -> LDS copy of 16 bytes per lane; lane i writes
-// lds_base + 16 i (lds_base must be the same for the whole wave); the copy
-// has no register result, and the kernel waits for it with counted vmcnt
-// waits (wait_vmem) before the workgroup barrier that publishes its stage.
-// BUILTIN: the compiler's global_load_lds builtin, which sets M0 (the LDS
-// base) itself. In the forward GEMMs (k-contiguous operands) the compiler
-// then adds no wait of its own before the LDS reads, so the copies of later
-// stages stay in flight. The backward GEMMs read k-major stages with the
-// transposing LDS read, before which the compiler drains every copy
-// (vmcnt(0)) when it can see them, so they issue the same three instructions
-// the builtin expands to (M0 = LDS base, one wait state,
-// global_load_lds_dwordx4) as inline assembly that declares M0 clobbered;
-// the build disassembles those kernels and fails if anything else in them
-// reads or writes M0 (moe_decoder_ffn_amd/build.py).
-template <bool BUILTIN>
+// lds_base + 16 i (lds_base must be the same for the whole wave). The copy
+// has no register result; the kernel waits for it with counted vmcnt waits
+// (wait_vmem) before the workgroup barrier that publishes its stage.
+// It is issued as the three instructions the compiler's own global_load_lds
+// builtin expands to (M0 = LDS base, one wait state,
+// global_load_lds_dwordx4), written as inline assembly that declares M0
+// clobbered. With the builtin, the compiler cannot order the copy against
+// the kernel's LDS reads and drains every outstanding LDS read (lgkmcnt(0))
+// before each MFMA that consumes a fragment, instead of waiting for the
+// fragment's own read (measured: 2-3% slower forward GEMMs); the backward's
+// transposing reads also get a vmcnt(0) drain each. The build disassembles
+// every kernel that uses this copy and fails if anything else in it reads
+// or writes M0 (moe_decoder_ffn_amd/build.py).
 __device__ __forceinline__ void lds_dma16(const void *g, u32x4_t *lds_base) {
-  if constexpr (BUILTIN) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(g),
-                                     (lds_void_t *)(lds_base), 16, 0, 0);
-  } else {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)(lds_base))));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(lds)
-                 : "memory", "m0");
-  }
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)(lds_base))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -343,7 +337,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
   constexpr int BN = kGemmBN;
   constexpr bool AT = MODE == 4;  // A stage k-major
   constexpr bool BT = MODE >= 2;  // B stage k-major
-  constexpr bool DMA_BUILTIN = kGemmDmaBuiltin && !AT && !BT;
   using L = LdsLayout<BK>;
   constexpr int NW = 2 * WN;                // waves: 2 along rows x WN along columns
   constexpr int A_CP = BM * BK * 2 / 1024 / NW;  // copies per wave per stage
@@ -406,7 +399,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     const int p = lane % LK::CPR;
     const int c = (((p >> 2) ^ (krow & 3)) << 2) | (p & 3);
     const int col = min(col0 + c * 8, cmax - 8);
-    lds_dma16<DMA_BUILTIN>(rowp(krow, col), stage + ci * 64);
+    lds_dma16(rowp(krow, col), stage + ci * 64);
   };
   const uint16_t *zrow = static_cast<const uint16_t *>(a.zrow) + 8 * (lane & 31);
   // Copies [q0, q1) of this wave (A copies first, then B) for k step kc.
@@ -430,7 +423,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
       } else {
         const int row = (wave * A_CP + q) * L::RPC + lane / L::CPR;
         const int c = (lane % L::CPR) ^ L::swz(row);
-        lds_dma16<DMA_BUILTIN>(A + static_cast<int64_t>(arow_src[q]) * lda + ko + c * 8,
+        lds_dma16(A + static_cast<int64_t>(arow_src[q]) * lda + ko + c * 8,
                   la + (wave * A_CP + q) * 64);
       }
     }
@@ -459,7 +452,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         } else {
           brow = min(j.nt * BN + row, N - 1);
         }
-        lds_dma16<DMA_BUILTIN>(B + static_cast<int64_t>(brow) * Kd + kob + c * 8,
+        lds_dma16(B + static_cast<int64_t>(brow) * Kd + kob + c * 8,
                   lb + (wave * B_CP + q) * 64);
       }
     }
