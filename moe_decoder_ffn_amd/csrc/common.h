@@ -24,10 +24,10 @@ constexpr int kMaxE = 64;
 // the per-block expert histograms that the stable counting sort scans use
 // the same blocking.
 constexpr int kRouterTB = 32;
-// The bf16 router splits the hidden dimension over at most this many slices.
-constexpr int kRouterMaxSlices = 16;
-// Tokens per block of the bf16 router's logit kernel.
+// The bf16 router: tokens per block of its logit kernel, and at most this
+// many slices of the hidden dimension.
 constexpr int kRouterMT = 128;
+constexpr int kRouterMaxSlices = 16;
 // Rows per partial sum of the RMSNorm weight gradient (block backward).
 constexpr int kNormBwdRows = 64;
 
@@ -179,6 +179,74 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// ---------------------------------------------------------------- RMSNorm steps
+
+// The block's RMSNorm in front of the layer (layers API page,
+// HunyuanRMSNorm), step by step to the rounding: the squares of one 16-byte
+// chunk summed in fp64 (chunk_sq); n = dtype(x * r), xn = dtype(w * n) for
+// the elements of one chunk (norm_chunk).
+template <int DT>
+__device__ __forceinline__ void unpack16(const u32x4_t &v, float *f) {
+  if (DT == kBF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(v[e] << 16);
+      f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+  }
+}
+
+// n = dtype(x * r), xn = dtype(w * n) for the elements of one chunk.
+template <int DT>
+__device__ __forceinline__ u32x4_t norm_chunk(const u32x4_t &xv, const u32x4_t &wv, float r) {
+  constexpr int PER = DT == kBF16 ? 8 : 4;
+  float f[PER], w[PER];
+  unpack16<DT>(xv, f);
+  unpack16<DT>(wv, w);
+  u32x4_t o;
+  if (DT == kBF16) {
+    uint16_t q[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float n = bf16_to_f32(f32_to_bf16(f[e] * r));
+      q[e] = f32_to_bf16(w[e] * n);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = static_cast<uint32_t>(q[2 * e]) | (static_cast<uint32_t>(q[2 * e + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = __float_as_uint(w[e] * (f[e] * r));
+  }
+  return o;
+}
+
+template <int DT>
+__device__ __forceinline__ double chunk_sq(const u32x4_t &v) {
+  constexpr int PER = DT == kBF16 ? 8 : 4;
+  float f[PER];
+  unpack16<DT>(v, f);
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) ss += static_cast<double>(f[e]) * static_cast<double>(f[e]);
+  return ss;
+}
+
+// The wave's partial sums of squares (lane l holding the chunks l, l + 64,
+// ... of the row, each summed in order) added in a fixed butterfly order,
+// m = the mean rounded to fp32, d = m + eps in fp32, r = 1 / sqrt(d)
+// evaluated in fp64 and rounded once to fp32; every lane returns the same r.
+__device__ __forceinline__ float rms_finish(double ss, int H, float eps) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float m = static_cast<float>(ss / static_cast<double>(H));
+  const float d = m + eps;
+  return static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+}
+
 // ---------------------------------------------------------------- waves
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -225,11 +293,10 @@ struct Plan {
   int64_t T;
   int H, E, K, I, Is, dtype;
   int NB;         // token blocks of kRouterTB rows
-  int Epad;       // E rounded up to 32 (router MFMA column tiles)
   int BM;         // grouped-GEMM tile rows (per dtype)
   int max_tiles;  // upper bound on grouped-GEMM row tiles
-  size_t wsplit;  // [3][Epad][H] bf16: router weight split into 3 bf16 terms
   size_t rpart;   // [slices][T][E] fp32: router partial logits
+  size_t wsplit;  // [3][E rounded up to 32][H] bf16: the router weight's terms
   size_t idx;     // [T*K] int32 routes when the caller passes none
   size_t wts;     // [T*K] fp32
   size_t blkcnt;  // [NB][E] int32 per-block expert histogram
@@ -246,6 +313,7 @@ struct Plan {
   size_t vtok;    // [T] int32 real-row index -> token
   size_t vidx;    // [T] int32 token -> real-row index (-1 padding)
   size_t xn;      // [T,H] dtype: rows after the block's RMSNorm (norm + residual entry)
+  size_t rnorm;   // [T] fp32: the RMSNorm's r of each row (norm + residual entry)
   size_t h;       // [T*K, I] dtype: SwiGLU activations of routed rows
   size_t hs;      // [T, Is] dtype: SwiGLU activations of the shared expert
   size_t y;       // [T*K, H] fp32: routed expert outputs by slot
@@ -284,7 +352,6 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
   Plan p{};
   p.T = T; p.H = H; p.E = E; p.K = K; p.I = I; p.Is = Is; p.dtype = dtype;
   p.NB = static_cast<int>((T + kRouterTB - 1) / kRouterTB);
-  p.Epad = (E + 31) / 32 * 32;
   if (dtype != kBF16)
     p.BM = kGemmF32BM;
   else
@@ -298,8 +365,8 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
     o = align_up(o + bytes, 256);
     return at;
   };
-  p.wsplit = take(dtype == kBF16 ? 3ull * p.Epad * H * 2 : 0);
   p.rpart = take(static_cast<size_t>(dtype == kBF16 ? router_slices(T, H) : 1) * T * E * 4);
+  p.wsplit = take(dtype == kBF16 ? static_cast<size_t>((E + 31) / 32 * 32) * H * 6 : 0);
   p.idx = take(TK * 4);
   p.wts = take(TK * 4);
   p.blkcnt = take(static_cast<size_t>(p.NB) * E * 4);
@@ -317,6 +384,7 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
   p.vidx = take(T * 4);
   if (I > 0) {
     p.xn = take(T * H * es);
+    p.rnorm = take(T * 4);
     p.h = take(TK * I * es);
     p.hs = take(T * Is * es);
     p.y = take(TK * H * 4);
@@ -350,10 +418,16 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
 struct RouterArgs {
   const void *x;
   const float *w_router;
-  uint16_t *wsplit;  // bf16 layers: the split weight (written by launch_router)
+  const void *norm_w;  // bf16 layers: the block's RMSNorm weight [H], or null (x feeds
+                       // the router as it is)
+  float eps;
+  void *xn;            // with norm_w: [T, H] normalised rows out (the experts' input)
+  void *wsplit;        // bf16 layers: [3][E rounded up to 32][H] bf16 scratch (the
+                       // weight's split terms)
+  float *rrow;         // with norm_w: [T] fp32 scratch (r of each row)
   const uint8_t *pad;
   int64_t T;
-  int H, E, K, Epad;
+  int H, E, K;
   int32_t *idx;
   float *wts;
   int32_t *blkcnt;

@@ -40,56 +40,117 @@ __device__ int block_exclusive_scan_1024(int v, int *total) {
   return base + inc - v;
 }
 
-// One block of 1024 threads: thread (seg, e) = (tid / 64, tid % 64) scans
-// expert e's histogram column over block segment seg.
+// One block of 1024 threads. The per-block expert histograms [NB][E] are
+// staged in LDS, kScanRows token blocks at a time, with coalesced loads;
+// thread (seg, e) = (tid / 64, tid % 64) then walks expert e's column over
+// rows [16 seg, 16 seg + 16) of the staged rows. Pass 1 sums each column
+// (the experts' totals, hence their offsets); pass 2 writes the first slot
+// of every (block, expert). With NB <= kScanRows the rows stay in LDS for
+// both passes.
+constexpr int kScanRows = 256;
+
 __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
+  __shared__ int hist[kScanRows][kMaxE];
   __shared__ int seg_sum[16][kMaxE];
   __shared__ int tot[kMaxE];
   __shared__ int eoff[kMaxE + 1];
   __shared__ int toff[kMaxE + 2];
+  __shared__ int chunk_base[kMaxE];
   __shared__ int nvalid_s;
   const int tid = threadIdx.x;
   const int e = tid & 63, seg = tid >> 6;
-  const int per = (a.NB + 15) / 16;
-  const int b_lo = seg * per;
-  const int b_hi = min(a.NB, b_lo + per);
-
-  // expert columns
-  int s = 0;
-  if (e < a.E)
-    for (int b = b_lo; b < b_hi; ++b) s += a.blkcnt[static_cast<int64_t>(b) * a.E + e];
-  seg_sum[seg][e] = s;
-  __syncthreads();
-  if (seg == 0) {
-    int t = 0;
-    for (int q = 0; q < 16; ++q) t += seg_sum[q][e];
-    tot[e] = e < a.E ? t : 0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int x = 0; x < a.E; ++x) {
-      eoff[x] = run;
-      run += tot[x];
-    }
-    eoff[a.E] = run;
-  }
-  __syncthreads();
-  if (e < a.E) {
-    int base = eoff[e];
-    for (int q = 0; q < seg; ++q) base += seg_sum[q][e];
-    for (int b = b_lo; b < b_hi; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * a.E + e;
-      a.blkoff[i] = base;
-      base += a.blkcnt[i];
-    }
-  }
-
-  // real rows: scan of per-block counts over all blocks
+  const int E = a.E;
+  const int nch = (a.NB + kScanRows - 1) / kScanRows;
+  static_assert(kScanRows == 16 * 16, "16 segments of 16 rows");
+  // real rows per block (loaded first, scanned after the histograms)
   const int vper = (a.NB + 1023) / 1024;
   const int v_lo = tid * vper, v_hi = min(a.NB, v_lo + vper);
   int vs = 0;
   for (int b = v_lo; b < v_hi; ++b) vs += a.blkval[b];
+
+  // (eight loads in flight per thread before any store: a chunk is at most
+  // 256 x 64 = 16 x 1024 values)
+  auto stage = [&](int ch) {
+    const int b0 = ch * kScanRows;
+    const int n = min(kScanRows, a.NB - b0) * E;
+    const int32_t *src = a.blkcnt + static_cast<int64_t>(b0) * E;
+    for (int i0 = 0; i0 < n; i0 += 8 * 1024) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 1024 + tid;
+        v[u] = i < n ? src[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 1024 + tid;
+        if (i < n) hist[i / E][i % E] = v[u];
+      }
+    }
+  };
+  // sum of this thread's 16 rows of column e in the staged chunk
+  auto seg_total = [&](int ch) {
+    const int nb = min(kScanRows, a.NB - ch * kScanRows);
+    int s = 0;
+    if (e < E)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int b = seg * 16 + j;
+        if (b < nb) s += hist[b][e];
+      }
+    return s;
+  };
+
+  // pass 1: column totals
+  int colsum = 0;  // (segment 0) expert e's total over the chunks so far
+  for (int ch = 0; ch < nch; ++ch) {
+    stage(ch);
+    __syncthreads();
+    seg_sum[seg][e] = seg_total(ch);
+    __syncthreads();
+    if (seg == 0)
+      for (int q = 0; q < 16; ++q) colsum += seg_sum[q][e];
+    __syncthreads();
+  }
+  if (seg == 0) tot[e] = e < E ? colsum : 0;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int x = 0; x < E; ++x) {
+      eoff[x] = run;
+      run += tot[x];
+    }
+    eoff[E] = run;
+  }
+  __syncthreads();
+  if (seg == 0) chunk_base[e] = e < E ? eoff[e] : 0;
+  // pass 2: first slot of every (block, expert)
+  for (int ch = 0; ch < nch; ++ch) {
+    if (nch > 1) stage(ch);  // a single chunk is still staged
+    __syncthreads();
+    const int b0 = ch * kScanRows;
+    const int nb = min(kScanRows, a.NB - b0);
+    seg_sum[seg][e] = seg_total(ch);
+    __syncthreads();
+    if (e < E) {
+      int base = chunk_base[e];
+      for (int q = 0; q < seg; ++q) base += seg_sum[q][e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int b = seg * 16 + j;
+        if (b < nb) {
+          a.blkoff[static_cast<int64_t>(b0 + b) * E + e] = base;
+          base += hist[b][e];
+        }
+      }
+    }
+    __syncthreads();
+    if (seg == 0 && e < E)
+      for (int q = 0; q < 16; ++q) chunk_base[e] += seg_sum[q][e];
+    __syncthreads();
+  }
+
+  // real rows: scan of per-block counts over all blocks
   int vtotal = 0;
   int vbase = block_exclusive_scan_1024(vs, &vtotal);
   for (int b = v_lo; b < v_hi; ++b) {
@@ -141,8 +202,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   __shared__ int ids[kRouterTB][kMaxE];
   __shared__ uint64_t selmask[kRouterTB];
   __shared__ int rank[kRouterTB][kMaxE];
+  __shared__ int first[kMaxE];
   const int tid = threadIdx.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
+  // this block's first slot per expert, fetched alongside the routes
+  if (tid < a.E) first[tid] = a.blkoff[static_cast<int64_t>(blockIdx.x) * a.E + tid];
   for (int i = tid; i < kRouterTB * a.K; i += blockDim.x) {
     const int rr = i / a.K, k = i % a.K;
     const int64_t t = t0 + rr;
@@ -178,7 +242,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
       if (ids[rr][q] == e) e = -1;  // a repeated id in one row is ignored
     int slot = -1;
     if (e >= 0) {
-      slot = a.blkoff[static_cast<int64_t>(blockIdx.x) * a.E + e] + rank[rr][e];
+      slot = first[e] + rank[rr][e];
       a.perm[slot] = static_cast<int32_t>(t);
     }
     a.slotof[t * a.K + k] = slot;

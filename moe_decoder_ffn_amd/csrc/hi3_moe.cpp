@@ -129,18 +129,27 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     fork.side = side_s;
     if (!fork.make()) return HI3_E_HIP;
   }
+  // The block's RMSNorm: bf16 layers normalise inside the router kernel
+  // (below), which writes the normalised rows for the expert GEMMs; fp32
+  // layers run the RMSNorm kernel first.
   const void *resid = nullptr;
+  const void *x_in = x;
+  const bool fused_norm = norm_weight && dtype == HI3_BF16;
   if (norm_weight) {
-    NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
-    HI3_TRY(launch_rmsnorm(na, dtype, s));
+    if (!fused_norm) {
+      NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
+      HI3_TRY(launch_rmsnorm(na, dtype, s));
+    }
     resid = x;
     x = at(p.xn);
   }
   // fork: the side stream starts after everything enqueued on s so far and
   // runs the shared expert's rows, the tokens 0 .. T-1 in order (measured:
   // forking here beats forking after the router or the scatter, though the
-  // shared GEMM's blocks then delay the routing's)
-  if (side) {
+  // shared GEMM's blocks then delay the routing's). With the RMSNorm fused
+  // into the router, the rows exist only after it: the fork follows it.
+  auto fork_shared = [&]() -> int {
+    if (!side) return HI3_OK;
     if (!fork.start()) return HI3_E_HIP;
     GemmArgs us{};
     us.cls[1] = GemmClass{x, H, nullptr, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
@@ -148,6 +157,11 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     GemmArgs ds{};
     ds.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
     HI3_TRY(launch_gemm_dense(ds, static_cast<int>(T), 1, side_s));
+    return HI3_OK;
+  };
+  if (!fused_norm) {
+    st = fork_shared();
+    if (st != HI3_OK) return st;
   }
   // the main list holds the shared group's row tiles only when the side
   // stream does not run them
@@ -165,9 +179,15 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
 
   // 0: router + per-block histogram
   rec.at(0);
-  RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K, p.Epad,
-                idx, wts, blkcnt, blkval};
+  RouterArgs ra{fused_norm ? x_in : x, w_router, fused_norm ? norm_weight : nullptr, eps,
+                fused_norm ? at(p.xn) : nullptr, at(p.wsplit),
+                static_cast<float *>(at(p.rnorm)), pad_mask, T, H, E, K, idx, wts, blkcnt,
+                blkval};
   HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
+  if (fused_norm) {
+    st = fork_shared();
+    if (st != HI3_OK) return st;
+  }
   // 1: scans -> expert offsets, real-row list, GEMM row tiles
   rec.at(1);
   ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
@@ -282,10 +302,13 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   // (dL/dxn) stays in fp32 for RMSNorm's backward at the end
   const void *h_in = x;
   const bool norm = norm_weight != nullptr;
+  const bool fused_norm = norm && dtype == HI3_BF16;  // normalised in the router kernel
   void *dh = dx;
   if (norm) {
-    NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
-    HI3_TRY(launch_rmsnorm(na, dtype, s));
+    if (!fused_norm) {
+      NormArgs na{x, norm_weight, pad_mask, T, H, eps, at(p.xn)};
+      HI3_TRY(launch_rmsnorm(na, dtype, s));
+    }
     x = at(p.xn);
     dx = nullptr;
   }
@@ -296,8 +319,10 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   // hi3_moe_forward_train all of this is already in the workspace.
   rec.at(0);
   if (!reuse) {
-    RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K,
-                  p.Epad, idx, wts, blkcnt, blkval};
+    RouterArgs ra{fused_norm ? h_in : x, w_router, fused_norm ? norm_weight : nullptr, eps,
+                  fused_norm ? at(p.xn) : nullptr, at(p.wsplit),
+                  static_cast<float *>(at(p.rnorm)), pad_mask, T, H, E, K, idx, wts, blkcnt,
+                  blkval};
     HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
   }
   rec.at(1);
@@ -479,8 +504,8 @@ int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask,
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
-  RouterArgs ra{x, w_router, static_cast<uint16_t *>(at(p.wsplit)), pad_mask, T, H, E, K, p.Epad,
-                topk_idx, topk_w,
+  RouterArgs ra{x, w_router, nullptr, 0.0f, nullptr, at(p.wsplit), nullptr,
+                pad_mask, T, H, E, K, topk_idx, topk_w,
                 static_cast<int32_t *>(at(p.blkcnt)),
                 static_cast<int32_t *>(at(p.blkval))};
   HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));

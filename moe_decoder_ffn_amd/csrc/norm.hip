@@ -20,56 +20,6 @@
 
 namespace hi3 {
 
-template <int DT>
-__device__ __forceinline__ void unpack16(const u32x4_t &v, float *f) {
-  if (DT == kBF16) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[2 * e] = __uint_as_float(v[e] << 16);
-      f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
-  }
-}
-
-// n = dtype(x * r), xn = dtype(w * n) for the elements of one chunk.
-template <int DT>
-__device__ __forceinline__ u32x4_t norm_chunk(const u32x4_t &xv, const u32x4_t &wv, float r) {
-  constexpr int PER = DT == kBF16 ? 8 : 4;
-  float f[PER], w[PER];
-  unpack16<DT>(xv, f);
-  unpack16<DT>(wv, w);
-  u32x4_t o;
-  if (DT == kBF16) {
-    uint16_t q[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float n = bf16_to_f32(f32_to_bf16(f[e] * r));
-      q[e] = f32_to_bf16(w[e] * n);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = static_cast<uint32_t>(q[2 * e]) | (static_cast<uint32_t>(q[2 * e + 1]) << 16);
-  } else {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = __float_as_uint(w[e] * (f[e] * r));
-  }
-  return o;
-}
-
-template <int DT>
-__device__ __forceinline__ double chunk_sq(const u32x4_t &v) {
-  constexpr int PER = DT == kBF16 ? 8 : 4;
-  float f[PER];
-  unpack16<DT>(v, f);
-  double ss = 0.0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) ss += static_cast<double>(f[e]) * static_cast<double>(f[e]);
-  return ss;
-}
-
 template <int DT, int CPL>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
   const int lane = threadIdx.x & 63;
@@ -86,13 +36,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
 
   // m = mean of x^2 (fp64 sum, fixed butterfly order), d = m + eps in fp32,
   // r = 1 / sqrt(d) rounded once to fp32; every lane computes the same r.
-  auto finish = [&](double ss) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-    const float m = static_cast<float>(ss / static_cast<double>(a.H));
-    const float d = m + a.eps;
-    return static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
-  };
+  auto finish = [&](double ss) { return rms_finish(ss, a.H, a.eps); };
 
   if constexpr (CPL > 0) {
     u32x4_t v[CPL];

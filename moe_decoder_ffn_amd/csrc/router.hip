@@ -3,13 +3,16 @@
 // build_moe_config; the gate kept in fp32 per the model-coverage page,
 // "Train", and 'mlp.gate' in _keep_in_fp32_modules_strict).
 //
-// bf16 activations: the fp32 router weight is split once per call into three
-// bf16 terms hi + mid + lo that sum to it exactly (Henry, Tang & Heinecke,
-// "Leveraging the bfloat16 Artificial Intelligence Datatype for
-// Higher-Precision Computations", ARITH 2019), stored in MFMA-fragment order
-// so every fragment load is one contiguous 1 KiB per wave. Each product
-// x*term is exact in fp32, so bf16 MFMA with fp32 accumulation gives the fp32
-// router at matrix-core rate instead of the vector-FMA rate.
+// bf16 activations: each fp32 router weight is split, in registers, into
+// three bf16 terms hi + mid + lo that sum to it exactly (Henry, Tang &
+// Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype for
+// Higher-Precision Computations", ARITH 2019). Each product x * term is exact
+// in fp32, so bf16 MFMA with fp32 accumulation gives the fp32 router at
+// matrix-core rate instead of the vector-FMA rate. When the layer runs inside
+// its decoder block, the block's RMSNorm (layers API page, HunyuanRMSNorm;
+// model API page, HunyuanImage3Block: post_attention_layernorm ahead of the
+// experts) is computed by the same kernel, which writes the normalised rows
+// once for the expert GEMMs and multiplies them in place.
 //
 // The selection kernel also builds the per-block expert histogram that the
 // stable counting sort scans (block b covers tokens [32b, 32b + 32)).
@@ -19,55 +22,20 @@
 
 namespace hi3 {
 
-// --------------------------------------------------------------- weight split
-
-// Output layout ("fragment order"): for split term sp, 32-expert column
-// tile n, 64-wide k chunk c and MFMA step q, the 64 lanes' 8-element pieces
-// lie next to each other (lane = 32 g + r holds expert 32 n + r, k =
-// 64 c + 32 g + 8 q + [0, 8)), so the router reads each B fragment as one
-// contiguous 1 KiB block.
-__device__ __forceinline__ int64_t wsplit_index(int sp, int e, int h, int ns, int nchunks) {
-  const int n = e >> 5, r = e & 31;
-  const int c = h >> 6, w = h & 63;
-  const int g = w >> 5, q = (w & 31) >> 3, j = w & 7;
-  const int lane = g * 32 + r;
-  return ((((static_cast<int64_t>(sp) * ns + n) * nchunks + c) * 4 + q) * 64 + lane) * 8 + j;
-}
-
-__global__ __launch_bounds__(256) void split_router_kernel(const float *__restrict__ wr,
-                                                           uint16_t *__restrict__ ws,
-                                                           int E, int Epad, int H) {
-  const int64_t n = static_cast<int64_t>(Epad) * H;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int e = static_cast<int>(i / H);
-  const int h = static_cast<int>(i % H);
-  const float v = e < E ? wr[i] : 0.0f;
-  // Truncating to the top 8 significand bits leaves an exact remainder.
-  const uint32_t hi = __float_as_uint(v) & 0xFFFF0000u;
-  const float r1 = v - __uint_as_float(hi);
-  const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
-  const float r2 = r1 - __uint_as_float(mid);
-  const int ns = Epad / 32, nchunks = H / 64;
-  ws[wsplit_index(0, e, h, ns, nchunks)] = static_cast<uint16_t>(hi >> 16);
-  ws[wsplit_index(1, e, h, ns, nchunks)] = static_cast<uint16_t>(mid >> 16);
-  ws[wsplit_index(2, e, h, ns, nchunks)] = f32_to_bf16(r2);  // at most 8 significant bits: exact
-}
-
-
 // --------------------------------------------------------------- selection
 
 // Softmax over all experts, top-K and renormalisation for 32 tokens per
-// block: 8 waves, one token per wave at a time, lane = expert; then the
-// block's expert histogram and real-row count.
-// The token's logits are the slice partials summed in slice order. Every
-// lane reads all of the token's logits from the other lanes (readlane, in
-// expert order) to get the maximum and its own rank in the selection order
-// (larger logit first, lower index first on equal logits; softmax is
-// strictly increasing, so this is the order of the probabilities, and fp32
-// underflow of small probabilities cannot change it). Z sums exp(l - max) in
-// ascending expert order, the selected p = exp(l - max) / Z are summed in
-// selection order, and each is divided by that sum.
+// block: one wave per token at a time, lane = expert; then the block's
+// expert histogram and real-row count.
+// Every lane reads all of the token's logits from the other lanes
+// (readlane, in expert order) to get the maximum and its own rank in the
+// selection order (larger logit first, lower index first on equal logits;
+// softmax is strictly increasing, so this is the order of the
+// probabilities, and fp32 underflow of small probabilities cannot change
+// it). Z sums exp(l - max) in ascending expert order, the selected
+// p = exp(l - max) / Z are summed in selection order, and each is divided by
+// that sum.
+// The token's logits are the slice partials summed in slice order.
 // partial: [slices][T][E] fp32. EC = 64: E is 64 (no per-expert guards);
 // EC = 0: any E <= 64.
 #ifndef HI3_SEL_THREADS
@@ -97,7 +65,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int EC>
 __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a,
                                                                    const float *partial,
-                                                            int slices) {
+                                                                   int slices) {
   __shared__ SelectShared sh;
   const int E = EC > 0 ? EC : a.E;
   const int K = a.K;
@@ -106,8 +74,8 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
 
   // logits of the wave's tokens: lane e sums partial[ks][t][e] over the
-  // slices in slice order (one coalesced 256-byte row per slice); all of the
-  // wave's loads are issued before the first sum
+  // slices in slice order (one coalesced row per slice); all of the wave's
+  // loads are issued before the first sum
   constexpr int TPW = kRouterTB / (kSelThreads / 64);  // tokens per wave
   float lsum[TPW];
   {
@@ -207,134 +175,237 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
 
 // --------------------------------------------------------------- bf16 router
 
-// Partial logits of kRouterMT tokens over one slice of the hidden
-// dimension. Grid: x = blocks of kRouterMT tokens, y = k slices (ranges of
-// 64-wide chunks). 256 threads = 4 waves; wave w takes the chunks
-// first + w, first + w + 4, ... of the slice for all kRouterMT / 32 token
-// tiles, so each router-weight fragment it loads (and splits) serves every
-// token tile of the block. The 4 waves' sums are added in a fixed order in
-// LDS and written to partial[slice][t][e].
+// The three bf16 terms of an fp32 value: hi is v with its low 16 bits
+// cleared (exact), mid the same of the remainder, lo the rest (at most 8
+// significant bits, so its bf16 rounding is exact): hi + mid + lo == v.
+__device__ __forceinline__ void split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+  const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
+  const float r1 = v - __uint_as_float(h);
+  const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(m);
+  hi = h >> 16;
+  mid = m >> 16;
+  lo = f32_to_bf16(r2);
+}
+
+// The router weight split once per call into its three bf16 terms (hi, mid,
+// lo; experts past E as zero rows), each stored in the logit kernel's
+// fragment order: the 8 terms that lane (r, g) multiplies in step q of chunk
+// c of expert tile y form the 16-byte piece
+//   ((((y * nchunks + c) * 3 + term) * 2 + g) * 4 + q) * 32 + r,
+// so each of the logit kernel's weight loads reads two contiguous 512-byte
+// runs, and no block splits the weight again.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w, int E,
+                                                           int Epad, int H,
+                                                           u32x4_t *__restrict__ wsplit) {
+  const int64_t n = static_cast<int64_t>(Epad) * H / 8;  // groups of 8 weights
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int nch = H / 64;
+  const int r = static_cast<int>(i % 32);
+  int64_t rest = i / 32;
+  const int q = static_cast<int>(rest % 4);
+  rest /= 4;
+  const int g = static_cast<int>(rest % 2);
+  rest /= 2;
+  const int c = static_cast<int>(rest % nch);
+  const int y = static_cast<int>(rest / nch);
+  const int e = y * 32 + r;
+  const int k = 64 * c + 32 * g + 8 * q;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+  if (e < E) {
+    const f32x4_t *src = reinterpret_cast<const f32x4_t *>(w + static_cast<int64_t>(e) * H + k);
+    const f32x4_t a0 = src[0], a1 = src[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a0[j];
+      v[4 + j] = a1[j];
+    }
+  }
+  u32x4_t th, tm, tl;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3(v[2 * p], h0, m0, l0);
+    split3(v[2 * p + 1], h1, m1, l1);
+    th[p] = h0 | (h1 << 16);
+    tm[p] = m0 | (m1 << 16);
+    tl[p] = l0 | (l1 << 16);
+  }
+  const int64_t base = ((((static_cast<int64_t>(y) * nch + c) * 3) * 2 + g) * 4 + q) * 32 + r;
+  constexpr int64_t TERM = 2 * 4 * 32;  // pieces between the terms of one chunk
+  wsplit[base] = th;
+  wsplit[base + TERM] = tm;
+  wsplit[base + 2 * TERM] = tl;
+}
+
+// Partial logits of kRouterMT = 128 tokens x 64 experts over one slice of the
+// hidden dimension (blockIdx.y; 64-wide chunks [y cps, (y + 1) cps)). The
+// router weight is the same for every block of tokens, so the blocks take
+// 128 tokens each (fewer weight reads per token) and split the hidden
+// dimension for parallelism; the selection kernel adds the slices in order.
+// 8 waves: wave w owns tokens 32 (w % 4) .. + 31 and experts 32 (w / 4) ..
+// + 31, so every (token, expert) of the block is summed by one wave; the
+// four waves of an expert tile read the same weight pieces (L1). Each wave
+// loads the next chunk's operands while it multiplies the current one.
+// With NORM the rows are normalised on the fly with their r (computed by
+// row_rms_kernel): n = bf16(x r), xn = bf16(w n), and the first expert
+// tile's waves write xn (the expert GEMMs' input; every chunk of every real
+// row is written by exactly one wave).
 //
-// MFMA operand layout (v_mfma_f32_32x32x16_bf16): lane l supplies row
-// (l % 32) of A and column (l % 32) of B, and 8 consecutive k values; lanes
-// 0-31 and 32-63 cover two disjoint k groups. Any k assignment is valid as
-// long as A and B agree: within a 64-wide chunk lane half g takes k in
-// [32g, 32g + 32) and step q uses its elements [8q, 8q + 8), so each lane
-// reads 64 contiguous bytes of x and 128 of the weight row per chunk.
-// Result element v of lane l is token 8 (v / 4) + 4 (l / 32) + v % 4 of the
-// tile and expert l % 32 of the column tile. The three terms of a weight go
-// into the same accumulator, hi first; the next chunk's operands are loaded
-// while the current chunk is multiplied.
-template <int NS>
-__global__ __launch_bounds__(256) void router_logits_kernel(RouterArgs a, float *partial,
-                                                            int chunks_per_slice) {
-  constexpr int TT = kRouterMT / 32;  // token tiles per block
-  __shared__ float part[4][kRouterMT][NS * 32 + 1];
+// MFMA operand layout (v_mfma_f32_32x32x16_bf16, A = the rows, B = the
+// weight terms): lane l supplies token l % 32 of A and expert l % 32 of B,
+// each with 8 consecutive k values; any k assignment is valid as long as A
+// and B agree: in chunk c lane half g takes k in 64 c + 32 g + [0, 32) and
+// step q its elements [8 q, 8 q + 8), so each lane reads 64 contiguous bytes
+// of its row per chunk, and the weight's terms come in the fragment order of
+// router_split_kernel. The three terms of a weight go into the same
+// accumulator, hi first. Result element v of lane l is token
+// 8 (v / 4) + 4 (l / 32) + v % 4 and expert l % 32 of the wave's tile.
+// Padding rows are not read (their partial logits are 0, never used) and get
+// no normalised row.
+struct RouterSliceArgs {
+  const uint16_t *x;
+  const u32x4_t *wsplit;   // the weight's three bf16 terms in fragment order
+  const uint16_t *norm_w;  // [H] (NORM)
+  const float *rrow;       // [T] r of each real row (NORM)
+  uint16_t *xn;            // [T, H] (NORM)
+  const uint8_t *pad;
+  int64_t T;
+  int H, E;
+  int cps;                 // chunks per slice
+  float *partial;          // [slices][T][E]
+};
+
+template <bool NORM>
+__global__ __launch_bounds__(512) void router_slice_kernel(RouterSliceArgs a) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int r = lane & 31;
-  const int g = lane >> 5;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterMT;
-  const uint16_t *x = static_cast<const uint16_t *>(a.x);
-  const int nchunks = a.H / 64;
-
-  const uint16_t *xrow[TT];
-  bool row_ok[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int64_t t = t0 + tt * 32 + r;
-    row_ok[tt] = t < a.T && !(a.pad && a.pad[t]);
-    xrow[tt] = x + (row_ok[tt] ? t : 0) * static_cast<int64_t>(a.H);
+  const int r = lane & 31, g = lane >> 5;
+  const int tt = wave & 3, y = wave >> 2;
+  if (y * 32 >= a.E) return;  // E <= 32: one expert tile (no barrier below)
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouterMT + tt * 32 + r;
+  const bool tok = t < a.T && !(a.pad && a.pad[t]);
+  const int H = a.H;
+  const int nchunks = H / 64;
+  const int c_lo = blockIdx.y * a.cps;
+  const int c_hi = min(nchunks, c_lo + a.cps);
+  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(a.x + (tok ? t : 0) * H) + 4 * g;
+  // this lane's weight pieces: (chunk c, term sp, step q) at
+  // wt[(c * 3 + sp) * 256 + q * 32]
+  const u32x4_t *wt = a.wsplit + (static_cast<int64_t>(y) * nchunks * 3 * 2 + g) * 128 + r;
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  float rt = 1.0f;
+  const u32x4_t *nwr = nullptr;
+  u32x4_t *xno = nullptr;
+  if constexpr (NORM) {
+    rt = tok ? a.rrow[t] : 1.0f;
+    nwr = reinterpret_cast<const u32x4_t *>(a.norm_w) + 4 * g;
+    xno = reinterpret_cast<u32x4_t *>(a.xn + (tok ? t : 0) * H) + 4 * g;
   }
+  const bool write_xn = NORM && tok && y == 0;
 
-  f32x16_t acc[TT][NS];
+  // four accumulators, chunk c into acc[(c - c_lo) % 4], added in a fixed
+  // order at the end: each fp32 sum runs over at most a quarter of the
+  // slice's products (large slices, when T is large, keep the rounding of
+  // the logits as small as small slices do)
+  f32x16_t acc[4];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[tt][n][v] = 0.0f;
-
-  const int c_first = blockIdx.y * chunks_per_slice;
-  const int c_end = min(nchunks, c_first + chunks_per_slice);
-  // operands of one chunk: the split weights' fragments and the token rows
-  u32x4_t wv[NS][3][4];
-  u32x4_t xv[TT][4];
+    for (int v = 0; v < 16; ++v) acc[u][v] = 0.0f;
+  u32x4_t xv[4], wv[3][4];
   auto load = [&](int c) __attribute__((always_inline)) {
-    const int k0 = c * 64 + g * 32;
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
+    for (int q = 0; q < 4; ++q) xv[q] = tok ? xr[8 * c + q] : zero4;
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp) {
-        // fragment order: the 4 steps' 1 KiB blocks of (sp, n, c) are adjacent
-        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(a.wsplit) +
-                           (((static_cast<int64_t>(sp) * NS + n) * nchunks + c) * 4) * 64 + lane;
+    for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wv[n][sp][q] = p[q * 64];
+      for (int q = 0; q < 4; ++q) wv[sp][q] = wt[(static_cast<int64_t>(c) * 3 + sp) * 256 + q * 32];
+  };
+  // one chunk: multiply the operands loaded for it (after starting the next
+  // chunk's loads) into accumulator ac
+  auto chunk = [&](int c, f32x16_t &ac) __attribute__((always_inline)) {
+    u32x4_t av[4], bw[3][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) av[q] = xv[q];
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bw[sp][q] = wv[sp][q];
+    if (c + 1 < c_hi) load(c + 1);
+    if constexpr (NORM) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q] = norm_chunk<kBF16>(av[q], nwr[8 * c + q], rt);
+        if (write_xn) xno[8 * c + q] = av[q];
       }
+    }
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const u32x4_t *p = reinterpret_cast<const u32x4_t *>(xrow[tt] + k0);
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, av[q]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[tt][q] = row_ok[tt] ? p[q] : u32x4_t{0u, 0u, 0u, 0u};
+      for (int sp = 0; sp < 3; ++sp)
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8_t, bw[sp][q]),
+                                                     ac, 0, 0, 0);
     }
   };
-  int c = c_first + wave;
-  if (c < c_end) load(c);
-  for (; c < c_end; c += 4) {
-    // keep this chunk's operands, then request the next chunk's before the
-    // MFMAs
-    u32x4_t bw[NS][3][4];
-    u32x4_t av[TT][4];
-#pragma unroll
-    for (int n = 0; n < NS; ++n)
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bw[n][sp][q] = wv[n][sp][q];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) av[tt][q] = xv[tt][q];
-    if (c + 4 < c_end) load(c + 4);
-    // consecutive MFMAs update different accumulators (TT x NS of them)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int n = 0; n < NS; ++n)
-            acc[tt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, av[tt][q]),
-                __builtin_bit_cast(bf16x8_t, bw[n][sp][q]), acc[tt][n], 0, 0, 0);
+  if (c_lo < c_hi) load(c_lo);
+  for (int c = c_lo; c < c_hi; c += 4) {
+    chunk(c, acc[0]);
+    if (c + 1 < c_hi) chunk(c + 1, acc[1]);
+    if (c + 2 < c_hi) chunk(c + 2, acc[2]);
+    if (c + 3 < c_hi) chunk(c + 3, acc[3]);
   }
+  float *out = a.partial + static_cast<int64_t>(blockIdx.y) * a.T * a.E;
+  const int e = y * 32 + r;
+  if (e < a.E) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-    for (int n = 0; n < NS; ++n)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        part[wave][tt * 32 + (v >> 2) * 8 + g * 4 + (v & 3)][n * 32 + r] = acc[tt][n][v];
-  __syncthreads();
-  float *out = partial + static_cast<int64_t>(blockIdx.y) * a.E * a.T;
-  for (int i = threadIdx.x; i < kRouterMT * a.E; i += blockDim.x) {
-    const int rr = i / a.E, e = i % a.E;
-    const int64_t t = t0 + rr;
-    if (t < a.T)
-      out[t * a.E + e] = ((part[0][rr][e] + part[1][rr][e]) + part[2][rr][e]) + part[3][rr][e];
+    for (int v = 0; v < 16; ++v) {
+      const int64_t tv = static_cast<int64_t>(blockIdx.x) * kRouterMT + tt * 32 + (v >> 2) * 8 +
+                         g * 4 + (v & 3);
+      if (tv < a.T) out[tv * a.E + e] = ((acc[0][v] + acc[1][v]) + acc[2][v]) + acc[3][v];
+    }
   }
+}
+
+// r = 1 / sqrt(mean(x^2) + eps) of every real row, exactly as the RMSNorm
+// kernel forms it (fp64 sum of the squares, the same butterfly order, one
+// rounding of the mean, r evaluated in fp64 and rounded once to fp32): one
+// wave per row, four rows per block, the row read once. Padding rows get
+// none.
+__global__ __launch_bounds__(256) void row_rms_kernel(const uint16_t *__restrict__ x,
+                                                      const uint8_t *__restrict__ pad,
+                                                      int64_t T, int H, float eps,
+                                                      float *__restrict__ rrow) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T || (pad && pad[t])) return;
+  const int nc = H / 8;  // 16-byte chunks
+  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + t * H);
+  double ss = 0.0;
+  // (eight loads in flight per lane at a time)
+  for (int i0 = 0; i0 < nc; i0 += 8 * 64) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 64 * u + lane;
+      v[u] = i < nc ? xr[i] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ss += chunk_sq<kBF16>(v[u]);
+  }
+  const float rv = rms_finish(ss, H, eps);
+  if (lane == 0) rrow[t] = rv;
 }
 
 int router_slices(int64_t T, int H) {
   const int nb = static_cast<int>((T + kRouterMT - 1) / kRouterMT);
-  // one block per CU (the block's LDS allows no second one): at most 256
-  // blocks, so none waits for a second round; at least 4 chunks (one per
-  // wave) per slice
-  const int max_slices = std::max(1, std::min(kRouterMaxSlices, H / 256));
-  const int want = 256 / nb;
-  return std::max(1, std::min(max_slices, want));
+  // one round of blocks (at most 256, one per CU), at least one chunk per
+  // slice
+  return std::max(1, std::min(std::min(kRouterMaxSlices, H / 64), 256 / nb));
 }
 
 // --------------------------------------------------------------- fp32 router
@@ -364,18 +435,30 @@ hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStre
   const int nb = static_cast<int>((a.T + kRouterTB - 1) / kRouterTB);
   int slices = 1;
   if (dtype == kF32) {
+    if (a.norm_w) return hipErrorInvalidValue;  // fp32 layers normalise in their own kernel
     hipLaunchKernelGGL(router_f32_kernel, dim3(nb), dim3(256), 0, s, a, partial);
   } else {
-    const int64_t nw = static_cast<int64_t>(a.Epad) * a.H;
-    hipLaunchKernelGGL(split_router_kernel, dim3(static_cast<unsigned>((nw + 255) / 256)),
-                       dim3(256), 0, s, a.w_router, a.wsplit, a.E, a.Epad, a.H);
+    const int Epad = (a.E + 31) / 32 * 32;
+    const int64_t n = static_cast<int64_t>(Epad) * a.H / 8;
+    hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, s, a.w_router, a.E, Epad, a.H,
+                       static_cast<u32x4_t *>(a.wsplit));
+    if (a.norm_w)
+      hipLaunchKernelGGL(row_rms_kernel, dim3(static_cast<unsigned>((a.T + 3) / 4)), dim3(256), 0,
+                         s, static_cast<const uint16_t *>(a.x), a.pad, a.T, a.H, a.eps, a.rrow);
     slices = router_slices(a.T, a.H);
-    const int cps = (a.H / 64 + slices - 1) / slices;
-    const dim3 grid(static_cast<unsigned>((a.T + kRouterMT - 1) / kRouterMT), slices);
-    if (a.Epad <= 32)
-      hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, s, a, partial, cps);
+    const int nchunks = a.H / 64;
+    const int cps = (nchunks + slices - 1) / slices;
+    slices = (nchunks + cps - 1) / cps;  // no empty slice
+    RouterSliceArgs ra{static_cast<const uint16_t *>(a.x), static_cast<const u32x4_t *>(a.wsplit),
+                       static_cast<const uint16_t *>(a.norm_w), a.rrow,
+                       static_cast<uint16_t *>(a.xn), a.pad, a.T, a.H, a.E, cps, partial};
+    const dim3 grid(static_cast<unsigned>((a.T + kRouterMT - 1) / kRouterMT),
+                    static_cast<unsigned>(slices));
+    if (a.norm_w)
+      hipLaunchKernelGGL(router_slice_kernel<true>, grid, dim3(512), 0, s, ra);
     else
-      hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, a, partial, cps);
+      hipLaunchKernelGGL(router_slice_kernel<false>, grid, dim3(512), 0, s, ra);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -159,3 +159,32 @@ def test_forward_norm_residual_full_size():
     out, idx, w, cnt = _gpu_forward_nr(upload(d), wl.shape.K, pad)
     rows = np.random.default_rng(0).choice(wl.T, 48, replace=False)
     _check_nr(d, wl.shape.K, pad, out, idx, w, cnt, rows=np.sort(rows))
+
+
+@pytest.mark.parametrize("H,T,pad_rows", [(512, 700, 0), (256, 333, 40), (4096, 4131, 0)])
+def test_fused_norm_routes_match_plain_forward_on_rmsnorm(H, T, pad_rows):
+    """The block forward normalises inside its router kernel (bf16): its
+    normalised rows must be hi3_moe_rmsnorm's bit for bit, so its routes and
+    counts equal those of hi3_moe_forward on hi3_moe_rmsnorm(h), bit for bit
+    (the router weights' fp32 bits included)."""
+    import moe_decoder_ffn_amd as m
+    _say(f"[norm] fused norm routes H={H} T={T} pad_rows={pad_rows}")
+    E, K = 64, 8
+    shape = wk.LayerShape(H=H, E=E, K=K, I=128, Is=128, dtype=wk.BF16)
+    wl = wk.custom(shape, (T - pad_rows,), T)
+    d = wk.make_inputs(wl, 17)
+    d["w_router"] = d["w_router"] * np.float32(3.0)
+    d["norm_w"] = wk.make_norm_weight(shape, 17)
+    pad = d["pad_mask"] if pad_rows else None
+    dd = upload(d)
+    padd = to_dev(pad) if pad is not None else None
+    _, idx_b, w_b, cnt_b = m.moe_forward_norm_residual(
+        dd["x"], dd["norm_w"], dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"], K,
+        pad_mask=padd, return_routes=True)
+    xn = torch.zeros_like(dd["x"])
+    m.hi3_moe_rmsnorm(dd["x"], dd["norm_w"], 1e-5, padd, xn)
+    _, idx_p, w_p, cnt_p = m.moe_forward(xn, dd["w_router"], dd["w13"], dd["w2"], dd["ws13"],
+                                         dd["ws2"], K, pad_mask=padd, return_routes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_b, idx_p) and torch.equal(cnt_b, cnt_p)
+    assert torch.equal(w_b.view(torch.int32), w_p.view(torch.int32))
