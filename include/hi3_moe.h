@@ -76,9 +76,9 @@ extern "C" {
 #define HI3_E_SCRATCH (-6)     /* sizes too large for hi3_moe_forward_noalloc */
 
 /* Number of timed stages of hi3_moe_forward_instrumented. */
-#define HI3_NUM_STAGES 6
+#define HI3_NUM_STAGES 5
 /* Number of timed stages of hi3_moe_backward_instrumented. */
-#define HI3_NUM_BWD_STAGES 11
+#define HI3_NUM_BWD_STAGES 10
 
 /*
  * Workspace bytes that hi3_moe_forward and hi3_moe_forward_norm_residual

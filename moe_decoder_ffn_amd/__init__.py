@@ -25,8 +25,8 @@ HI3_E_WORKSPACE = -4
 HI3_E_HIP = -5
 HI3_E_SCRATCH = -6
 HI3_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
-HI3_NUM_STAGES = 6
-HI3_NUM_BWD_STAGES = 11
+HI3_NUM_STAGES = 5
+HI3_NUM_BWD_STAGES = 10
 
 EXPORTED = (
     "hi3_moe_workspace_size",

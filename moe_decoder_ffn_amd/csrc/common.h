@@ -300,9 +300,7 @@ struct Plan {
   size_t idx;     // [T*K] int32 routes when the caller passes none
   size_t wts;     // [T*K] fp32
   size_t blkcnt;  // [NB][E] int32 per-block expert histogram
-  size_t blkoff;  // [NB][E] int32 first slot of each (block, expert)
   size_t blkval;  // [NB] int32 real rows per block
-  size_t blkvoff; // [NB] int32 first real-row index of each block
   size_t eoff;    // [E+1] int32 expert offsets
   size_t counts;  // [E] int32
   size_t misc;    // [16] int32: [0] real rows
@@ -370,9 +368,7 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
   p.idx = take(TK * 4);
   p.wts = take(TK * 4);
   p.blkcnt = take(static_cast<size_t>(p.NB) * E * 4);
-  p.blkoff = take(static_cast<size_t>(p.NB) * E * 4);
   p.blkval = take(static_cast<size_t>(p.NB) * 4);
-  p.blkvoff = take(static_cast<size_t>(p.NB) * 4);
   p.eoff = take((E + 1) * 4);
   p.counts = take(E * 4);
   p.misc = take(16 * 4);
@@ -438,8 +434,6 @@ struct ScanArgs {
   const int32_t *blkcnt;
   const int32_t *blkval;
   int NB, E, BM;
-  int32_t *blkoff;
-  int32_t *blkvoff;
   int32_t *eoff;
   int32_t *counts_out;  // nullable (caller's expert_counts)
   int32_t *counts;      // workspace copy
@@ -454,8 +448,6 @@ struct ScanArgs {
 struct ScatterArgs {
   const int32_t *idx;
   const uint8_t *pad;
-  const int32_t *blkoff;
-  const int32_t *blkvoff;
   int64_t T;
   int E, K;
   int32_t *perm;
@@ -560,8 +552,9 @@ hipError_t launch_rmsnorm_backward(const NormBwdArgs &a, int dtype, hipStream_t 
 hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStream_t s);
 hipError_t launch_histogram(const int32_t *idx, const uint8_t *pad, int64_t T, int E,
                             int K, int32_t *blkcnt, int32_t *blkval, hipStream_t s);
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
-hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
+// Expert offsets, counts and row tiles (a) and, with c, the slots of every
+// pair (one block per kRouterTB tokens); without c only the former.
+hipError_t launch_dispatch(const ScanArgs &a, const ScatterArgs *c, hipStream_t s);
 hipError_t launch_gather(const void *x, int64_t row_bytes, const int32_t *slotof,
                          const uint8_t *pad, int64_t T, int K, void *xs, hipStream_t s);
 // tile_rows: rows per listed row tile (the plan's BM); it selects the bf16

@@ -188,24 +188,19 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     st = fork_shared();
     if (st != HI3_OK) return st;
   }
-  // 1: scans -> expert offsets, real-row list, GEMM row tiles
+  // 1: dispatch: expert offsets, GEMM row tiles, real-row list, stable slots
   rec.at(1);
-  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
-              static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
-              static_cast<int32_t *>(at(p.eoff)), expert_counts,
+  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM, static_cast<int32_t *>(at(p.eoff)), expert_counts,
               static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
               static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
   sa.no_shared = side ? 1 : 0;
-  HI3_TRY(launch_scan(sa, s));
-  // 2: stable slots
-  rec.at(2);
   int32_t *perm = static_cast<int32_t *>(at(p.perm));
-  ScatterArgs sc{idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm, slotof, vtok, vidx};
-  HI3_TRY(launch_scatter(sc, s));
-  // 3: grouped [up; gate] projection + SwiGLU (routed experts and the shared
+  ScatterArgs sc{idx, pad_mask, T, E, K, perm, slotof, vtok, vidx};
+  HI3_TRY(launch_dispatch(sa, &sc, s));
+  // 2: grouped [up; gate] projection + SwiGLU (routed experts and the shared
   // expert); the routed rows are gathered from x through the slot -> token map
   // by the GEMM's operand copies, so no grouped copy of x is materialised
-  rec.at(3);
+  rec.at(2);
   GemmArgs up{};
   up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
   up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
@@ -217,8 +212,8 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   up.gto = gto;
   up.E = E;
   HI3_TRY(launch_gemm_upgate(up, main_tiles, p.BM, dtype, s));
-  // 4: grouped down projection
-  rec.at(4);
+  // 3: grouped down projection
+  rec.at(3);
   GemmArgs dn{};
   dn.cls[0] = GemmClass{at(p.h), I, nullptr, w_down, int64_t{H} * I, at(p.y), H, H, I};
   dn.cls[1] = GemmClass{at(p.hs), Is, nullptr, w_shared_down, 0, at(p.ys), H, H, Is};
@@ -226,8 +221,8 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   dn.gto = gto;
   dn.E = E;
   HI3_TRY(launch_gemm_down(dn, main_tiles, p.BM, dtype, s));
-  // 5: combine (after the shared expert's output, when the side stream made it)
-  rec.at(5);
+  // 4: combine (after the shared expert's output, when the side stream made it)
+  rec.at(4);
   if (side && !fork.end()) return HI3_E_HIP;
   CombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                  slotof, vidx, wts, pad_mask, T, H, K, out, resid};
@@ -236,7 +231,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
     HI3_TRY(hipMemcpyAsync(topk_idx, idx, size_t(T) * K * 4, hipMemcpyDeviceToDevice, s));
   if (save && topk_w)
     HI3_TRY(hipMemcpyAsync(topk_w, wts, size_t(T) * K * 4, hipMemcpyDeviceToDevice, s));
-  rec.at(6);
+  rec.at(5);
   return rec.ok ? HI3_OK : HI3_E_HIP;
 }
 
@@ -327,20 +322,13 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   }
   rec.at(1);
   if (!reuse) {
-    ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
-                static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
-                static_cast<int32_t *>(at(p.eoff)), nullptr,
+    ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM, static_cast<int32_t *>(at(p.eoff)), nullptr,
                 static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
                 static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
-    HI3_TRY(launch_scan(sa, s));
+    ScatterArgs sc{idx, pad_mask, T, E, K, perm, slotof, vtok, vidx};
+    HI3_TRY(launch_dispatch(sa, &sc, s));
   }
   rec.at(2);
-  if (!reuse) {
-    ScatterArgs sc{idx, pad_mask, static_cast<int32_t *>(at(p.blkoff)),
-                   static_cast<int32_t *>(at(p.blkvoff)), T, E, K, perm, slotof, vtok, vidx};
-    HI3_TRY(launch_scatter(sc, s));
-  }
-  rec.at(3);
   if (!reuse) {
     GemmArgs up{};
     up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
@@ -353,7 +341,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
     HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
   }
   // 4: x and w dout by slot; x and dout by real row when there is padding
-  rec.at(4);
+  rec.at(3);
   const bool compact = pad_mask != nullptr;
   BwdGatherArgs ga{x, dout, wts, slotof, vidx, pad_mask, T, H, K, at(p.xs), at(p.dys),
                    static_cast<float *>(at(p.wslot)), compact ? at(p.xv) : nullptr,
@@ -361,7 +349,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   HI3_TRY(launch_bwd_gather(ga, dtype, s));
   // 5: dh = w W2^T dout (dout rows gathered through the slot -> token map, w
   // applied in fp32) and the SwiGLU backward: [du; dg], partial sums of dh h
-  rec.at(5);
+  rec.at(4);
   GemmArgs d2{};
   d2.cls[0] = GemmClass{dout, H, perm, w_down, int64_t{H} * I, at(p.dd), 2 * I, I, H};
   d2.cls[0].rowscale = static_cast<const float *>(at(p.wslot));
@@ -379,7 +367,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   d2.E = E;
   HI3_TRY(launch_gemm_dgrad_down(d2, p.max_tiles, p.BM, dtype, s));
   // 6: dx by slot / by real row = W13^T [du; dg]
-  rec.at(6);
+  rec.at(5);
   if (dx || want_dxn) {
     GemmArgs d3{};
     d3.cls[0] = GemmClass{at(p.dd), 2 * I, nullptr, w_up_gate, int64_t{2} * I * H, at(p.y), H,
@@ -394,7 +382,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
     HI3_TRY(launch_gemm_dgrad_up_gate(d3, p.max_tiles, p.BM, dtype, s));
   }
   // 7: logit gradient and dx
-  rec.at(7);
+  rec.at(6);
   float *dls = static_cast<float *>(at(p.dls));
   BwdCombineArgs ca{static_cast<const float *>(at(p.y)), static_cast<const float *>(at(p.ys)),
                     static_cast<const float *>(at(p.apart)), p.P, slotof, idx, vidx, wts,
@@ -402,13 +390,13 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
                     want_dxn ? static_cast<float *>(at(p.dxn)) : nullptr};
   HI3_TRY(launch_bwd_combine(ca, dtype, s));
   // 8: router weight gradient
-  rec.at(8);
+  rec.at(7);
   if (dw_router)
     HI3_TRY(launch_dw_router(dls, at(p.xs), tiles, gto, p.max_tiles, E, H, dtype,
                              static_cast<float *>(at(p.dwrpart)), dw_router, s));
   // 9, 10: expert weight gradients
   HI3_TRY(launch_zero(at(p.zrow), 512, s));
-  rec.at(9);
+  rec.at(8);
   GemmArgs w2{};
   w2.goff = eoff;
   w2.gcnt = counts;
@@ -428,7 +416,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
     w2.cls[1].M = H; w2.cls[1].N = Is;
   }
   HI3_TRY(launch_gemm_wgrad(w2, E, dtype, s));
-  rec.at(10);
+  rec.at(9);
   GemmArgs w13 = w2;
   w13.cls[0] = GemmClass{};
   w13.cls[1] = GemmClass{};
@@ -445,7 +433,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
     w13.cls[1].M = 2 * Is; w13.cls[1].N = H;
   }
   HI3_TRY(launch_gemm_wgrad(w13, E, dtype, s));
-  rec.at(11);
+  rec.at(10);
   if (want_dxn) {
     NormBwdArgs nb{h_in, norm_weight, pad_mask, T, H, eps,
                    static_cast<const float *>(at(p.dxn)), dout, dh,
@@ -510,12 +498,11 @@ int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask,
                 static_cast<int32_t *>(at(p.blkval))};
   HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
   if (expert_counts) {
-    ScanArgs sa{ra.blkcnt, ra.blkval, p.NB, E, p.BM,
-                static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
-                static_cast<int32_t *>(at(p.eoff)), expert_counts,
-                static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
-                static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
-    HI3_TRY(launch_scan(sa, s));
+    ScanArgs sa{ra.blkcnt, ra.blkval, p.NB, E, p.BM, static_cast<int32_t *>(at(p.eoff)),
+                expert_counts, static_cast<int32_t *>(at(p.counts)),
+                static_cast<int32_t *>(at(p.misc)), static_cast<int32_t *>(at(p.gto)),
+                static_cast<int4 *>(at(p.tiles))};
+    HI3_TRY(launch_dispatch(sa, nullptr, s));
   }
   return HI3_OK;
 }
@@ -542,15 +529,11 @@ int hi3_moe_dispatch(const int32_t *topk_idx, const uint8_t *pad_mask, const voi
   int32_t *blkcnt = static_cast<int32_t *>(at(p.blkcnt));
   int32_t *blkval = static_cast<int32_t *>(at(p.blkval));
   HI3_TRY(launch_histogram(topk_idx, pad_mask, T, E, K, blkcnt, blkval, s));
-  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM,
-              static_cast<int32_t *>(at(p.blkoff)), static_cast<int32_t *>(at(p.blkvoff)),
-              expert_offsets, nullptr, static_cast<int32_t *>(at(p.counts)),
-              static_cast<int32_t *>(at(p.misc)), static_cast<int32_t *>(at(p.gto)),
-              static_cast<int4 *>(at(p.tiles))};
-  HI3_TRY(launch_scan(sa, s));
-  ScatterArgs sc{topk_idx, pad_mask, sa.blkoff, sa.blkvoff, T, E, K, perm_token, slot_of,
-                 nullptr, nullptr};
-  HI3_TRY(launch_scatter(sc, s));
+  ScanArgs sa{blkcnt, blkval, p.NB, E, p.BM, expert_offsets, nullptr,
+              static_cast<int32_t *>(at(p.counts)), static_cast<int32_t *>(at(p.misc)),
+              static_cast<int32_t *>(at(p.gto)), static_cast<int4 *>(at(p.tiles))};
+  ScatterArgs sc{topk_idx, pad_mask, T, E, K, perm_token, slot_of, nullptr, nullptr};
+  HI3_TRY(launch_dispatch(sa, &sc, s));
   if (x_sorted) {
     const size_t es = dtype == HI3_BF16 ? 2 : 4;
     HI3_TRY(launch_gather(x, static_cast<int64_t>(H) * es, slot_of, pad_mask, T, K, x_sorted, s));
@@ -714,7 +697,7 @@ int hi3_moe_backward_norm_residual(const void *h, const void *norm_weight, float
 
 const char *hi3_moe_backward_stage_name(int stage) {
   static const char *names[HI3_NUM_BWD_STAGES] = {
-      "router", "scan", "scatter", "gemm_up_gate_recompute", "gather_bwd", "gemm_dgrad_down",
+      "router", "dispatch", "gemm_up_gate_recompute", "gather_bwd", "gemm_dgrad_down",
       "gemm_dgrad_up_gate", "combine_bwd", "dw_router", "gemm_wgrad_down",
       "gemm_wgrad_up_gate"};
   if (stage < 0 || stage >= HI3_NUM_BWD_STAGES) return "?";
@@ -723,7 +706,7 @@ const char *hi3_moe_backward_stage_name(int stage) {
 
 const char *hi3_moe_stage_name(int stage) {
   static const char *names[HI3_NUM_STAGES] = {
-      "router", "scan", "scatter", "gemm_up_gate_swiglu", "gemm_down", "combine"};
+      "router", "dispatch", "gemm_up_gate_swiglu", "gemm_down", "combine"};
   if (stage < 0 || stage >= HI3_NUM_STAGES) return "?";
   return names[stage];
 }

@@ -47,6 +47,7 @@ struct SelectShared {
   float psel[kRouterTB][kMaxE];
   int esel[kRouterTB][kMaxE];
   uint64_t selmask[kRouterTB];
+  float row[kSelThreads / 64][kMaxE];  // one token's values, broadcast to its wave
 };
 
 __device__ __forceinline__ float nan_as_neg_inf(float v) { return v != v ? -INFINITY : v; }
@@ -118,26 +119,42 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
     // A NaN logit counts as -infinity: the order (larger first, lower index
     // on equal values) is then total, the ranks of the E lanes are a
     // permutation, and exactly K experts are selected whatever the inputs.
-    // Every lane walks the row's logits in expert order (readlane: no
-    // memory round trips) for the maximum, its own rank in the selection
-    // order and the softmax denominator, summed in ascending expert order.
+    // Every lane reads the row's logits (written to LDS once, read back as
+    // broadcasts) in expert order for the maximum, its own rank in the
+    // selection order and the softmax denominator, summed in ascending
+    // expert order (every lane forms the same sum).
     const bool live = lane < E;
     const float l = live ? nan_as_neg_inf(lsum[j]) : -INFINITY;
+    const f32x4_t *rowv = reinterpret_cast<const f32x4_t *>(sh.row[wave]);
+    sh.row[wave][lane] = l;
+    wave_lds_sync();
     float m = -INFINITY;
     int rank = 0;
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if (EC == 0 && e >= E) continue;  // (wave-uniform)
-      const float ve = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
-      m = fmaxf(m, ve);
-      rank += (ve > l || (ve == l && e < lane)) ? 1 : 0;
+    for (int e4 = 0; e4 < kMaxE / 4; ++e4) {
+      const f32x4_t v4 = rowv[e4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * e4 + u;
+        if (EC == 0 && e >= E) continue;
+        const float ve = v4[u];
+        m = fmaxf(m, ve);
+        rank += (ve > l || (ve == l && e < lane)) ? 1 : 0;
+      }
     }
     const float ex = live ? expf(l - m) : 0.0f;
+    wave_lds_sync();  // every lane has read the logits before they are overwritten
+    sh.row[wave][lane] = ex;
+    wave_lds_sync();
     float z = 0.0f;
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if (EC == 0 && e >= E) continue;
-      z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), e));
+    for (int e4 = 0; e4 < kMaxE / 4; ++e4) {
+      const f32x4_t v4 = rowv[e4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (EC == 0 && 4 * e4 + u >= E) continue;
+        z += v4[u];
+      }
     }
     const float p = ex / z;
     const bool sel = live && rank < K;
