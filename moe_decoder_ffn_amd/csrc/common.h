@@ -28,6 +28,11 @@ constexpr int kRouterTB = 32;
 // many slices of the hidden dimension.
 constexpr int kRouterMT = 128;
 constexpr int kRouterMaxSlices = 16;
+// Logit blocks per round of the GPU (two 4-wave blocks per CU).
+#ifndef HI3_ROUTER_ROUND
+#define HI3_ROUTER_ROUND 512
+#endif
+constexpr int kRouterRound = HI3_ROUTER_ROUND;
 // Rows per partial sum of the RMSNorm weight gradient (block backward).
 constexpr int kNormBwdRows = 64;
 
@@ -296,7 +301,6 @@ struct Plan {
   int BM;         // grouped-GEMM tile rows (per dtype)
   int max_tiles;  // upper bound on grouped-GEMM row tiles
   size_t rpart;   // [slices][T][E] fp32: router partial logits
-  size_t wsplit;  // [3][E rounded up to 32][H] bf16: the router weight's terms
   size_t idx;     // [T*K] int32 routes when the caller passes none
   size_t wts;     // [T*K] fp32
   size_t blkcnt;  // [NB][E] int32 per-block expert histogram
@@ -364,7 +368,6 @@ inline Plan make_plan(int64_t T, int H, int E, int K, int I, int Is, int dtype,
     return at;
   };
   p.rpart = take(static_cast<size_t>(dtype == kBF16 ? router_slices(T, H) : 1) * T * E * 4);
-  p.wsplit = take(dtype == kBF16 ? static_cast<size_t>((E + 31) / 32 * 32) * H * 6 : 0);
   p.idx = take(TK * 4);
   p.wts = take(TK * 4);
   p.blkcnt = take(static_cast<size_t>(p.NB) * E * 4);
@@ -418,8 +421,6 @@ struct RouterArgs {
                        // the router as it is)
   float eps;
   void *xn;            // with norm_w: [T, H] normalised rows out (the experts' input)
-  void *wsplit;        // bf16 layers: [3][E rounded up to 32][H] bf16 scratch (the
-                       // weight's split terms)
   float *rrow;         // with norm_w: [T] fp32 scratch (r of each row)
   const uint8_t *pad;
   int64_t T;

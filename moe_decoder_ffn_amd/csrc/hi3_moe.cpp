@@ -180,7 +180,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   // 0: router + per-block histogram
   rec.at(0);
   RouterArgs ra{fused_norm ? x_in : x, w_router, fused_norm ? norm_weight : nullptr, eps,
-                fused_norm ? at(p.xn) : nullptr, at(p.wsplit),
+                fused_norm ? at(p.xn) : nullptr,
                 static_cast<float *>(at(p.rnorm)), pad_mask, T, H, E, K, idx, wts, blkcnt,
                 blkval};
   HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
@@ -315,7 +315,7 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
   rec.at(0);
   if (!reuse) {
     RouterArgs ra{fused_norm ? h_in : x, w_router, fused_norm ? norm_weight : nullptr, eps,
-                  fused_norm ? at(p.xn) : nullptr, at(p.wsplit),
+                  fused_norm ? at(p.xn) : nullptr,
                   static_cast<float *>(at(p.rnorm)), pad_mask, T, H, E, K, idx, wts, blkcnt,
                   blkval};
     HI3_TRY(launch_router(ra, dtype, static_cast<float *>(at(p.rpart)), s));
@@ -492,7 +492,7 @@ int hi3_moe_route(const void *x, const float *w_router, const uint8_t *pad_mask,
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   char *ws = static_cast<char *>(workspace);
   auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
-  RouterArgs ra{x, w_router, nullptr, 0.0f, nullptr, at(p.wsplit), nullptr,
+  RouterArgs ra{x, w_router, nullptr, 0.0f, nullptr, nullptr,
                 pad_mask, T, H, E, K, topk_idx, topk_w,
                 static_cast<int32_t *>(at(p.blkcnt)),
                 static_cast<int32_t *>(at(p.blkval))};

@@ -3,8 +3,8 @@
 // build_moe_config; the gate kept in fp32 per the model-coverage page,
 // "Train", and 'mlp.gate' in _keep_in_fp32_modules_strict).
 //
-// bf16 activations: each fp32 router weight is split, in registers, into
-// three bf16 terms hi + mid + lo that sum to it exactly (Henry, Tang &
+// bf16 activations: each fp32 router weight is split, as the logit kernel
+// stages it in LDS, into three bf16 terms hi + mid + lo that sum to it exactly (Henry, Tang &
 // Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype for
 // Higher-Precision Computations", ARITH 2019). Each product x * term is exact
 // in fp32, so bf16 MFMA with fp32 accumulation gives the fp32 router at
@@ -17,6 +17,7 @@
 // The selection kernel also builds the per-block expert histogram that the
 // stable counting sort scans (block b covers tokens [32b, 32b + 32)).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -192,70 +193,23 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
 
 // --------------------------------------------------------------- bf16 router
 
-// The three bf16 terms of an fp32 value: hi is v with its low 16 bits
-// cleared (exact), mid the same of the remainder, lo the rest (at most 8
-// significant bits, so its bf16 rounding is exact): hi + mid + lo == v.
-__device__ __forceinline__ void split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
-  const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
-  const float r1 = v - __uint_as_float(h);
-  const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
-  const float r2 = r1 - __uint_as_float(m);
-  hi = h >> 16;
-  mid = m >> 16;
-  lo = f32_to_bf16(r2);
-}
-
-// The router weight split once per call into its three bf16 terms (hi, mid,
-// lo; experts past E as zero rows), each stored in the logit kernel's
-// fragment order: the 8 terms that lane (r, g) multiplies in step q of chunk
-// c of expert tile y form the 16-byte piece
-//   ((((y * nchunks + c) * 3 + term) * 2 + g) * 4 + q) * 32 + r,
-// so each of the logit kernel's weight loads reads two contiguous 512-byte
-// runs, and no block splits the weight again.
-__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w, int E,
-                                                           int Epad, int H,
-                                                           u32x4_t *__restrict__ wsplit) {
-  const int64_t n = static_cast<int64_t>(Epad) * H / 8;  // groups of 8 weights
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int nch = H / 64;
-  const int r = static_cast<int>(i % 32);
-  int64_t rest = i / 32;
-  const int q = static_cast<int>(rest % 4);
-  rest /= 4;
-  const int g = static_cast<int>(rest % 2);
-  rest /= 2;
-  const int c = static_cast<int>(rest % nch);
-  const int y = static_cast<int>(rest / nch);
-  const int e = y * 32 + r;
-  const int k = 64 * c + 32 * g + 8 * q;
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-  if (e < E) {
-    const f32x4_t *src = reinterpret_cast<const f32x4_t *>(w + static_cast<int64_t>(e) * H + k);
-    const f32x4_t a0 = src[0], a1 = src[1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = a0[j];
-      v[4 + j] = a1[j];
-    }
-  }
-  u32x4_t th, tm, tl;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t h0, m0, l0, h1, m1, l1;
-    split3(v[2 * p], h0, m0, l0);
-    split3(v[2 * p + 1], h1, m1, l1);
-    th[p] = h0 | (h1 << 16);
-    tm[p] = m0 | (m1 << 16);
-    tl[p] = l0 | (l1 << 16);
-  }
-  const int64_t base = ((((static_cast<int64_t>(y) * nch + c) * 3) * 2 + g) * 4 + q) * 32 + r;
-  constexpr int64_t TERM = 2 * 4 * 32;  // pieces between the terms of one chunk
-  wsplit[base] = th;
-  wsplit[base + TERM] = tm;
-  wsplit[base + 2 * TERM] = tl;
+// The three bf16 terms of two fp32 values, packed in pairs (value 0 in the
+// low half): hi is v with its low 16 bits cleared (exact), mid the same of
+// the remainder, lo the rest, which has at most 8 significant bits and so
+// is a bf16 value itself (for |v| above 2^-110, below which lo may lose
+// bits of the fp32 subnormal range): hi + mid + lo == v, and each term is
+// the top half of an fp32 word, taken by a byte permute.
+__device__ __forceinline__ void split3x2(float v0, float v1, uint32_t &hi, uint32_t &mid,
+                                         uint32_t &lo) {
+  constexpr uint32_t kTop = 0xFFFF0000u;
+  constexpr uint32_t kTops = 0x07060302u;  // bytes 2, 3 of the second operand, then of the first
+  const uint32_t u0 = __float_as_uint(v0), u1 = __float_as_uint(v1);
+  const float r0 = v0 - __uint_as_float(u0 & kTop), r1 = v1 - __uint_as_float(u1 & kTop);
+  const uint32_t q0 = __float_as_uint(r0), q1 = __float_as_uint(r1);
+  const float s0 = r0 - __uint_as_float(q0 & kTop), s1 = r1 - __uint_as_float(q1 & kTop);
+  hi = __builtin_amdgcn_perm(u1, u0, kTops);
+  mid = __builtin_amdgcn_perm(q1, q0, kTops);
+  lo = __builtin_amdgcn_perm(__float_as_uint(s1), __float_as_uint(s0), kTops);
 }
 
 // Partial logits of kRouterMT = 128 tokens x 64 experts over one slice of the
@@ -263,29 +217,33 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
 // router weight is the same for every block of tokens, so the blocks take
 // 128 tokens each (fewer weight reads per token) and split the hidden
 // dimension for parallelism; the selection kernel adds the slices in order.
-// 8 waves: wave w owns tokens 32 (w % 4) .. + 31 and experts 32 (w / 4) ..
-// + 31, so every (token, expert) of the block is summed by one wave; the
-// four waves of an expert tile read the same weight pieces (L1). Each wave
-// loads the next chunk's operands while it multiplies the current one.
-// With NORM the rows are normalised on the fly with their r (computed by
-// row_rms_kernel): n = bf16(x r), xn = bf16(w n), and the first expert
-// tile's waves write xn (the expert GEMMs' input; every chunk of every real
-// row is written by exactly one wave).
 //
+// Each chunk is staged in LDS by all 256 threads with coalesced 16-byte
+// loads: the 128 token rows (normalised on the way with NORM), and the 64
+// expert rows of the fp32 weight, split on the way into their three bf16
+// terms. The loads run two chunks ahead of the multiplication (two register
+// sets, two LDS buffers, one barrier per chunk). With NORM the rows
+// are normalised with their r (computed by row_rms_kernel):
+// n = bf16(x r), xn = bf16(w n); the staging threads also write xn (the
+// expert GEMMs' input): every element of every real row is written once.
+//
+// 4 waves: wave w multiplies tokens 64 (w % 2) .. + 63 (two 32-token tiles)
+// by experts 32 (w / 2) .. + 31.
 // MFMA operand layout (v_mfma_f32_32x32x16_bf16, A = the rows, B = the
 // weight terms): lane l supplies token l % 32 of A and expert l % 32 of B,
 // each with 8 consecutive k values; any k assignment is valid as long as A
 // and B agree: in chunk c lane half g takes k in 64 c + 32 g + [0, 32) and
-// step q its elements [8 q, 8 q + 8), so each lane reads 64 contiguous bytes
-// of its row per chunk, and the weight's terms come in the fragment order of
-// router_split_kernel. The three terms of a weight go into the same
-// accumulator, hi first. Result element v of lane l is token
-// 8 (v / 4) + 4 (l / 32) + v % 4 and expert l % 32 of the wave's tile.
-// Padding rows are not read (their partial logits are 0, never used) and get
-// no normalised row.
+// step q its elements [8 q, 8 q + 8). The three terms of a weight go into
+// the same accumulator, hi first; chunk c goes into accumulator
+// (c - first chunk) % 2, and the two are added at the end (each fp32 sum
+// runs over at most half of the slice's products; with two blocks per CU
+// in a round, a slice holds at most 64 / (round / token blocks) chunks). Result
+// element v of lane l is token 8 (v / 4) + 4 (l / 32) + v % 4 and expert
+// l % 32 of the tile. Padding rows are not read (their partial logits are
+// 0, never used) and get no normalised row.
 struct RouterSliceArgs {
   const uint16_t *x;
-  const u32x4_t *wsplit;   // the weight's three bf16 terms in fragment order
+  const float *w;          // [E, H] fp32 router weight
   const uint16_t *norm_w;  // [H] (NORM)
   const float *rrow;       // [T] r of each real row (NORM)
   uint16_t *xn;            // [T, H] (NORM)
@@ -296,95 +254,176 @@ struct RouterSliceArgs {
   float *partial;          // [slices][T][E]
 };
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations
+// (lgkmcnt(0)) but not for its global loads, which may stay in flight
+// across it (__syncthreads() would also drain them).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// LDS position (16-byte units) of 16-byte piece c (0..7) of row `row` of a
+// staged chunk (128 bytes per row): piece c is stored at c ^ ((row / 2) % 8),
+// so the 16 rows of one fragment read fall in 16 distinct bank groups.
+__device__ __forceinline__ int rl_pos(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+
+struct RouterStage {
+  u32x4_t x[kRouterMT * 8];  // the chunk of the block's token rows
+  u32x4_t w[3][kMaxE * 8];   // the chunk of the weight's hi, mid and lo terms
+};
+
 template <bool NORM>
-__global__ __launch_bounds__(512) void router_slice_kernel(RouterSliceArgs a) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a) {
+  __shared__ RouterStage st[2];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int r = lane & 31, g = lane >> 5;
-  const int tt = wave & 3, y = wave >> 2;
-  if (y * 32 >= a.E) return;  // E <= 32: one expert tile (no barrier below)
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouterMT + tt * 32 + r;
-  const bool tok = t < a.T && !(a.pad && a.pad[t]);
+  const int tb = wave & 1, y = wave >> 1;
+  const int64_t T0 = static_cast<int64_t>(blockIdx.x) * kRouterMT;
   const int H = a.H;
   const int nchunks = H / 64;
   const int c_lo = blockIdx.y * a.cps;
   const int c_hi = min(nchunks, c_lo + a.cps);
-  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(a.x + (tok ? t : 0) * H) + 4 * g;
-  // this lane's weight pieces: (chunk c, term sp, step q) at
-  // wt[(c * 3 + sp) * 256 + q * 32]
-  const u32x4_t *wt = a.wsplit + (static_cast<int64_t>(y) * nchunks * 3 * 2 + g) * 128 + r;
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-  float rt = 1.0f;
-  const u32x4_t *nwr = nullptr;
-  u32x4_t *xno = nullptr;
-  if constexpr (NORM) {
-    rt = tok ? a.rrow[t] : 1.0f;
-    nwr = reinterpret_cast<const u32x4_t *>(a.norm_w) + 4 * g;
-    xno = reinterpret_cast<u32x4_t *>(a.xn + (tok ? t : 0) * H) + 4 * g;
-  }
-  const bool write_xn = NORM && tok && y == 0;
 
-  // four accumulators, chunk c into acc[(c - c_lo) % 4], added in a fixed
-  // order at the end: each fp32 sum runs over at most a quarter of the
-  // slice's products (large slices, when T is large, keep the rounding of
-  // the logits as small as small slices do)
-  f32x16_t acc[4];
+  // staging: piece p = tid + 256 u (u = 0..3) of the token rows (row p / 8,
+  // 16 bytes at 8 (p % 8) elements) and of the weight (expert p / 16, 4
+  // floats at 4 (p % 16))
+  // (row r0 + 32 u of the block and expert e0 + 16 u)
+  const int xp = tid & 7, wp = tid & 15;
+  const int r0 = tid >> 3, e0 = tid >> 4;
+  const int64_t xstep = int64_t{32} * H / 8;
+  // The loads are not predicated (a divergent branch around each would make
+  // the compiler drain every load in flight before the first use of any):
+  // a padding row or a row past T reads row 0 and an expert past E reads
+  // expert 0, and the staging zeroes them.
+  const u32x4_t *xsrc = reinterpret_cast<const u32x4_t *>(a.x) + xp;
+  const f32x4_t *wsrc = reinterpret_cast<const f32x4_t *>(a.w) + wp;
+  u32x4_t *xdst = NORM ? reinterpret_cast<u32x4_t *>(a.xn + (T0 + r0) * H) + xp : nullptr;
+  uint32_t xok = 0, wok = 0;  // bit u: row / expert u is real
+  int64_t xoff[4];            // 16-byte units
+  int32_t woff[4];
+  float rr[NORM ? 4 : 1];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u) {
+    const int64_t t = T0 + r0 + 32 * u;
+    const bool ok = t < a.T && !(a.pad && a.pad[t]);
+    const bool eok = e0 + 16 * u < a.E;
+    xok |= ok ? 1u << u : 0u;
+    wok |= eok ? 1u << u : 0u;
+    xoff[u] = ok ? t * (H / 8) : 0;
+    woff[u] = eok ? (e0 + 16 * u) * (H / 4) : 0;
+    if constexpr (NORM) rr[u] = ok ? a.rrow[t] : 1.0f;
+  }
+  const u32x4_t *nwsrc = NORM ? reinterpret_cast<const u32x4_t *>(a.norm_w) + xp : nullptr;
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  // two register sets of staged pieces: the chunk being loaded and the one
+  // loaded a step earlier (stored to LDS this step)
+  u32x4_t xs[2][4];
+  f32x4_t ws[2][4];
+  u32x4_t nws[2] = {zero4, zero4};
+  auto load = [&](auto S, int c) __attribute__((always_inline)) {
+    constexpr int b = decltype(S)::value;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[u][v] = 0.0f;
-  u32x4_t xv[4], wv[3][4];
-  auto load = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xv[q] = tok ? xr[8 * c + q] : zero4;
-#pragma unroll
-    for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wv[sp][q] = wt[(static_cast<int64_t>(c) * 3 + sp) * 256 + q * 32];
-  };
-  // one chunk: multiply the operands loaded for it (after starting the next
-  // chunk's loads) into accumulator ac
-  auto chunk = [&](int c, f32x16_t &ac) __attribute__((always_inline)) {
-    u32x4_t av[4], bw[3][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) av[q] = xv[q];
-#pragma unroll
-    for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bw[sp][q] = wv[sp][q];
-    if (c + 1 < c_hi) load(c + 1);
-    if constexpr (NORM) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        av[q] = norm_chunk<kBF16>(av[q], nwr[8 * c + q], rt);
-        if (write_xn) xno[8 * c + q] = av[q];
-      }
+    for (int u = 0; u < 4; ++u) {
+      xs[b][u] = xsrc[xoff[u] + 8 * c];
+      ws[b][u] = wsrc[woff[u] + 16 * c];
     }
+    if constexpr (NORM) nws[b] = nwsrc[8 * c];
+  };
+  auto store = [&](auto S, RouterStage &sg, int c) __attribute__((always_inline)) {
+    constexpr int b = decltype(S)::value;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = r0 + 32 * u;
+      const bool ok = (xok >> u) & 1u;
+      u32x4_t v = ok ? xs[b][u] : zero4;
+      if constexpr (NORM) {
+        v = norm_chunk<kBF16>(v, nws[b], rr[u]);
+        if (ok) xdst[u * xstep + 8 * c] = v;
+      }
+      sg.x[rl_pos(row, xp)] = v;
+      // the weight's three terms: 4 bf16 each, the half of a 16-byte piece
+      const int e = e0 + 16 * u;
+      const bool eok = (wok >> u) & 1u;
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3x2(eok ? ws[b][u][0] : 0.0f, eok ? ws[b][u][1] : 0.0f, h0, m0, l0);
+      split3x2(eok ? ws[b][u][2] : 0.0f, eok ? ws[b][u][3] : 0.0f, h1, m1, l1);
+      const int pos = rl_pos(e, wp >> 1);
+      const int half = wp & 1;
+      reinterpret_cast<u32x2_t *>(&sg.w[0][pos])[half] = u32x2_t{h0, h1};
+      reinterpret_cast<u32x2_t *>(&sg.w[1][pos])[half] = u32x2_t{m0, m1};
+      reinterpret_cast<u32x2_t *>(&sg.w[2][pos])[half] = u32x2_t{l0, l1};
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][u][v] = 0.0f;
+  // multiply the staged chunk in sg into accumulator u of both token tiles
+  auto compute = [&](const RouterStage &sg, auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value & 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, av[q]);
+      const int cc = 4 * g + q;
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, sg.x[rl_pos(64 * tb + r, cc)]);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, sg.x[rl_pos(64 * tb + 32 + r, cc)]);
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
-        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8_t, bw[sp][q]),
-                                                     ac, 0, 0, 0);
+      for (int sp = 0; sp < 3; ++sp) {
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, sg.w[sp][rl_pos(32 * y + r, cc)]);
+        acc[0][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][u], 0, 0, 0);
+        acc[1][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][u], 0, 0, 0);
+      }
     }
   };
-  if (c_lo < c_hi) load(c_lo);
-  for (int c = c_lo; c < c_hi; c += 4) {
-    chunk(c, acc[0]);
-    if (c + 1 < c_hi) chunk(c + 1, acc[1]);
-    if (c + 2 < c_hi) chunk(c + 2, acc[2]);
-    if (c + 3 < c_hi) chunk(c + 3, acc[3]);
+  // chunk c_lo + i is loaded into register set i % 2 and staged in LDS
+  // buffer i % 2; step i loads chunk i + 2, multiplies chunk i and stores
+  // chunk i + 1 (loaded a step earlier)
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (c_lo < c_hi) {
+    load(I0{}, c_lo);
+    if (c_lo + 1 < c_hi) load(I1{}, c_lo + 1);
+    store(I0{}, st[0], c_lo);
+  }
+  __syncthreads();
+  for (int c = c_lo; c < c_hi; c += 2) {
+    auto step = [&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int cu = c + u;
+      if (cu < c_hi) {
+        // (the scheduling barriers keep the loads ahead of the multiplication
+        // and of the staging, whose waits then leave them in flight)
+        if (cu + 2 < c_hi) load(U, cu + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st[u], U);
+        __builtin_amdgcn_sched_barrier(0);
+        if (cu + 1 < c_hi) store(std::integral_constant<int, 1 - u>{}, st[1 - u], cu + 1);
+        lds_barrier();
+      }
+    };
+    step(I0{});
+    step(I1{});
   }
   float *out = a.partial + static_cast<int64_t>(blockIdx.y) * a.T * a.E;
   const int e = y * 32 + r;
   if (e < a.E) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t tv = static_cast<int64_t>(blockIdx.x) * kRouterMT + tt * 32 + (v >> 2) * 8 +
-                         g * 4 + (v & 3);
-      if (tv < a.T) out[tv * a.E + e] = ((acc[0][v] + acc[1][v]) + acc[2][v]) + acc[3][v];
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t tv = T0 + 64 * tb + 32 * i + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (tv < a.T)
+          out[tv * a.E + e] = acc[i][0][v] + acc[i][1][v];
+      }
   }
 }
 
@@ -420,9 +459,8 @@ __global__ __launch_bounds__(256) void row_rms_kernel(const uint16_t *__restrict
 
 int router_slices(int64_t T, int H) {
   const int nb = static_cast<int>((T + kRouterMT - 1) / kRouterMT);
-  // one round of blocks (at most 256, one per CU), at least one chunk per
-  // slice
-  return std::max(1, std::min(std::min(kRouterMaxSlices, H / 64), 256 / nb));
+  // one round of blocks (at most kRouterRound), at least one chunk per slice
+  return std::max(1, std::min(std::min(kRouterMaxSlices, H / 64), kRouterRound / nb));
 }
 
 // --------------------------------------------------------------- fp32 router
@@ -455,11 +493,6 @@ hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStre
     if (a.norm_w) return hipErrorInvalidValue;  // fp32 layers normalise in their own kernel
     hipLaunchKernelGGL(router_f32_kernel, dim3(nb), dim3(256), 0, s, a, partial);
   } else {
-    const int Epad = (a.E + 31) / 32 * 32;
-    const int64_t n = static_cast<int64_t>(Epad) * a.H / 8;
-    hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, s, a.w_router, a.E, Epad, a.H,
-                       static_cast<u32x4_t *>(a.wsplit));
     if (a.norm_w)
       hipLaunchKernelGGL(row_rms_kernel, dim3(static_cast<unsigned>((a.T + 3) / 4)), dim3(256), 0,
                          s, static_cast<const uint16_t *>(a.x), a.pad, a.T, a.H, a.eps, a.rrow);
@@ -467,15 +500,15 @@ hipError_t launch_router(const RouterArgs &a, int dtype, float *partial, hipStre
     const int nchunks = a.H / 64;
     const int cps = (nchunks + slices - 1) / slices;
     slices = (nchunks + cps - 1) / cps;  // no empty slice
-    RouterSliceArgs ra{static_cast<const uint16_t *>(a.x), static_cast<const u32x4_t *>(a.wsplit),
+    RouterSliceArgs ra{static_cast<const uint16_t *>(a.x), a.w_router,
                        static_cast<const uint16_t *>(a.norm_w), a.rrow,
                        static_cast<uint16_t *>(a.xn), a.pad, a.T, a.H, a.E, cps, partial};
     const dim3 grid(static_cast<unsigned>((a.T + kRouterMT - 1) / kRouterMT),
                     static_cast<unsigned>(slices));
     if (a.norm_w)
-      hipLaunchKernelGGL(router_slice_kernel<true>, grid, dim3(512), 0, s, ra);
+      hipLaunchKernelGGL(router_slice_kernel<true>, grid, dim3(256), 0, s, ra);
     else
-      hipLaunchKernelGGL(router_slice_kernel<false>, grid, dim3(512), 0, s, ra);
+      hipLaunchKernelGGL(router_slice_kernel<false>, grid, dim3(256), 0, s, ra);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
