@@ -20,10 +20,14 @@ constexpr int kBF16 = 1;
 constexpr int kWave = 64;
 constexpr int kMaxE = 64;
 
-// Router / dispatch token blocking: one router block handles 32 tokens, and
-// the per-block expert histograms that the stable counting sort scans use
-// the same blocking.
-constexpr int kRouterTB = 32;
+// Router / dispatch token blocking: one selection block handles kRouterTB
+// tokens, and the per-block expert histograms that the stable counting sort
+// scans use the same blocking.
+#ifndef HI3_ROUTER_TB
+#define HI3_ROUTER_TB 32
+#endif
+constexpr int kRouterTB = HI3_ROUTER_TB;
+static_assert(kRouterTB >= 1 && kRouterTB <= 64, "token block: one wave's lanes");
 // The bf16 router: tokens per block of its logit kernel, and at most this
 // many slices of the hidden dimension.
 constexpr int kRouterMT = 128;
