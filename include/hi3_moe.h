@@ -322,7 +322,13 @@ int hi3_moe_backward(const void *x, const float *w_router, const void *w_up_gate
 /*
  * hi3_moe_backward with per-stage timing: HI3_NUM_BWD_STAGES + 1 events,
  * recorded as in hi3_moe_forward_instrumented (names:
- * hi3_moe_backward_stage_name). stage_events must not be NULL.
+ * hi3_moe_backward_stage_name: routes, dispatch, slot gathers, the GEMM
+ * through the down projection, the recomputed [up; gate] projection with
+ * the SwiGLU backward in its epilogue, the GEMM through [up; gate], the
+ * logit gradient and dx, the router weight gradient, the two expert weight
+ * gradients). For fp32 layers the recompute runs first and is timed with the
+ * gathers (its u and g feed the down-projection GEMM's epilogue), and after
+ * hi3_moe_forward_train there is no recompute. stage_events must not be NULL.
  */
 int hi3_moe_backward_instrumented(const void *x, const float *w_router,
                                   const void *w_up_gate, const void *w_down,

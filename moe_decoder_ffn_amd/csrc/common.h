@@ -347,9 +347,11 @@ struct Plan {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Partial sums of dh * h per routed row written by the mode-2 GEMM.
+// Partial sums of dh * h per routed row (bf16: one per 128 columns, written
+// by the mode-2 GEMM or by the recompute's SwiGLU backward epilogue).
 inline int apart_cols(int I, int dtype) {
-  return dtype == kBF16 ? (I + kGemmBN - 1) / kGemmBN : (I + kGemmF32BN - 1) / kGemmF32BN;
+  return dtype == kBF16 ? (I + kGemmBN / 2 - 1) / (kGemmBN / 2)
+                        : (I + kGemmF32BN - 1) / kGemmF32BN;
 }
 
 
@@ -485,10 +487,18 @@ struct GemmClass {
   int64_t strideC;      // mode 4: elements between consecutive experts' C
   float *ug;            // mode 0: when set, u and g are also stored here (fp32,
                         // [rows, N] with u in the first N/2 columns); mode 2: read
+                        // (when null, mode 2 stores dh itself, fp32, to C)
   const void *hsave;    // mode 2: SwiGLU activations [rows, N] (layer dtype)
-  float *apart;         // mode 2 (nullable): per-row partial sums of dh * h
+  float *apart;         // modes 2, 0 with dh_in (nullable): per-row partial sums of
+                        // dh * h, one per 128 columns
   int apart_ld;         // partial sums per row
   const float *rowscale;  // mode 2 (nullable): dh = rowscale[row] * (B^T A row)
+  // mode 0, bf16 (the backward's recompute after mode 2 ran without ug): when
+  // set, the epilogue also runs the SwiGLU backward from the accumulators' u
+  // and g: dh_in [rows, N/2] fp32 in, [du; dg] [rows, N] (layer dtype, du
+  // first) to dd_out, and the partial sums of dh * h per 128 columns to apart
+  const float *dh_in;
+  void *dd_out;
 };
 
 struct GemmArgs {

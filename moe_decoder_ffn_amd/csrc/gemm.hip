@@ -697,11 +697,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         *reinterpret_cast<u32x2_t *>(C + (static_cast<int64_t>(j.row0) + rl) * ldc + hcol) =
             *reinterpret_cast<const u32x2_t *>(sh + rl * HLD + 4 * (lane & 31));
     }
-    if (ug) {
+    const float *dhp = cl.dh_in;
+    if (ug || dhp) {
       float *su = reinterpret_cast<float *>(sA0);
       float *sgt = su + UGR * ULD;
+      // with dh_in: this lane's rows of a chunk (2 per wave step) and their dh,
+      // loaded before the chunk is staged so that the loads overlap it
+      constexpr int DPR = (UGR + 2 * NW - 1) / (2 * NW);
+      f32x4_t dhv[DPR];
 #pragma unroll 1
       for (int ch = 0; ch < BM / UGR && ch * UGR < j.rows; ++ch) {
+        if (dhp) {
+          const int nr = min(UGR, j.rows - ch * UGR);
+#pragma unroll
+          for (int i = 0; i < DPR; ++i) {
+            const int rl = 2 * wave + (lane >> 5) + 2 * NW * i;
+            dhv[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if (hok && rl < nr)
+              dhv[i] = *reinterpret_cast<const f32x4_t *>(
+                  dhp + (static_cast<int64_t>(j.row0) + ch * UGR + rl) * Ih + hcol);
+          }
+        }
         __syncthreads();
         static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
           constexpr int mi = decltype(Mv)::value;
@@ -722,6 +738,49 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
         });
         __syncthreads();
         const int nr = min(UGR, j.rows - ch * UGR);
+        if (dhp) {
+          // the SwiGLU backward (as mode 2's epilogue computes it from stored
+          // u, g, h; the same operations in the same order): h as stored
+          // above, du = dh SiLU(g), dg = dh u SiLU'(g), and the sum of dh h
+          // over the tile's 128 columns of each row (lanes 0-31 one row,
+          // 32-63 the next)
+          uint16_t *D = static_cast<uint16_t *>(cl.dd_out);
+#pragma unroll
+          for (int i = 0; i < DPR; ++i) {
+            const int rl = 2 * wave + (lane >> 5) + 2 * NW * i;
+            if (rl >= nr) break;  // uniform in each half-wave (one row)
+            const int64_t grow = static_cast<int64_t>(j.row0) + ch * UGR + rl;
+            const f32x4_t u4 = *reinterpret_cast<const f32x4_t *>(su + rl * ULD + 4 * (lane & 31));
+            const f32x4_t g4 = *reinterpret_cast<const f32x4_t *>(sgt + rl * ULD + 4 * (lane & 31));
+            const f32x4_t dh4 = dhv[i];
+            float du[4], dg[4], asum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float u = u4[e], gt = g4[e], dh = dh4[e];
+              const float hv = gt * u * __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+              const float hq = __uint_as_float(static_cast<uint32_t>(f32_to_bf16(hv)) << 16);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+              du[e] = dh * (gt * sg);
+              dg[e] = dh * u * (sg * (1.0f + gt * (1.0f - sg)));
+              asum += dh * hq;
+            }
+            if (hok) {
+              u32x2_t o;
+              o[0] = pack_bf16x2(du[0], du[1]);
+              o[1] = pack_bf16x2(du[2], du[3]);
+              *reinterpret_cast<u32x2_t *>(D + grow * N + hcol) = o;
+              o[0] = pack_bf16x2(dg[0], dg[1]);
+              o[1] = pack_bf16x2(dg[2], dg[3]);
+              *reinterpret_cast<u32x2_t *>(D + grow * N + Ih + hcol) = o;
+            } else {
+              asum = 0.0f;
+            }
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) asum += __shfl_xor(asum, o, kWave);
+            if (cl.apart && (lane & 31) == 0) cl.apart[grow * cl.apart_ld + j.nt] = asum;
+          }
+          continue;
+        }
 #pragma unroll 2
         for (int rl = 2 * wave + (lane >> 5); rl < nr; rl += 2 * NW) {
           if (!hok) continue;
@@ -778,7 +837,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     // them. du = dh SiLU(g), dg = dh u SiLU'(g) with
     // SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g)); [du; dg] is
     // stored in the layer dtype (row stride 2N, du first); the sum of dh h
-    // over the tile's columns of each row goes to apart[row, column tile].
+    // over each 128 columns of each row goes to apart[row, 128-column block].
+    // Without u and g (ug null: the recompute that follows runs the SwiGLU
+    // backward in its own epilogue) this epilogue stores dh itself (fp32, C).
     // The accumulators hold one row per lane, which would make every global
     // access of this epilogue touch 64 rows; so the tile of acc is staged in
     // the (now idle) LDS ring and each wave then walks whole rows: lane l
@@ -818,6 +879,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
       });
       __syncthreads();
       const int nr = min(CH, j.rows - ch * CH);
+      if (!ugp) {
+        // dh alone (the recompute's epilogue runs the SwiGLU backward), fp32
+        float *Cf = static_cast<float *>(Cv);
+#pragma unroll 2
+        for (int rl = wave; rl < nr; rl += NW) {
+          const int64_t grow = static_cast<int64_t>(j.row0) + ch * CH + rl;
+          const float rs = cl.rowscale ? cl.rowscale[grow] : 1.0f;
+          const f32x4_t a4 = *reinterpret_cast<const f32x4_t *>(stg + rl * SLD + 4 * lane);
+          if (cok)
+            *reinterpret_cast<f32x4_t *>(Cf + grow * ldc + col) =
+                f32x4_t{rs * a4[0], rs * a4[1], rs * a4[2], rs * a4[3]};
+        }
+        continue;
+      }
 #pragma unroll 1
       for (int r0 = wave; r0 < nr; r0 += NW * UR) {
         f32x4_t u4[UR], g4[UR];
@@ -867,9 +942,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
           } else {
             asum = 0.0f;
           }
+          // one partial per 128 columns: lanes 0-31 and 32-63 cover the two
+          // halves of the tile's 256 columns
 #pragma unroll
-          for (int o = 32; o > 0; o >>= 1) asum += __shfl_xor(asum, o, kWave);
-          if (cl.apart && lane == 0) cl.apart[grow * cl.apart_ld + j.nt] = asum;
+          for (int o = 16; o > 0; o >>= 1) asum += __shfl_xor(asum, o, kWave);
+          const int pi = 2 * j.nt + (lane >> 5);
+          if (cl.apart && (lane & 31) == 0 && pi < cl.apart_ld)
+            cl.apart[grow * cl.apart_ld + pi] = asum;
         }
       }
     }

@@ -328,44 +328,79 @@ int backward_impl(const void *x, const float *w_router, const void *w_up_gate,
     ScatterArgs sc{idx, pad_mask, T, E, K, perm, slotof, vtok, vidx};
     HI3_TRY(launch_dispatch(sa, &sc, s));
   }
-  rec.at(2);
-  if (!reuse) {
+  // The [up; gate] projection again (h as the forward stores it). bf16
+  // layers run it after dh, with the SwiGLU backward in its epilogue (u and g
+  // never leave the registers; dh is kept in the u, g buffer); fp32 layers
+  // store u and g (fp32) for the dh GEMM's epilogue, as the training forward
+  // does for hi3_moe_backward_after_forward.
+  const bool fused_swiglu_bwd = !reuse && dtype == HI3_BF16 && kGemmStagedStore;
+  float *apart = static_cast<float *>(at(p.apart));
+  auto recompute = [&](bool with_bwd) -> int {
     GemmArgs up{};
     up.cls[0] = GemmClass{x, H, perm, w_up_gate, int64_t{2} * I * H, at(p.h), I, 2 * I, H};
     up.cls[1] = GemmClass{x, H, vtok, w_shared_up_gate, 0, at(p.hs), Is, 2 * Is, H};
-    up.cls[0].ug = static_cast<float *>(at(p.ug));
-    up.cls[1].ug = static_cast<float *>(at(p.ugs));
+    if (with_bwd) {
+      up.cls[0].dh_in = static_cast<const float *>(at(p.ug));
+      up.cls[0].dd_out = at(p.dd);
+      up.cls[0].apart = apart;
+      up.cls[0].apart_ld = p.P;
+      up.cls[1].dh_in = static_cast<const float *>(at(p.ugs));
+      up.cls[1].dd_out = at(p.dds);
+    } else {
+      up.cls[0].ug = static_cast<float *>(at(p.ug));
+      up.cls[1].ug = static_cast<float *>(at(p.ugs));
+    }
     up.tiles = tiles;
     up.gto = gto;
     up.E = E;
     HI3_TRY(launch_gemm_upgate(up, p.max_tiles, p.BM, dtype, s));
+    return HI3_OK;
+  };
+  // 2: x and w dout by slot; x and dout by real row when there is padding
+  // (fp32 layers: after the recompute, which this stage then includes)
+  rec.at(2);
+  if (!reuse && !fused_swiglu_bwd) {
+    st = recompute(false);
+    if (st != HI3_OK) return st;
   }
-  // 4: x and w dout by slot; x and dout by real row when there is padding
-  rec.at(3);
   const bool compact = pad_mask != nullptr;
   BwdGatherArgs ga{x, dout, wts, slotof, vidx, pad_mask, T, H, K, at(p.xs), at(p.dys),
                    static_cast<float *>(at(p.wslot)), compact ? at(p.xv) : nullptr,
                    compact ? at(p.doutv) : nullptr};
   HI3_TRY(launch_bwd_gather(ga, dtype, s));
-  // 5: dh = w W2^T dout (dout rows gathered through the slot -> token map, w
-  // applied in fp32) and the SwiGLU backward: [du; dg], partial sums of dh h
-  rec.at(4);
+  // 3: dh = w W2^T dout (dout rows gathered through the slot -> token map, w
+  // applied in fp32); with u and g stored, the SwiGLU backward in the same
+  // epilogue: [du; dg], partial sums of dh h; else dh alone (fp32)
+  rec.at(3);
   GemmArgs d2{};
   d2.cls[0] = GemmClass{dout, H, perm, w_down, int64_t{H} * I, at(p.dd), 2 * I, I, H};
   d2.cls[0].rowscale = static_cast<const float *>(at(p.wslot));
   d2.cls[0].ldb = I;
-  d2.cls[0].ug = static_cast<float *>(at(p.ug));
-  d2.cls[0].hsave = at(p.h);
-  d2.cls[0].apart = static_cast<float *>(at(p.apart));
-  d2.cls[0].apart_ld = p.P;
   d2.cls[1] = GemmClass{dout, H, vtok, w_shared_down, 0, at(p.dds), 2 * Is, Is, H};
   d2.cls[1].ldb = Is;
-  d2.cls[1].ug = static_cast<float *>(at(p.ugs));
-  d2.cls[1].hsave = at(p.hs);
+  if (fused_swiglu_bwd) {
+    d2.cls[0].C = at(p.ug);  // dh [T*K, I] fp32
+    d2.cls[0].ldc = I;
+    d2.cls[1].C = at(p.ugs);  // dh [T, Is] fp32
+    d2.cls[1].ldc = Is;
+  } else {
+    d2.cls[0].ug = static_cast<float *>(at(p.ug));
+    d2.cls[0].hsave = at(p.h);
+    d2.cls[0].apart = apart;
+    d2.cls[0].apart_ld = p.P;
+    d2.cls[1].ug = static_cast<float *>(at(p.ugs));
+    d2.cls[1].hsave = at(p.hs);
+  }
   d2.tiles = tiles;
   d2.gto = gto;
   d2.E = E;
   HI3_TRY(launch_gemm_dgrad_down(d2, p.max_tiles, p.BM, dtype, s));
+  // 4: (bf16) the recompute with the SwiGLU backward
+  rec.at(4);
+  if (fused_swiglu_bwd) {
+    st = recompute(true);
+    if (st != HI3_OK) return st;
+  }
   // 6: dx by slot / by real row = W13^T [du; dg]
   rec.at(5);
   if (dx || want_dxn) {
@@ -697,7 +732,7 @@ int hi3_moe_backward_norm_residual(const void *h, const void *norm_weight, float
 
 const char *hi3_moe_backward_stage_name(int stage) {
   static const char *names[HI3_NUM_BWD_STAGES] = {
-      "router", "dispatch", "gemm_up_gate_recompute", "gather_bwd", "gemm_dgrad_down",
+      "router", "dispatch", "gather_bwd", "gemm_dgrad_down", "gemm_up_gate_recompute",
       "gemm_dgrad_up_gate", "combine_bwd", "dw_router", "gemm_wgrad_down",
       "gemm_wgrad_up_gate"};
   if (stage < 0 || stage >= HI3_NUM_BWD_STAGES) return "?";
