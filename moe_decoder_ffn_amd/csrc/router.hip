@@ -28,14 +28,12 @@ namespace hi3 {
 // Softmax over all experts, top-K and renormalisation for 32 tokens per
 // block: one wave per token at a time, lane = expert; then the block's
 // expert histogram and real-row count.
-// Every lane reads all of the token's logits from the other lanes
-// (readlane, in expert order) to get the maximum and its own rank in the
-// selection order (larger logit first, lower index first on equal logits;
-// softmax is strictly increasing, so this is the order of the
-// probabilities, and fp32 underflow of small probabilities cannot change
-// it). Z sums exp(l - max) in ascending expert order, the selected
-// p = exp(l - max) / Z are summed in selection order, and each is divided by
-// that sum.
+// Every lane ranks its expert in the selection order (larger logit first,
+// lower index first on equal logits; softmax is strictly increasing, so
+// this is the order of the probabilities, and fp32 underflow of small
+// probabilities cannot change it) by comparing selection keys. Z sums
+// exp(l - max) in ascending expert order, the selected p = exp(l - max) / Z
+// are summed in selection order, and each is divided by that sum.
 // The token's logits are the slice partials summed in slice order.
 // partial: [slices][T][E] fp32. EC = 64: E is 64 (no per-expert guards);
 // EC = 0: any E <= 64.
@@ -49,6 +47,7 @@ struct SelectShared {
   int esel[kRouterTB][kMaxE];
   uint64_t selmask[kRouterTB];
   float row[kSelThreads / 64][kMaxE];  // one token's values, broadcast to its wave
+  uint64_t key[kSelThreads / 64][kMaxE];  // one token's selection keys, likewise
 };
 
 __device__ __forceinline__ float nan_as_neg_inf(float v) { return v != v ? -INFINITY : v; }
@@ -120,31 +119,36 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(RouterArgs a
     // A NaN logit counts as -infinity: the order (larger first, lower index
     // on equal values) is then total, the ranks of the E lanes are a
     // permutation, and exactly K experts are selected whatever the inputs.
-    // Every lane reads the row's logits (written to LDS once, read back as
-    // broadcasts) in expert order for the maximum, its own rank in the
-    // selection order and the softmax denominator, summed in ascending
-    // expert order (every lane forms the same sum).
+    // Each lane's selection key orders the lanes in that order as unsigned
+    // 64-bit integers: the logit's bits made monotonic (with -0 read as +0,
+    // an equal value), then 63 - lane (the lower index first on equal
+    // logits); lanes past E get key 0, below every live key. Every lane
+    // reads all keys (written to LDS once, read back as broadcasts) and
+    // counts those above its own: its rank. The maximum is the logit of the
+    // rank-0 lane. The softmax denominator is summed in ascending expert
+    // order from the broadcast values (every lane forms the same sum).
     const bool live = lane < E;
     const float l = live ? nan_as_neg_inf(lsum[j]) : -INFINITY;
-    const f32x4_t *rowv = reinterpret_cast<const f32x4_t *>(sh.row[wave]);
-    sh.row[wave][lane] = l;
+    const uint32_t lb = __float_as_uint(l + 0.0f);
+    const uint32_t mono = (lb & 0x80000000u) ? ~lb : (lb | 0x80000000u);
+    const uint64_t key =
+        live ? (static_cast<uint64_t>(mono) << 6) | static_cast<uint64_t>(63 - lane) : 0ull;
+    typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+    const u64x2_t *keyv = reinterpret_cast<const u64x2_t *>(sh.key[wave]);
+    sh.key[wave][lane] = key;
     wave_lds_sync();
-    float m = -INFINITY;
     int rank = 0;
 #pragma unroll
-    for (int e4 = 0; e4 < kMaxE / 4; ++e4) {
-      const f32x4_t v4 = rowv[e4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = 4 * e4 + u;
-        if (EC == 0 && e >= E) continue;
-        const float ve = v4[u];
-        m = fmaxf(m, ve);
-        rank += (ve > l || (ve == l && e < lane)) ? 1 : 0;
-      }
+    for (int e2 = 0; e2 < kMaxE / 2; ++e2) {
+      const u64x2_t k2 = keyv[e2];
+      rank += k2[0] > key ? 1 : 0;
+      rank += k2[1] > key ? 1 : 0;
     }
+    const uint64_t first = __ballot(live && rank == 0);  // exactly one lane
+    const float m = __int_as_float(
+        __builtin_amdgcn_readlane(__float_as_int(l), static_cast<int>(__builtin_ctzll(first))));
     const float ex = live ? expf(l - m) : 0.0f;
-    wave_lds_sync();  // every lane has read the logits before they are overwritten
+    const f32x4_t *rowv = reinterpret_cast<const f32x4_t *>(sh.row[wave]);
     sh.row[wave][lane] = ex;
     wave_lds_sync();
     float z = 0.0f;
