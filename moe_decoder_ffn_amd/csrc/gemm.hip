@@ -23,10 +23,10 @@
 // and their fragments are read with the transposing LDS read of gfx950, so no
 // transposed copy is ever written to HBM.
 //
-// Work list: the row tiles of all groups (written on the device by the scan
-// kernel, expert-major, the shared expert last) times the column tiles; the
-// gradient through the down projection (mode 2) runs each listed row tile as
-// `split` blocks of sub_rows rows. The grid is sized for the largest
+// Work list: the row tiles of all groups (written on the device by the
+// dispatch kernel, expert-major, the shared expert last) times the column
+// tiles; the gradient through the down projection (mode 2) runs each listed
+// row tile as `split` blocks of sub_rows rows. The grid is sized for the largest
 // possible tile count; surplus blocks exit. Block b runs on XCD b % 8 (the
 // hardware's round-robin); how jobs map to blocks is resolve_job's. When no
 // row is padding, the forward runs the shared expert alone instead, as dense

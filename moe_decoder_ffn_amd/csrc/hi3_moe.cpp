@@ -145,7 +145,7 @@ int forward_impl(const void *x, const void *norm_weight, float eps, const float 
   }
   // fork: the side stream starts after everything enqueued on s so far and
   // runs the shared expert's rows, the tokens 0 .. T-1 in order (measured:
-  // forking here beats forking after the router or the scatter, though the
+  // forking here beats forking after the router or the dispatch, though the
   // shared GEMM's blocks then delay the routing's). With the RMSNorm fused
   // into the router, the rows exist only after it: the fork follows it.
   auto fork_shared = [&]() -> int {
