@@ -160,7 +160,12 @@ constexpr int kDgradUpStages = HI3_DGRAD_UP_STAGES;
 #endif
 constexpr int kWgradBM = HI3_WGRAD_BM;
 constexpr int kWgradGroupRows = HI3_WGRAD_GROUP_ROWS;
-constexpr int kWgradWN = kWgradBM == 256 ? kGemmWN : 2;
+// waves along the output columns (2 along the rows): 128-row tiles run 4 or
+// 8 waves
+#ifndef HI3_WGRAD_WN
+#define HI3_WGRAD_WN 4
+#endif
+constexpr int kWgradWN = kWgradBM == 256 ? kGemmWN : HI3_WGRAD_WN;
 constexpr int kWgradBK = HI3_WGRAD_BK;
 constexpr int kWgradStages = HI3_WGRAD_STAGES;
 static_assert(kGemmBM % kDgradDownSplit == 0 && (kGemmBM / kDgradDownSplit) % 64 == 0,
