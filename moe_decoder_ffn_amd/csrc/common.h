@@ -111,10 +111,10 @@ constexpr int kGemmWN = HI3_GEMM_WN;  // waves along the columns (2 along the ro
 // [up; gate] (mode 3) and the weight gradients (mode 4) use the given k step
 // and stage counts.
 #ifndef HI3_DGRAD_DOWN_SPLIT
-#define HI3_DGRAD_DOWN_SPLIT 2
+#define HI3_DGRAD_DOWN_SPLIT 1
 #endif
 #ifndef HI3_DGRAD_DOWN_STAGES
-#define HI3_DGRAD_DOWN_STAGES 3
+#define HI3_DGRAD_DOWN_STAGES 2
 #endif
 #ifndef HI3_DGRAD_UP_BK
 #define HI3_DGRAD_UP_BK 64
@@ -139,6 +139,20 @@ constexpr bool kOverlapShared = HI3_OVERLAP_SHARED != 0;
 constexpr int kGemmColChunk = HI3_GEMM_COL_CHUNK;
 constexpr bool kGemmQuarterBody = HI3_GEMM_QUARTER_BODY != 0;
 constexpr int kDgradDownSplit = HI3_DGRAD_DOWN_SPLIT;
+// k step of the dh GEMM and the blocks per CU its registers allow
+#ifndef HI3_DGRAD_DOWN_BK
+#define HI3_DGRAD_DOWN_BK 64
+#endif
+#ifndef HI3_DGRAD_DOWN_OCC
+#define HI3_DGRAD_DOWN_OCC 1
+#endif
+constexpr int kDgradDownBK = HI3_DGRAD_DOWN_BK;
+// the third weight stage for the dh GEMM too (on 256-row tiles, 2 stages)
+#ifndef HI3_DGRAD_DOWN_DEEP_B
+#define HI3_DGRAD_DOWN_DEEP_B 0
+#endif
+constexpr bool kDgradDownDeepB = HI3_DGRAD_DOWN_DEEP_B != 0;
+constexpr int kDgradDownOcc = HI3_DGRAD_DOWN_OCC;
 constexpr int kDgradDownStages = HI3_DGRAD_DOWN_STAGES;
 // Rows per wave in flight in the mode-2 epilogue (its u, g, h reads).
 #ifndef HI3_DGRAD_EPI_ROWS

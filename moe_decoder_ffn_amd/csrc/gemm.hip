@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(128 * WN, OCC * 2 * WN / 4) void gemm_bf16_kernel(G
   // the 8-wave blocks whose B is a weight (modes 0, 1, 3) take a third B
   // stage where it fits
   constexpr bool DB = kGemmDeepB && WN == 4 && NST == 2 && BK == 64 &&
-                      (MODE == 0 || MODE == 1 || MODE == 3) &&
+                      (MODE == 0 || MODE == 1 || MODE == 3 || (MODE == 2 && kDgradDownDeepB)) &&
                       (NST * (BM + BN) + BN) * BK * 2 <= 160 * 1024;
   // one array: stage s holds A at (AE + BE) s and B right after it (with DB
   // the third B stage follows); the whole ring is reused by the epilogues
@@ -1359,7 +1359,10 @@ static hipError_t launch_gemm(GemmArgs a, int max_tiles, int tile_rows, int dtyp
         break;
       case 2:
         if (stream) HI3_LAUNCH(2, kGemmStreamBM, 64, kGemmStreamStages);
-        else HI3_LAUNCH(2, kGemmBM / kDgradDownSplit, 64, kDgradDownStages);
+        else
+          hipLaunchKernelGGL((gemm_bf16_kernel<2, kGemmBM / kDgradDownSplit, kDgradDownBK,
+                                               kDgradDownStages, kGemmWN, kDgradDownOcc>),
+                             dim3(grid), block, 0, s, a);
         break;
       default:
         if (stream) HI3_LAUNCH(3, kGemmStreamBM, 64, kGemmStreamStages);
