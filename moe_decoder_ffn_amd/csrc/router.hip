@@ -303,14 +303,14 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
   const int64_t xstep = int64_t{32} * H / 8;
   // The loads are not predicated (a divergent branch around each would make
   // the compiler drain every load in flight before the first use of any):
-  // a padding row or a row past T reads row 0 and an expert past E reads
+  // a padding row or a row past T reads the router weight's first row
+  // instead (x's padding rows are never read), an expert past E reads
   // expert 0, and the staging zeroes them.
-  const u32x4_t *xsrc = reinterpret_cast<const u32x4_t *>(a.x) + xp;
   const f32x4_t *wsrc = reinterpret_cast<const f32x4_t *>(a.w) + wp;
   u32x4_t *xdst = NORM ? reinterpret_cast<u32x4_t *>(a.xn + (T0 + r0) * H) + xp : nullptr;
   uint32_t xok = 0, wok = 0;  // bit u: row / expert u is real
-  int64_t xoff[4];            // 16-byte units
-  int32_t woff[4];
+  const u32x4_t *xsrc[4];
+  int32_t woff[4];            // 16-byte units
   float rr[NORM ? 4 : 1];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -319,7 +319,8 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
     const bool eok = e0 + 16 * u < a.E;
     xok |= ok ? 1u << u : 0u;
     wok |= eok ? 1u << u : 0u;
-    xoff[u] = ok ? t * (H / 8) : 0;
+    xsrc[u] = (ok ? reinterpret_cast<const u32x4_t *>(a.x + t * H)
+                  : reinterpret_cast<const u32x4_t *>(a.w)) + xp;
     woff[u] = eok ? (e0 + 16 * u) * (H / 4) : 0;
     if constexpr (NORM) rr[u] = ok ? a.rrow[t] : 1.0f;
   }
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
     constexpr int b = decltype(S)::value;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      xs[b][u] = xsrc[xoff[u] + 8 * c];
+      xs[b][u] = xsrc[u][8 * c];
       ws[b][u] = wsrc[woff[u] + 16 * c];
     }
     if constexpr (NORM) nws[b] = nwsrc[8 * c];
