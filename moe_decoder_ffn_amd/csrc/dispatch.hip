@@ -30,8 +30,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 
 // Counting sort of the routed (token, k) pairs, one block per 32 tokens (the
 // histogram blocking), no atomics. Every block reads all per-block expert
-// histograms [NB][E] and real-row counts [NB] (coalesced, eight loads in
-// flight per thread): the column totals give the experts' offsets, the
+// histograms [NB][E] and real-row counts [NB] (coalesced, 16 waves with up
+// to 16 loads in flight per thread): the column totals give the experts' offsets, the
 // rows before its own give its first slot per expert and its first real-row
 // index. Block 0 also writes the global results: expert offsets, counts,
 // the real-row count and the grouped GEMMs' row-tile list (experts
@@ -39,11 +39,14 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // block places its own pairs: the rank of token t among the block's tokens
 // routed to expert e (tokens ascending) completes the slot. With
 // do_scatter = 0 (counts only) the grid is block 0 alone.
-__global__ __launch_bounds__(256) void dispatch_kernel(ScanArgs a, ScatterArgs c,
-                                                       int do_scatter) {
-  __shared__ int part_all[4][kMaxE];
-  __shared__ int part_pre[4][kMaxE];
-  __shared__ int vred[2][4];
+constexpr int kDispThreads = 1024;
+constexpr int kDispGroups = kDispThreads / 64;  // waves, each summing every 16th histogram row
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(ScanArgs a, ScatterArgs c,
+                                                                int do_scatter) {
+  __shared__ int part_all[kDispGroups][kMaxE];
+  __shared__ int part_pre[kDispGroups][kMaxE];
+  __shared__ int vred[2][kDispGroups];
   __shared__ int eoff[kMaxE + 1];
   __shared__ int first[kMaxE];
   __shared__ int toff[kMaxE + 2];
@@ -71,37 +74,38 @@ __global__ __launch_bounds__(256) void dispatch_kernel(ScanArgs a, ScatterArgs c
     }
   }
 
-  // column sums of the histograms: thread (grp, lane) takes rows
-  // grp, grp + 4, ...; all rows, and the rows before this block
+  // column sums of the histograms: thread (grp, lane) takes rows grp,
+  // grp + 16, ... (all loads of up to 16 rows in flight at once); all rows,
+  // and the rows before this block
   int s_all = 0, s_pre = 0;
-  for (int b0 = grp; b0 < NB; b0 += 4 * 8) {
-    int v[8];
+  for (int b0 = grp; b0 < NB; b0 += kDispGroups * 16) {
+    int v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int b = b0 + 4 * u;
+    for (int u = 0; u < 16; ++u) {
+      const int b = b0 + kDispGroups * u;
       v[u] = lane < E && b < NB ? a.blkcnt[static_cast<int64_t>(b) * E + lane] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       s_all += v[u];
-      if (b0 + 4 * u < me) s_pre += v[u];
+      if (b0 + kDispGroups * u < me) s_pre += v[u];
     }
   }
   part_all[grp][lane] = s_all;
   part_pre[grp][lane] = s_pre;
   // real rows per block: all blocks, and the blocks before this one
   int va = 0, vp = 0;
-  for (int b0 = tid; b0 < NB; b0 += 256 * 4) {
+  for (int b0 = tid; b0 < NB; b0 += kDispThreads * 4) {
     int v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int b = b0 + 256 * u;
+      const int b = b0 + kDispThreads * u;
       v[u] = b < NB ? a.blkval[b] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       va += v[u];
-      if (b0 + 256 * u < me) vp += v[u];
+      if (b0 + kDispThreads * u < me) vp += v[u];
     }
   }
   va = wave_inclusive_sum(va);
@@ -113,18 +117,25 @@ __global__ __launch_bounds__(256) void dispatch_kernel(ScanArgs a, ScatterArgs c
   __syncthreads();
   if (grp == 0) {
     // expert totals and offsets (an exclusive scan over the experts)
-    const int tot = lane < E ? ((part_all[0][lane] + part_all[1][lane]) + part_all[2][lane]) +
-                                   part_all[3][lane]
-                             : 0;
-    const int pre = ((part_pre[0][lane] + part_pre[1][lane]) + part_pre[2][lane]) +
-                    part_pre[3][lane];
+    int tot = 0, pre = 0;
+#pragma unroll
+    for (int q = 0; q < kDispGroups; ++q) {
+      tot += part_all[q][lane];
+      pre += part_pre[q][lane];
+    }
+    if (lane >= E) tot = 0;
     const int inc = wave_inclusive_sum(tot);
     eoff[lane] = inc - tot;
     if (lane == 63) eoff[64] = inc;
     first[lane] = inc - tot + pre;
     if (lane == 0) {
-      nvalid_s = ((vred[0][0] + vred[0][1]) + vred[0][2]) + vred[0][3];
-      vbase_s = ((vred[1][0] + vred[1][1]) + vred[1][2]) + vred[1][3];
+      int nv = 0, vb = 0;
+      for (int q = 0; q < kDispGroups; ++q) {
+        nv += vred[0][q];
+        vb += vred[1][q];
+      }
+      nvalid_s = nv;
+      vbase_s = vb;
     }
     if (me == 0) {
       // row tiles per expert, then their offsets
@@ -208,10 +219,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(ScanArgs a, ScatterArgs c
 
 hipError_t launch_dispatch(const ScanArgs &a, const ScatterArgs *c, hipStream_t s) {
   if (c) {
-    hipLaunchKernelGGL(dispatch_kernel, dim3(static_cast<unsigned>(a.NB)), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(dispatch_kernel, dim3(static_cast<unsigned>(a.NB)), dim3(kDispThreads), 0,
+                       s, a,
                        *c, 1);
   } else {
-    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(256), 0, s, a, ScatterArgs{}, 0);
+    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, a, ScatterArgs{}, 0);
   }
   return hipGetLastError();
 }
