@@ -4,9 +4,9 @@
 // "Train", and 'mlp.gate' in _keep_in_fp32_modules_strict).
 //
 // bf16 activations: each fp32 router weight is split, as the logit kernel
-// stages it in LDS, into three bf16 terms hi + mid + lo that sum to it exactly (Henry, Tang &
-// Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype for
-// Higher-Precision Computations", ARITH 2019). Each product x * term is exact
+// stages it in LDS, into three bf16 terms hi + mid + lo that sum to it
+// exactly (Henry, Tang & Heinecke, "Leveraging the bfloat16 Artificial
+// Intelligence Datatype for Higher-Precision Computations", ARITH 2019). Each product x * term is exact
 // in fp32, so bf16 MFMA with fp32 accumulation gives the fp32 router at
 // matrix-core rate instead of the vector-FMA rate. When the layer runs inside
 // its decoder block, the block's RMSNorm (layers API page, HunyuanRMSNorm;
