@@ -225,8 +225,8 @@ __device__ __forceinline__ void split3x2(float v0, float v1, uint32_t &hi, uint3
 // Each chunk is staged in LDS by all 256 threads with coalesced 16-byte
 // loads: the 128 token rows (normalised on the way with NORM), and the 64
 // expert rows of the fp32 weight, split on the way into their three bf16
-// terms. The loads run two chunks ahead of the multiplication (two register
-// sets, two LDS buffers, one barrier per chunk). With NORM the rows
+// terms. The loads run kRouterLoadSets chunks ahead of the multiplication
+// (that many register sets, two LDS buffers, one barrier per chunk). With NORM the rows
 // are normalised with their r (computed by row_rms_kernel):
 // n = bf16(x r), xn = bf16(w n); the staging threads also write xn (the
 // expert GEMMs' input): every element of every real row is written once.
@@ -243,8 +243,8 @@ __device__ __forceinline__ void split3x2(float v0, float v1, uint32_t &hi, uint3
 // runs over at most half of the slice's products; with two blocks per CU
 // in a round, a slice holds at most 64 / (round / token blocks) chunks). Result
 // element v of lane l is token 8 (v / 4) + 4 (l / 32) + v % 4 and expert
-// l % 32 of the tile. Padding rows are not read (their partial logits are
-// 0, never used) and get no normalised row.
+// l % 32 of the tile. x's padding rows are not read (their partial logits
+// are never used) and get no normalised row.
 struct RouterSliceArgs {
   const uint16_t *x;
   const float *w;          // [E, H] fp32 router weight
@@ -274,6 +274,26 @@ __device__ __forceinline__ void lds_barrier() {
 // staged chunk (128 bytes per row): piece c is stored at c ^ ((row / 2) % 8),
 // so the 16 rows of one fragment read fall in 16 distinct bank groups.
 __device__ __forceinline__ int rl_pos(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+
+// f(integral_constant<S>, i + S) for S = 0 .. N - 1
+template <int N, int S = 0, typename F>
+__device__ __forceinline__ void unroll_steps(F &&f, int i) {
+  if constexpr (S < N) {
+    f(std::integral_constant<int, S>{}, i + S);
+    unroll_steps<N, S + 1>(f, i);
+  }
+}
+
+// The same for the steps i + S < n, each guard inside the previous one.
+template <int N, int S = 0, typename F>
+__device__ __forceinline__ void tail_steps(F &&f, int i, int n) {
+  if constexpr (S < N) {
+    if (i + S < n) {
+      f(std::integral_constant<int, S>{}, i + S);
+      tail_steps<N, S + 1>(f, i, n);
+    }
+  }
+}
 
 struct RouterStage {
   u32x4_t x[kRouterMT * 8];  // the chunk of the block's token rows
@@ -305,32 +325,45 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
   // the compiler drain every load in flight before the first use of any):
   // a padding row or a row past T reads the router weight's first row
   // instead (x's padding rows are never read), an expert past E reads
-  // expert 0, and the staging zeroes them.
+  // expert 0. Their values are staged as they are: an output element
+  // depends on its own row and expert only, and the partial logits of
+  // those rows and experts are never stored or used.
   const f32x4_t *wsrc = reinterpret_cast<const f32x4_t *>(a.w) + wp;
   u32x4_t *xdst = NORM ? reinterpret_cast<u32x4_t *>(a.xn + (T0 + r0) * H) + xp : nullptr;
-  uint32_t xok = 0, wok = 0;  // bit u: row / expert u is real
+  uint32_t xok = 0;           // bit u: row u is real
   const u32x4_t *xsrc[4];
   int32_t woff[4];            // 16-byte units
   float rr[NORM ? 4 : 1];
+  // (the padding flags and the rows' r are read for a clamped row, all
+  // loads before the first use)
+  uint8_t pv[4] = {0, 0, 0, 0};
+  if (a.pad) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pv[u] = a.pad[min(T0 + r0 + 32 * u, a.T - 1)];
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rr[u] = a.rrow[min(T0 + r0 + 32 * u, a.T - 1)];
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t t = T0 + r0 + 32 * u;
-    const bool ok = t < a.T && !(a.pad && a.pad[t]);
+    const bool ok = t < a.T && !pv[u];
     const bool eok = e0 + 16 * u < a.E;
     xok |= ok ? 1u << u : 0u;
-    wok |= eok ? 1u << u : 0u;
     xsrc[u] = (ok ? reinterpret_cast<const u32x4_t *>(a.x + t * H)
                   : reinterpret_cast<const u32x4_t *>(a.w)) + xp;
     woff[u] = eok ? (e0 + 16 * u) * (H / 4) : 0;
-    if constexpr (NORM) rr[u] = ok ? a.rrow[t] : 1.0f;
   }
   const u32x4_t *nwsrc = NORM ? reinterpret_cast<const u32x4_t *>(a.norm_w) + xp : nullptr;
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-  // two register sets of staged pieces: the chunk being loaded and the one
-  // loaded a step earlier (stored to LDS this step)
-  u32x4_t xs[2][4];
-  f32x4_t ws[2][4];
-  u32x4_t nws[2] = {zero4, zero4};
+  // NS register sets of staged pieces: chunk c_lo + i goes to set i % NS
+  constexpr int NS = kRouterLoadSets;
+  u32x4_t xs[NS][4];
+  f32x4_t ws[NS][4];
+  u32x4_t nws[NS];
+#pragma unroll
+  for (int b = 0; b < NS; ++b) nws[b] = zero4;
   auto load = [&](auto S, int c) __attribute__((always_inline)) {
     constexpr int b = decltype(S)::value;
 #pragma unroll
@@ -340,24 +373,23 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
     }
     if constexpr (NORM) nws[b] = nwsrc[8 * c];
   };
-  auto store = [&](auto S, RouterStage &sg, int c) __attribute__((always_inline)) {
+  // (wr: also write the normalised rows; false when the chunk is a repeat)
+  auto store = [&](auto S, RouterStage &sg, int c, bool wr) __attribute__((always_inline)) {
     constexpr int b = decltype(S)::value;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int row = r0 + 32 * u;
-      const bool ok = (xok >> u) & 1u;
-      u32x4_t v = ok ? xs[b][u] : zero4;
+      u32x4_t v = xs[b][u];
       if constexpr (NORM) {
         v = norm_chunk<kBF16>(v, nws[b], rr[u]);
-        if (ok) xdst[u * xstep + 8 * c] = v;
+        if (((xok >> u) & 1u) && wr) xdst[u * xstep + 8 * c] = v;
       }
       sg.x[rl_pos(row, xp)] = v;
       // the weight's three terms: 4 bf16 each, the half of a 16-byte piece
       const int e = e0 + 16 * u;
-      const bool eok = (wok >> u) & 1u;
       uint32_t h0, m0, l0, h1, m1, l1;
-      split3x2(eok ? ws[b][u][0] : 0.0f, eok ? ws[b][u][1] : 0.0f, h0, m0, l0);
-      split3x2(eok ? ws[b][u][2] : 0.0f, eok ? ws[b][u][3] : 0.0f, h1, m1, l1);
+      split3x2(ws[b][u][0], ws[b][u][1], h0, m0, l0);
+      split3x2(ws[b][u][2], ws[b][u][3], h1, m1, l1);
       const int pos = rl_pos(e, wp >> 1);
       const int half = wp & 1;
       reinterpret_cast<u32x2_t *>(&sg.w[0][pos])[half] = u32x2_t{h0, h1};
@@ -389,34 +421,40 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
       }
     }
   };
-  // chunk c_lo + i is loaded into register set i % 2 and staged in LDS
-  // buffer i % 2; step i loads chunk i + 2, multiplies chunk i and stores
-  // chunk i + 1 (loaded a step earlier)
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  if (c_lo < c_hi) {
-    load(I0{}, c_lo);
-    if (c_lo + 1 < c_hi) load(I1{}, c_lo + 1);
-    store(I0{}, st[0], c_lo);
-  }
-  __syncthreads();
-  for (int c = c_lo; c < c_hi; c += 2) {
-    auto step = [&](auto U) __attribute__((always_inline)) {
-      constexpr int u = decltype(U)::value;
-      const int cu = c + u;
-      if (cu < c_hi) {
-        // (the scheduling barriers keep the loads ahead of the multiplication
-        // and of the staging, whose waits then leave them in flight)
-        if (cu + 2 < c_hi) load(U, cu + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st[u], U);
-        __builtin_amdgcn_sched_barrier(0);
-        if (cu + 1 < c_hi) store(std::integral_constant<int, 1 - u>{}, st[1 - u], cu + 1);
-        lds_barrier();
-      }
-    };
-    step(I0{});
-    step(I1{});
+  // Chunk c_lo + i is loaded into register set i % NS, staged in LDS
+  // buffer i % 2 and multiplied into accumulator i % 2. Step i loads chunk
+  // i + NS into the set staged in step i - 1, multiplies chunk i and stages
+  // chunk i + 1, so the loads of NS - 1 chunks stay in flight across the
+  // multiplication. Past the slice's last chunk the loads and the staging
+  // repeat it (into a set and a buffer that are not read again) instead of
+  // being skipped: with no branch around them, the compiler's waits for a
+  // set are exactly the loads issued before it (a load that might have been
+  // skipped makes it wait for every load in flight). For the same reason
+  // the steps run in whole periods of lcm(NS, 2) steps and the remaining
+  // steps nest their guards.
+  const int n = c_hi - c_lo;
+  constexpr int P = NS % 2 == 0 ? NS : 2 * NS;
+  auto step = [&](auto Sv, int i) __attribute__((always_inline)) {
+    constexpr int sp = decltype(Sv)::value;  // i % P
+    constexpr int u = sp & 1;
+    // (the scheduling barriers keep the loads ahead of the multiplication
+    // and of the staging, whose waits then leave them in flight)
+    load(std::integral_constant<int, sp % NS>{}, c_lo + min(i + NS, n - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st[u], std::integral_constant<int, u>{});
+    __builtin_amdgcn_sched_barrier(0);
+    store(std::integral_constant<int, (sp + 1) % NS>{}, st[1 - u], c_lo + min(i + 1, n - 1),
+          i + 1 < n);
+    lds_barrier();
+  };
+  int i = 0;
+  if (n > 0) {
+    unroll_steps<NS>([&](auto B, int b) __attribute__((always_inline)) { load(B, c_lo + min(b, n - 1)); },
+                     0);
+    store(std::integral_constant<int, 0>{}, st[0], c_lo, true);
+    __syncthreads();
+    for (; i + P <= n; i += P) unroll_steps<P>(step, i);
+    tail_steps<P - 1>(step, i, n);
   }
   float *out = a.partial + static_cast<int64_t>(blockIdx.y) * a.T * a.E;
   const int e = y * 32 + r;
