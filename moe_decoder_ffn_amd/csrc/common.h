@@ -37,12 +37,6 @@ constexpr int kRouterMaxSlices = 16;
 #define HI3_ROUTER_ROUND 512
 #endif
 constexpr int kRouterRound = HI3_ROUTER_ROUND;
-// Register sets of the logit kernel's load pipeline (chunks loaded ahead).
-#ifndef HI3_ROUTER_LOAD_SETS
-#define HI3_ROUTER_LOAD_SETS 2
-#endif
-constexpr int kRouterLoadSets = HI3_ROUTER_LOAD_SETS;
-static_assert(kRouterLoadSets >= 2 && kRouterLoadSets <= 4, "router load sets");
 // Rows per partial sum of the RMSNorm weight gradient (block backward).
 constexpr int kNormBwdRows = 64;
 

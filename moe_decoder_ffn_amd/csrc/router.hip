@@ -23,6 +23,13 @@
 
 namespace hi3 {
 
+// Register sets of the logit kernel's load pipeline (chunks loaded ahead).
+#ifndef HI3_ROUTER_LOAD_SETS
+#define HI3_ROUTER_LOAD_SETS 2
+#endif
+constexpr int kRouterLoadSets = HI3_ROUTER_LOAD_SETS;
+static_assert(kRouterLoadSets >= 2 && kRouterLoadSets <= 4, "router load sets");
+
 // --------------------------------------------------------------- selection
 
 // Softmax over all experts, top-K and renormalisation for 32 tokens per
