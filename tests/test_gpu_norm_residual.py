@@ -150,6 +150,21 @@ def test_forward_norm_residual_in_place():
     assert np.array_equal(out[pad == 1], d["x"][pad == 1])
 
 
+def test_forward_norm_residual_multichunk():
+    """157 token blocks: the router kernel splits H = 512 into 3 slices of
+    3, 3 and 2 chunks, so its load pipeline runs whole periods and both tail
+    lengths while it writes the normalised rows (every chunk of a real row
+    exactly once); padding rows hold NaN and keep the sentinel."""
+    _say("[norm] forward_norm_residual multi-chunk slices T=20000 H=512")
+    d, pad = _case(wk.BF16, 512, 64, 8, 128, 128, (19667,), 20000, 11, 0.05)
+    out, idx, w, cnt = _gpu_forward_nr(upload(d), 8, pad, 0.75)
+    real = np.nonzero(pad == 0)[0]
+    pick = np.random.default_rng(3).choice(real, 40, replace=False)
+    rows = np.unique(np.concatenate([real[:4], real[-4:], pick]))
+    _check_nr(d, 8, pad, out, idx, w, cnt, rows=rows)
+    assert np.all(as_f64(out[pad == 1]) == 0.75)
+
+
 def test_forward_norm_residual_full_size():
     _say("[norm] forward_norm_residual full size image_1024")
     wl = wk.workload("image_1024", 0)
@@ -161,7 +176,8 @@ def test_forward_norm_residual_full_size():
     _check_nr(d, wl.shape.K, pad, out, idx, w, cnt, rows=np.sort(rows))
 
 
-@pytest.mark.parametrize("H,T,pad_rows", [(512, 700, 0), (256, 333, 40), (4096, 4131, 0)])
+@pytest.mark.parametrize("H,T,pad_rows", [(512, 700, 0), (256, 333, 40), (4096, 4131, 0),
+                                           (512, 20000, 333)])
 def test_fused_norm_routes_match_plain_forward_on_rmsnorm(H, T, pad_rows):
     """The block forward normalises inside its router kernel (bf16): its
     normalised rows must be hi3_moe_rmsnorm's bit for bit, so its routes and

@@ -45,6 +45,9 @@ CASES = [
     ("bf16_e40_pad", wk.BF16, 0, 1024, 40, 6, (300, 17, 255), 3.0),
     ("bf16_e8_k8", wk.BF16, 257, 256, 8, 8, None, 10.0),
     ("bf16_e33_k1", wk.BF16, 95, 320, 33, 1, None, 10.0),
+    # 157 token blocks: 3 slices of the 8 chunks (3, 3, 2), so the logit
+    # kernel runs whole periods of its load pipeline and both tail lengths
+    ("bf16_multichunk", wk.BF16, 20000, 512, 64, 8, None, 1.0),
 ]
 
 
