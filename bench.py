@@ -1,17 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE feed-forward layer on one MI355X.
 
-One step = one hi3_moe_forward_overlap call over one batch of synthetic
-tokens: the router, dispatch, grouped [up; gate] + SwiGLU GEMM, grouped down
-GEMM, shared expert (on a second stream of the caller's where every row is
-real) and combine. Inputs are resident in HBM before timing starts.
+One step = one hi3_moe_forward call over one batch of synthetic tokens, on
+one stream: the router, dispatch, grouped [up; gate] + SwiGLU GEMM, grouped
+down GEMM (the shared expert's rows ride in both grouped launches) and
+combine. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s over the real tokens (the metric), with the
 layer's TFLOP/s and fraction of the bf16 MFMA peak, the roofline entry of the
 dominant kernel (its duration measured with HIP events recorded on the
-launch stream inside the timed region), per-stage times with the side stream
-and on one stream (where each kernel has the GPU to itself), the achievable
-peaks measured on this GPU next to the published ones, the batch's per-expert
+launch stream inside the timed region, where it has the GPU to itself),
+per-stage times, the same call with the shared expert on a second stream of
+the caller's (hi3_moe_forward_overlap) for comparison, the achievable peaks
+measured on this GPU next to the published ones, the batch's per-expert
 load, and the CPU oracle timed on a bounded sample of the same workload on
 this host's cores.
 """
@@ -594,8 +595,10 @@ def main():
     side_stream = torch.cuda.Stream()
     wargs = (dd["w_router"], dd["w13"], dd["w2"], dd["ws13"], dd["ws2"])
 
-    def step(events=None, side=side_stream):
-        if events is None:
+    def step(events=None, side=None):
+        if events is None and side is None:
+            m.hi3_moe_forward(x, *wargs, pad, sh.K, out, idx, wts, cnt, ws, stream=stream)
+        elif events is None:
             m.hi3_moe_forward_overlap(x, *wargs, pad, sh.K, out, idx, wts, cnt, ws,
                                       side_stream=side, stream=stream)
         else:
@@ -654,26 +657,27 @@ def main():
             hip.destroy(evs)
         return st_ms / args.steps, call
 
-    # with the side stream (the timed entry point) ...
-    stage_ms, step_ms = stage_pass(side_stream)
-    log(f"[bench] {args.steps} per-stage steps done (side stream)")
-    # ... and on one stream, where every kernel has the GPU to itself: the
-    # routing stages' own times and the grouped GEMMs' own rates (routed and
-    # shared rows in one launch)
-    alone_ms, alone_call = stage_pass(None)
+    # on one stream (the timed entry point), where every kernel has the GPU
+    # to itself ...
+    stage_ms, step_ms = stage_pass(None)
     log(f"[bench] {args.steps} per-stage steps done (one stream)")
+    # ... and with the shared expert's GEMMs on the side stream where every
+    # row is real (hi3_moe_forward_overlap): the grouped launches then hold
+    # the routed rows alone and share the GPU with the dense launches
+    side = m.hi3_moe_forward_shared_on_side(wl.T, sh.H, sh.E, sh.K, sh.I, sh.Is, sh.dtype,
+                                            pad is not None)
+    ov_ms, ov_call = stage_pass(side_stream)
+    log(f"[bench] {args.steps} per-stage steps done (side stream)")
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_s = wl.T_valid / (ms_per_step * 1e-3)
     flops = wl.T_valid * wk.flop_per_valid_token(sh)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    # the shared expert's GEMMs on the side stream: the GEMM stages (and the
-    # dominant kernel) are the routed experts' alone
-    side = m.hi3_moe_forward_shared_on_side(wl.T, sh.H, sh.E, sh.K, sh.I, sh.Is, sh.dtype,
-                                            pad is not None)
-    gf = gemm_flops(wl, shared=not side)
-    gf_all = gemm_flops(wl, shared=True)
+    # one stream: the GEMM stages (and the dominant kernel) hold the routed
+    # and the shared rows; beside the side stream, the routed rows alone
+    gf = gemm_flops(wl, shared=True)
+    gf_ov = gemm_flops(wl, shared=not side)
     sb = stage_bytes(wl)
 
     def stage_table(st_ms, g):
@@ -690,38 +694,35 @@ def main():
         return out_
 
     stages = stage_table(stage_ms, gf)
-    stages_alone = stage_table(alone_ms, gf_all)
+    stages_ov = stage_table(ov_ms, gf_ov)
     for name in names:
-        log(f"  {name:22s} side: {stages[name]}  alone: {stages_alone[name]}")
+        log(f"  {name:22s} one stream: {stages[name]}  side stream: {stages_ov[name]}")
 
-    kname = ("gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU, routed experts; the shared "
-             "expert runs as gemm_bf16_dense_kernel<0> on the side stream)" if side else
-             "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU)")
+    kname = "gemm_bf16_kernel<0> (grouped [up; gate] + SwiGLU, routed and shared rows)"
+    kname_ov = ("gemm_bf16_kernel<0> (routed rows alone, beside the shared expert's "
+                "gemm_bf16_dense_kernel<0> on the side stream)" if side else kname)
     ui = names.index("gemm_up_gate_swiglu")
     wi = names.index("gemm_down")
     if sh.dtype == wk.BF16 and wl.T_valid * sh.K <= RIDGE_ROWS * sh.E:
         # few rows per expert: the weights are the traffic (HBM roofline)
-        gb = upgate_bytes(wl, shared=not side)
-        achieved = gb / (dom_ms * 1e-3) / 1e9
+        achieved = upgate_bytes(wl, shared=True) / (dom_ms * 1e-3) / 1e9
         roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(wl.name)}
-        a_alone = upgate_bytes(wl, shared=True) / (alone_ms[ui] * 1e-3) / 1e9
-        roofline_alone = {"kernel": "gemm_bf16_kernel<0> (routed and shared rows, one stream)",
-                          "achieved": round(a_alone, 1), "unit": "GB/s",
-                          "frac": round(a_alone / PEAK_HBM_GBS, 4)}
+        a_ov = upgate_bytes(wl, shared=not side) / (ov_ms[ui] * 1e-3) / 1e9
+        roofline_ov = {"kernel": kname_ov, "achieved": round(a_ov, 1), "unit": "GB/s",
+                       "frac": round(a_ov / PEAK_HBM_GBS, 4)}
     else:
         achieved = gf[dom] / (dom_ms * 1e-3) / 1e12
         roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic(wl.name)}
-        a_alone = gf_all[dom] / (alone_ms[ui] * 1e-3) / 1e12
-        roofline_alone = {"kernel": "gemm_bf16_kernel<0> (routed and shared rows, one stream)",
-                          "achieved": round(a_alone, 1), "unit": "TFLOP/s",
-                          "frac": round(a_alone / PEAK_BF16_TFLOPS, 4)}
-    gemm_alone_ms = alone_ms[ui] + alone_ms[wi]
-    gemm_alone = sum(gf_all.values()) / (gemm_alone_ms * 1e-3) / 1e12
+        a_ov = gf_ov[dom] / (ov_ms[ui] * 1e-3) / 1e12
+        roofline_ov = {"kernel": kname_ov, "achieved": round(a_ov, 1), "unit": "TFLOP/s",
+                       "frac": round(a_ov / PEAK_BF16_TFLOPS, 4)}
+    gemm_ms = stage_ms[ui] + stage_ms[wi]
+    gemm_rate = sum(gf.values()) / (gemm_ms * 1e-3) / 1e12
 
     peaks = None
     if not args.no_peaks:
@@ -739,7 +740,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if sh.dtype == wk.BF16 else "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "entry": "forward_overlap", "T": wl.T,
+        "config": {"workload": wl.name, "entry": "forward", "T": wl.T,
                    "T_valid": wl.T_valid, "H": sh.H, "E": sh.E, "K": sh.K, "I": sh.I,
                    "I_shared": sh.Is, "seed": args.seed},
         "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -748,13 +749,15 @@ def main():
         # steps' own: dominant_kernel_us
         "call_ms": {"median": round(float(np.median(step_ms)), 4),
                     "min": round(float(np.min(step_ms)), 4),
-                    "one_stream_median": round(float(np.median(alone_call)), 4)},
+                    "overlap_median": round(float(np.median(ov_call)), 4)},
         "dominant_kernel_us": round(dom_ms * 1e3, 2),
-        "stages": stages, "stages_one_stream": stages_alone,
-        "roofline": roofline, "roofline_one_stream": roofline_alone,
-        "gemms_one_stream": {"us": round(gemm_alone_ms * 1e3, 1),
-                             "tflops": round(gemm_alone, 1),
-                             "frac_bf16_peak": round(gemm_alone / PEAK_BF16_TFLOPS, 4)},
+        "stages": stages,
+        "roofline": roofline,
+        "gemms": {"us": round(gemm_ms * 1e3, 1), "tflops": round(gemm_rate, 1),
+                  "frac_bf16_peak": round(gemm_rate / PEAK_BF16_TFLOPS, 4)},
+        # hi3_moe_forward_overlap: the shared expert on the side stream
+        "overlap": {"shared_on_side": bool(side), "stages": stages_ov,
+                    "roofline": roofline_ov},
         "peaks": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
                   "achievable": peaks},
         "expert_load": load,
