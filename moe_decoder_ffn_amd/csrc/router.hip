@@ -233,8 +233,8 @@ __device__ __forceinline__ void split3x2(float v0, float v1, uint32_t &hi, uint3
 // loads: the 128 token rows (normalised on the way with NORM), and the 64
 // expert rows of the fp32 weight, split on the way into their three bf16
 // terms. The loads run kRouterLoadSets chunks ahead of the multiplication
-// (that many register sets, two LDS buffers, one barrier per chunk). With NORM the rows
-// are normalised with their r (computed by row_rms_kernel):
+// (that many register sets, two LDS buffers, one barrier per chunk). With
+// NORM the rows are normalised with their r (computed by row_rms_kernel):
 // n = bf16(x r), xn = bf16(w n); the staging threads also write xn (the
 // expert GEMMs' input): every element of every real row is written once.
 //
@@ -431,8 +431,9 @@ __global__ __launch_bounds__(256, 2) void router_slice_kernel(RouterSliceArgs a)
   // Chunk c_lo + i is loaded into register set i % NS, staged in LDS
   // buffer i % 2 and multiplied into accumulator i % 2. Step i loads chunk
   // i + NS into the set staged in step i - 1, multiplies chunk i and stages
-  // chunk i + 1, so the loads of NS - 1 chunks stay in flight across the
-  // multiplication. Past the slice's last chunk the loads and the staging
+  // chunk i + 1: the loads of chunks i + 1 .. i + NS may be in flight during
+  // the multiplication, and those of NS - 1 chunks stay in flight past the
+  // staging. Past the slice's last chunk the loads and the staging
   // repeat it (into a set and a buffer that are not read again) instead of
   // being skipped: with no branch around them, the compiler's waits for a
   // set are exactly the loads issued before it (a load that might have been
