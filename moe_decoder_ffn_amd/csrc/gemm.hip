@@ -289,6 +289,20 @@ __device__ __forceinline__ void barrier_no_fence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Workgroup barrier of the epilogues, which stage the tile in the idle LDS
+// ring: waits for this wave's LDS operations only (its staging writes, or
+// its reads of the staged chunk), so the wave's global stores and loads stay
+// in flight across it. __syncthreads() would wait for them to complete (its
+// fence drains vmcnt), which exposed the store latency at every chunk.
+__device__ __forceinline__ void epi_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time.
 template <int N, typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
@@ -658,7 +672,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     constexpr int HC = BN / 2;         // columns of the h tile
     constexpr int HLD = HC + 8;        // staged h row stride (bf16, 16 B pad)
     constexpr int ULD = HC + 4;        // staged u / g row stride (fp32, 16 B pad)
-    constexpr int RING = NST * (BM + BN) * BK * 2;
+    constexpr int RING = (NST * (BM + BN) + (DB ? BN : 0)) * BK * 2;
     constexpr int UGR = 2 * 64 * ULD * 4 <= RING ? 64 : 32;
     static_assert(BM * HLD * 2 <= RING && 2 * UGR * ULD * 4 <= RING && NI == 2 * (NI / 2),
                   "staged h / ug tiles fit in the LDS ring");
@@ -686,7 +700,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
           const int c = wn * (HC / WN) + p * 32 + 8 * q + 4 * g;
           *reinterpret_cast<u32x2_t *>(sh + row * HLD + c) = o;
         }
-    __syncthreads();
+    epi_barrier();
     // two rows per wave instruction: lanes 0-31 one row, 32-63 the next;
     // lane l takes columns 4 (l % 32) .. + 3
     const int hcol = j.nt * HC + 4 * (lane & 31);
@@ -718,7 +732,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
                   dhp + (static_cast<int64_t>(j.row0) + ch * UGR + rl) * Ih + hcol);
           }
         }
-        __syncthreads();
+        epi_barrier();
         static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
           constexpr int mi = decltype(Mv)::value;
           const int rb = wm * (BM / 2) + mi * 32;
@@ -736,7 +750,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
                           acc[mi][p + NI / 2][4 * q + 2], acc[mi][p + NI / 2][4 * q + 3]};
             }
         });
-        __syncthreads();
+        epi_barrier();
         const int nr = min(UGR, j.rows - ch * UGR);
         if (dhp) {
           // the SwiGLU backward (as mode 2's epilogue computes it from stored
@@ -846,7 +860,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     // takes columns 4 l .. 4 l + 3, and the u, g, h reads and the du, dg
     // writes are contiguous row segments.
     constexpr int SLD = BN + 4;  // staged row stride in floats (16 B pad: bank spread)
-    constexpr int RING = NST * (BM + BN) * BK * 2;
+    constexpr int RING = (NST * (BM + BN) + (DB ? BN : 0)) * BK * 2;
     // rows staged at a time: the whole tile when it fits the ring
     constexpr int CH = BM * SLD * 4 <= RING ? BM : (BM / 2) * SLD * 4 <= RING ? BM / 2 : BM / 4;
     static_assert(CH * SLD * 4 <= RING && CH % 32 == 0 && BM % CH == 0,
@@ -862,7 +876,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     // and the last step ended with a workgroup barrier: the ring is free
 #pragma unroll 1
     for (int ch = 0; ch < BM / CH && ch * CH < j.rows; ++ch) {
-      if (ch > 0) __syncthreads();
+      if (ch > 0) epi_barrier();
       static_for<MI>([&](auto Mv) __attribute__((always_inline)) {
         constexpr int mi = decltype(Mv)::value;
         const int rb = wm * (BM / 2) + mi * 32;
@@ -877,7 +891,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
                         acc[mi][ni][4 * q + 3]};
           }
       });
-      __syncthreads();
+      epi_barrier();
       const int nr = min(CH, j.rows - ch * CH);
       if (!ugp) {
         // dh alone (the recompute's epilogue runs the SwiGLU backward), fp32
@@ -960,7 +974,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
     using OT = std::conditional_t<MODE == 4, uint16_t, float>;
     constexpr int OB = sizeof(OT);
     constexpr int LD = BN + 16 / OB;  // staged row stride in elements (16 B pad)
-    constexpr int RING = NST * (BM + BN) * BK * 2;
+    // (the dx GEMM keeps 64-row chunks: with 128-row chunks its body spills
+    // 320 B/lane instead of 76)
+    constexpr int RING = (NST * (BM + BN) + (DB && MODE != 3 ? BN : 0)) * BK * 2;
     constexpr int CH = BM * LD * OB <= RING ? BM : (BM / 2) * LD * OB <= RING ? BM / 2 : BM / 4;
     static_assert(CH * LD * OB <= RING && CH % 32 == 0 && BM % CH == 0, "staged chunk fits");
     OT *stg = reinterpret_cast<OT *>(sA0);
@@ -991,7 +1007,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
             }
           }
       });
-      __syncthreads();
+      epi_barrier();
       const int nr = min(CH, j.rows - ch * CH);
 #pragma unroll 4
       for (int rl = wave; rl < nr; rl += NW) {
@@ -1004,7 +1020,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const TileJob &j, u
             *reinterpret_cast<f32x4_t *>(dst) = *reinterpret_cast<const f32x4_t *>(src);
         }
       }
-      __syncthreads();
+      epi_barrier();
     }
   } else if constexpr (MODE == 4) {
     uint16_t *C = static_cast<uint16_t *>(Cv) + static_cast<int64_t>(j.g < a.E ? j.g : 0) * cl.strideC;
