@@ -56,20 +56,20 @@ __device__ __forceinline__ int class_col_tiles(const GemmClass &c) {
   return MODE == 0 ? (c.N / 2 + BN / 2 - 1) / (BN / 2) : (c.N + BN - 1) / BN;
 }
 
-// The job list: groups in order. Modes 0 and 1: within a group, chunks of
+// The job list: groups in order. Modes 0, 1 and 2: within a group, chunks of
 // kGemmColChunk column tiles, each chunk taking every row (sub-)tile of the
 // group, row tile major, so the blocks that share a weight tile or a row
 // tile's rows are neighbours; block b runs on XCD b % 8, and XCD x takes
 // the contiguous part [x per, (x + 1) per) of the list (per = ceil(jobs /
 // 8)): a group's weights and rows are fetched into one XCD's L2 (two at a
-// part boundary), where the neighbours run at the same time. Modes 2 and 3
+// part boundary), where the neighbours run at the same time. Mode 3
 // (measured faster so): row tile major, column fastest, block b = job b.
 template <int MODE, int BN>
 __device__ __forceinline__ bool resolve_job(const GemmArgs &a, TileJob &j) {
   const int ntiles = a.gto[a.E + 1];
   const int SP = a.split;
   const int W = ntiles * SP * a.NTn;
-  constexpr bool XM = MODE <= 1;
+  constexpr bool XM = MODE <= 2;
   const int per = (W + 7) / 8;
   if (XM && static_cast<int>(blockIdx.x) / 8 >= per) return false;
   const int L = XM ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
